@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle checks.
+
+This module draws random numbers and nothing else: it holds none of the
+attention layer's arithmetic. Both the GPU path and the CPU oracle read the
+same arrays from here, so a parity failure can never come from two different
+input streams.
+
+Recipe (stated once, used everywhere):
+  * every tensor has an integer "tensor id": x 0, Wq 1, Wk 2, Wv 3, Wo 4,
+    dY 5, q-norm gamma 6, k-norm gamma 7;
+  * a 2-D tensor is drawn in blocks of ``ROW_BLOCK`` rows; block ``b`` of
+    tensor ``t`` under run seed ``s`` uses
+    ``numpy.random.default_rng(SeedSequence([s, t, b]))`` and draws
+    ``standard_normal(float32)``, scaled by the tensor's std;
+  * bf16 inputs are the fp32 draws rounded to nearest-even bf16, so the value
+    the GPU sees is exactly representable in fp32/fp64 on the host.
+
+Any block can therefore be regenerated on its own, which lets the oracle check
+sampled rows of a very long sequence without holding the whole of x.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 65536
+
+TENSOR_IDS = {"x": 0, "wq": 1, "wk": 2, "wv": 3, "wo": 4, "dy": 5, "q_norm": 6, "k_norm": 7}
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    # NaN never occurs in these draws; keep the branch-free form.
+    return r.view(np.float32)
+
+
+def _block_rng(seed: int, tensor_id: int, block: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(seed), int(tensor_id), int(block)]))
+
+
+def gen_rows(name: str, rows: int, cols: int, std: float, dtype: str, seed: int = 0,
+             row_start: int = 0, row_stop: int | None = None) -> np.ndarray:
+    """Rows ``[row_start, row_stop)`` of the ``rows x cols`` tensor ``name``.
+
+    Returns float32 (already bf16-rounded when ``dtype == 'bf16'``).
+    """
+    if row_stop is None:
+        row_stop = rows
+    assert 0 <= row_start <= row_stop <= rows
+    tid = TENSOR_IDS[name]
+    out = np.empty((row_stop - row_start, cols), dtype=np.float32)
+    b0 = row_start // ROW_BLOCK
+    b1 = (row_stop + ROW_BLOCK - 1) // ROW_BLOCK
+    for b in range(b0, b1):
+        lo = b * ROW_BLOCK
+        hi = min(rows, lo + ROW_BLOCK)
+        blk = _block_rng(seed, tid, b).standard_normal((hi - lo, cols), dtype=np.float32)
+        if std != 1.0:
+            blk *= np.float32(std)
+        s0 = max(lo, row_start)
+        s1 = min(hi, row_stop)
+        out[s0 - row_start:s1 - row_start] = blk[s0 - lo:s1 - lo]
+    if dtype == "bf16":
+        out = round_to_bf16(out)
+    elif dtype != "fp32":
+        raise ValueError(f"unknown dtype {dtype}")
+    return out
+
+
+def gen_rows_at(name: str, rows: int, cols: int, std: float, dtype: str, seed: int,
+                idx: np.ndarray) -> np.ndarray:
+    """Selected rows ``idx`` (any order) of tensor ``name``; regenerates only their blocks."""
+    idx = np.asarray(idx, dtype=np.int64)
+    out = np.empty((idx.size, cols), dtype=np.float32)
+    blocks = np.unique(idx // ROW_BLOCK)
+    for b in blocks:
+        lo = int(b) * ROW_BLOCK
+        hi = min(rows, lo + ROW_BLOCK)
+        blk = gen_rows(name, rows, cols, std, dtype, seed, lo, hi)
+        sel = np.nonzero((idx >= lo) & (idx < hi))[0]
+        out[sel] = blk[idx[sel] - lo]
+    return out
+
+
+def gen_gamma(name: str, d: int, mode: str, dtype: str, seed: int = 0) -> np.ndarray:
+    """RMSNorm weight of length d: ``mode='ones'`` or ``'random'`` (1 + 0.1*N(0,1))."""
+    if mode == "ones":
+        return np.ones(d, dtype=np.float32)
+    g = 1.0 + 0.1 * gen_rows(name, 1, d, 1.0, "fp32", seed)[0]
+    g = g.astype(np.float32)
+    return round_to_bf16(g) if dtype == "bf16" else g
+
+
+class LayerInputs:
+    """All inputs of one attention-layer problem, as float32 host arrays.
+
+    Shapes follow the library's layout: x, dy ``[N][D]``; wq ``[Hq*d][D]``;
+    wk, wv ``[Hkv*d][D]``; wo ``[D][Hq*d]``; gammas ``[d]`` or None.
+    """
+
+    def __init__(self, n_tokens: int, d_model: int, n_q_heads: int, n_kv_heads: int,
+                 head_dim: int, dtype: str, seed: int = 0, w_std: float = 0.02,
+                 qk_norm: str | None = None, with_x: bool = True, with_dy: bool = True):
+        self.n_tokens, self.d_model = n_tokens, d_model
+        self.n_q_heads, self.n_kv_heads, self.head_dim = n_q_heads, n_kv_heads, head_dim
+        self.dtype, self.seed, self.w_std = dtype, seed, w_std
+        N, D, d = n_tokens, d_model, head_dim
+        self.x = gen_rows("x", N, D, 1.0, dtype, seed) if with_x else None
+        self.dy = gen_rows("dy", N, D, 1.0, dtype, seed) if with_dy else None
+        self.wq = gen_rows("wq", n_q_heads * d, D, w_std, dtype, seed)
+        self.wk = gen_rows("wk", n_kv_heads * d, D, w_std, dtype, seed)
+        self.wv = gen_rows("wv", n_kv_heads * d, D, w_std, dtype, seed)
+        self.wo = gen_rows("wo", D, n_q_heads * d, w_std, dtype, seed)
+        if qk_norm is None:
+            self.q_norm = self.k_norm = None
+        else:
+            self.q_norm = gen_gamma("q_norm", d, qk_norm, dtype, seed)
+            self.k_norm = gen_gamma("k_norm", d, qk_norm, dtype, seed)

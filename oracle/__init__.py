@@ -1,0 +1,20 @@
+"""CPU fp64 oracle for headwise-chunked causal RoPE/GQA attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product package imports this; only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may call it.
+"""
+from .attention import (  # noqa: F401
+    rope_cos_sin,
+    apply_rope,
+    rope_transpose,
+    rmsnorm,
+    rmsnorm_bwd,
+    causal_attention,
+    causal_attention_bwd,
+    layer_fwd,
+    layer_bwd,
+    layer_fwd_rows,
+    layer_bwd_tail_dx,
+    chunk_plan,
+)
