@@ -1,0 +1,196 @@
+"""Thin Python binding of libupipe.so (ctypes): argument marshalling only.
+
+PyTorch supplies device memory and the stream; every step of the attention
+layer runs in the library's HIP kernels. There is no fallback: if the library
+is missing or the tensors are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libupipe.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "upipe.h")
+
+UPIPE_F32, UPIPE_BF16 = 0, 1
+_DTYPES = {torch.float32: UPIPE_F32, torch.bfloat16: UPIPE_BF16}
+
+_lib = None
+
+
+class UpipeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def load():
+    """Load libupipe.so (built in-tree by headwise_chunked_attention_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m headwise_chunked_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, dbl, flt, vp, sz = (ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_float,
+                                  ctypes.c_void_p, ctypes.c_size_t)
+    lib.upipe_attn_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32, i32]
+    lib.upipe_attn_workspace_bytes.restype = sz
+    lib.upipe_attn_fwd.argtypes = [i32, i64, i64, i32, i32, i32, dbl, i32,
+                                   vp, vp, vp, vp, vp, vp, vp, flt, vp, vp, vp, sz, vp]
+    lib.upipe_attn_fwd.restype = i32
+    lib.upipe_attn_bwd.argtypes = [i32, i64, i64, i32, i32, i32, dbl, i32,
+                                   vp, vp, vp, vp, vp, vp, vp, flt, vp, vp, vp,
+                                   vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.upipe_attn_bwd.restype = i32
+    lib.upipe_strerror.argtypes = [i32]
+    lib.upipe_strerror.restype = ctypes.c_char_p
+    lib.upipe_version.argtypes = []
+    lib.upipe_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions include/upipe.h declares."""
+    txt = open(HEADER_PATH).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(upipe_[a-z_]+)\s*\(", txt)))
+
+
+def strerror(code: int) -> str:
+    return load().upipe_strerror(int(code)).decode()
+
+
+def dtype_code(dtype) -> int:
+    if dtype in _DTYPES:
+        return _DTYPES[dtype]
+    if dtype in ("fp32", "f32", "float32"):
+        return UPIPE_F32
+    if dtype in ("bf16", "bfloat16"):
+        return UPIPE_BF16
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def workspace_bytes(n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, chunk_heads, qk_norm,
+                    dtype, backward) -> int:
+    return int(load().upipe_attn_workspace_bytes(int(n_tokens), int(d_model), int(n_q_heads),
+                                                  int(n_kv_heads), int(head_dim), int(chunk_heads),
+                                                  int(bool(qk_norm)), dtype_code(dtype), int(bool(backward))))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A 256-byte aligned device buffer of at least nbytes (torch's allocator aligns to 512)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def attn_fwd(x, wq, wk, wv, wo, *, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads,
+             q_norm=None, k_norm=None, eps=1e-6, y=None, lse=None, workspace=None, stream=None):
+    """Forward of the headwise-chunked attention layer; returns ``(y, lse)``."""
+    lib = load()
+    N, D = x.shape
+    dev = x.device
+    dt = x.dtype
+    d = head_dim
+    _check(x, "x", dt, (N, D), dev)
+    _check(wq, "wq", dt, (n_q_heads * d, D), dev)
+    _check(wk, "wk", dt, (n_kv_heads * d, D), dev)
+    _check(wv, "wv", dt, (n_kv_heads * d, D), dev)
+    _check(wo, "wo", dt, (D, n_q_heads * d), dev)
+    if (q_norm is None) != (k_norm is None):
+        raise ValueError("q_norm and k_norm must both be given or both be None")
+    if q_norm is not None:
+        _check(q_norm, "q_norm", dt, (d,), dev)
+        _check(k_norm, "k_norm", dt, (d,), dev)
+    if y is None:
+        y = torch.empty((N, D), dtype=dt, device=dev)
+    if lse is None:
+        lse = torch.empty((n_q_heads, N), dtype=torch.float32, device=dev)
+    _check(y, "y", dt, (N, D), dev)
+    _check(lse, "lse", torch.float32, (n_q_heads, N), dev)
+    need = workspace_bytes(N, D, n_q_heads, n_kv_heads, d, chunk_heads, q_norm is not None, dt, False)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    rc = lib.upipe_attn_fwd(dtype_code(dt), N, D, n_q_heads, n_kv_heads, d, float(rope_theta), chunk_heads,
+                            _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(q_norm), _ptr(k_norm),
+                            float(eps), _ptr(y), _ptr(lse), _ptr(workspace), workspace.numel(),
+                            _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_attn_fwd")
+    return y, lse
+
+
+def attn_bwd(x, wq, wk, wv, wo, dy, lse, *, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads,
+             q_norm=None, k_norm=None, eps=1e-6, out=None, workspace=None, stream=None):
+    """Backward of the layer; returns ``(dx, dwq, dwk, dwv, dwo, dq_norm, dk_norm)``."""
+    lib = load()
+    N, D = x.shape
+    dev = x.device
+    dt = x.dtype
+    d = head_dim
+    _check(x, "x", dt, (N, D), dev)
+    _check(wq, "wq", dt, (n_q_heads * d, D), dev)
+    _check(wk, "wk", dt, (n_kv_heads * d, D), dev)
+    _check(wv, "wv", dt, (n_kv_heads * d, D), dev)
+    _check(wo, "wo", dt, (D, n_q_heads * d), dev)
+    _check(dy, "dy", dt, (N, D), dev)
+    _check(lse, "lse", torch.float32, (n_q_heads, N), dev)
+    norm = q_norm is not None
+    if (q_norm is None) != (k_norm is None):
+        raise ValueError("q_norm and k_norm must both be given or both be None")
+    if norm:
+        _check(q_norm, "q_norm", dt, (d,), dev)
+        _check(k_norm, "k_norm", dt, (d,), dev)
+    f32 = torch.float32
+    if out is None:
+        out = (torch.empty((N, D), dtype=dt, device=dev),
+               torch.empty(wq.shape, dtype=f32, device=dev), torch.empty(wk.shape, dtype=f32, device=dev),
+               torch.empty(wv.shape, dtype=f32, device=dev), torch.empty(wo.shape, dtype=f32, device=dev),
+               torch.empty((d,), dtype=f32, device=dev) if norm else None,
+               torch.empty((d,), dtype=f32, device=dev) if norm else None)
+    dx, dwq, dwk, dwv, dwo, dqn, dkn = out
+    _check(dx, "dx", dt, (N, D), dev)
+    for t, n, ref in ((dwq, "dwq", wq), (dwk, "dwk", wk), (dwv, "dwv", wv), (dwo, "dwo", wo)):
+        _check(t, n, f32, tuple(ref.shape), dev)
+    if norm:
+        _check(dqn, "dq_norm", f32, (d,), dev)
+        _check(dkn, "dk_norm", f32, (d,), dev)
+    need = workspace_bytes(N, D, n_q_heads, n_kv_heads, d, chunk_heads, norm, dt, True)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    rc = lib.upipe_attn_bwd(dtype_code(dt), N, D, n_q_heads, n_kv_heads, d, float(rope_theta), chunk_heads,
+                            _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(q_norm), _ptr(k_norm),
+                            float(eps), _ptr(dy), _ptr(lse), _ptr(dx), _ptr(dwq), _ptr(dwk), _ptr(dwv),
+                            _ptr(dwo), _ptr(dqn), _ptr(dkn), _ptr(workspace), workspace.numel(),
+                            _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_attn_bwd")
+    return dx, dwq, dwk, dwv, dwo, dqn, dkn

@@ -1,0 +1,280 @@
+// Causal GQA flash-attention forward for one chunk of heads on gfx950.
+//
+// The chunk's heads each attend over the whole sequence (one GPU computes
+// full-sequence attention for the heads it owns, then the next chunk reuses
+// the buffers: "500 万トークンへの道 — Max Ryabinin (Together AI) の Untied
+// Ulysses", section "Untied Ulysses (UPipe) — head 単位のチャンク化").
+//
+// Orientation: each wave computes S^T = K Q^T for its queries, so a lane owns
+// one query column and 16 keys of each 32x32 tile. Row statistics of the
+// softmax are then an in-lane reduction plus one exchange between the two
+// half-waves, and P^T feeds O^T = V^T P^T straight from the accumulators
+// (see common.h). K tiles are staged [key][d] and V^T tiles [d][key] in LDS,
+// double buffered, prefetched through registers one tile ahead.
+//
+// Workgroup: 4 waves x (32*NQT) query rows. `hp` heads of the same kv head
+// are packed per workgroup (GQA): the K/V tile in LDS then serves hp heads.
+// Mode 0 (training forward): online softmax; writes O and LSE.
+// Mode 1 (backward recompute): LSE is given; writes O and
+//   Delta_i = dO_i . O_i, the row term of the softmax backward.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace upipe {
+
+namespace {
+
+constexpr int BC = 64;  // keys per tile
+constexpr int NTHREADS = 256;
+
+template <typename T, int D>
+struct FwdGeo {
+  static constexpr int NQT = (sizeof(T) == 4 && D == 128) ? 1 : 2;  // 32-query tiles per wave
+  static constexpr int ROWS_W = 32 * NQT;
+  static constexpr int SKD = lds_stride<T>(D);   // K tile row stride
+  static constexpr int SVT = lds_stride<T>(BC);  // V^T tile row stride
+  static constexpr int K_ELEMS = BC * SKD;
+  static constexpr int V_ELEMS = D * SVT;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int KCH = BC * D / VEC / NTHREADS;  // 16-byte chunks per thread (K)
+  static constexpr int VCH = D * BC / VEC / NTHREADS;  // (V^T)
+};
+
+template <typename T, int D>
+DEV void load_kv(const AttnFwd<T>& p, int64_t k0, u32x4 (&rk)[FwdGeo<T, D>::KCH],
+                 u32x4 (&rv)[FwdGeo<T, D>::VCH]) {
+  using G = FwdGeo<T, D>;
+  const int tid = threadIdx.x;
+  constexpr int KC_ROW = D / G::VEC, VC_ROW = BC / G::VEC;
+#pragma unroll
+  for (int i = 0; i < G::KCH; ++i) {
+    const int c = tid + i * NTHREADS;
+    rk[i] = ld_raw16(p.k + (k0 + c / KC_ROW) * D + (c % KC_ROW) * G::VEC);
+  }
+#pragma unroll
+  for (int i = 0; i < G::VCH; ++i) {
+    const int c = tid + i * NTHREADS;
+    rv[i] = ld_raw16(p.vt + (int64_t)(c / VC_ROW) * p.Np + k0 + (c % VC_ROW) * G::VEC);
+  }
+}
+
+template <typename T, int D>
+DEV void store_kv(T* stage, const u32x4 (&rk)[FwdGeo<T, D>::KCH], const u32x4 (&rv)[FwdGeo<T, D>::VCH]) {
+  using G = FwdGeo<T, D>;
+  const int tid = threadIdx.x;
+  constexpr int KC_ROW = D / G::VEC, VC_ROW = BC / G::VEC;
+  T* Ks = stage;
+  T* Vs = stage + G::K_ELEMS;
+#pragma unroll
+  for (int i = 0; i < G::KCH; ++i) {
+    const int c = tid + i * NTHREADS;
+    st_raw16(Ks + (c / KC_ROW) * G::SKD + (c % KC_ROW) * G::VEC, rk[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < G::VCH; ++i) {
+    const int c = tid + i * NTHREADS;
+    st_raw16(Vs + (c / VC_ROW) * G::SVT + (c % VC_ROW) * G::VEC, rv[i]);
+  }
+}
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(const AttnFwd<T> p, int hp) {
+  using G = FwdGeo<T, D>;
+  constexpr int NQT = G::NQT, ND = D / 32, NS = D / 16;
+  __shared__ __attribute__((aligned(16))) T smem[2 * G::STAGE];
+
+  const int l = lane_id(), r = l & 31, h = l >> 5;
+  const int w = wave_id();
+  const int qb_rows = 4 * G::ROWS_W / hp;  // query positions per workgroup
+  const int64_t nqb = p.Np / qb_rows;
+  const int64_t qb = nqb - 1 - (int64_t)blockIdx.x;  // longest rows first
+  const int hh = (int)blockIdx.y * hp + (w % hp);
+  const int64_t qs = qb * qb_rows;
+  const int64_t q0w = qs + (int64_t)(w / hp) * G::ROWS_W;
+
+  // Q^T as B operands, resident for the whole key loop.
+  const T* qh = p.q + (int64_t)hh * p.Np * D;
+  Frag<T> qf[NQT][NS];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[t][s] = ld_frag(qh + (q0w + t * 32 + r) * D + s * 16 + 8 * h);
+
+  float m_run[NQT], l_run[NQT], base_row[NQT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+    base_row[t] = 0.f;
+    if constexpr (MODE == 1) {
+      const int64_t q = q0w + t * 32 + r;
+      base_row[t] = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : 0.f;
+    }
+  }
+  f32x16 oacc[NQT][ND];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t)
+#pragma unroll
+    for (int j = 0; j < ND; ++j) oacc[t][j] = zero16();
+
+  const int64_t ntiles = (qs + qb_rows) / BC;
+  u32x4 rk[G::KCH], rv[G::VCH];
+  load_kv<T, D>(p, 0, rk, rv);
+  store_kv<T, D>(smem, rk, rv);
+  __syncthreads();
+
+  for (int64_t kt_i = 0; kt_i < ntiles; ++kt_i) {
+    const int64_t k0 = kt_i * BC;
+    const int buf = (int)(kt_i & 1);
+    if (kt_i + 1 < ntiles) load_kv<T, D>(p, k0 + BC, rk, rv);
+    const T* Ks = smem + buf * G::STAGE;
+    const T* Vs = Ks + G::K_ELEMS;
+
+    if (k0 <= q0w + G::ROWS_W - 1) {  // some key of the tile is visible to this wave
+      f32x16 sacc[2][NQT];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) sacc[kt][t] = zero16();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const Frag<T> a = ld_frag(Ks + (kt * 32 + r) * G::SKD + s * 16 + 8 * h);
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) mma(sacc[kt][t], a, qf[t][s]);
+        }
+      }
+      const bool diag = (k0 + BC - 1 > q0w);
+#pragma unroll
+      for (int t = 0; t < NQT; ++t) {
+        const int64_t q = q0w + t * 32 + r;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float x = sacc[kt][t][e] * p.scale_log2;
+            if (diag) {
+              const int64_t key = k0 + kt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+              if (key > q) x = -INFINITY;
+            }
+            sacc[kt][t][e] = x;
+          }
+        if constexpr (MODE == 0) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][t][e]);
+          mx = wave_max_pair(mx);
+          const float m_new = fmaxf(m_run[t], mx);
+          const float base = (m_new == -INFINITY) ? 0.f : m_new;
+          const float alpha = fast_exp2(m_run[t] - base);
+          m_run[t] = m_new;
+          base_row[t] = base;
+          l_run[t] *= alpha;
+#pragma unroll
+          for (int j = 0; j < ND; ++j) oacc[t][j] *= alpha;
+        }
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float pe = fast_exp2(sacc[kt][t][e] - base_row[t]);
+            sacc[kt][t][e] = pe;
+            psum += pe;
+          }
+        l_run[t] += psum;
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          Frag<T> pf[NQT];
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) pf[t] = frag_from_acc<T>(sacc[kt][t], s2, 1.0f);
+#pragma unroll
+          for (int j = 0; j < ND; ++j) {
+            const T* vrow = Vs + (j * 32 + r) * G::SVT + kt * 32 + 16 * s2 + 4 * h;
+            const Frag<T> a = ld_frag2(vrow, vrow + 8);
+#pragma unroll
+            for (int t = 0; t < NQT; ++t) mma(oacc[t][j], a, pf[t]);
+          }
+        }
+    }
+    if (kt_i + 1 < ntiles) store_kv<T, D>(smem + (buf ^ 1) * G::STAGE, rk, rv);
+    __syncthreads();
+  }
+
+  // epilogue
+  T* oh = p.o + (int64_t)hh * p.Np * D;
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const int64_t q = q0w + t * 32 + r;
+    const float l_tot = l_run[t] + __shfl_xor(l_run[t], 32);
+    float scale = 1.f;
+    if constexpr (MODE == 0) {
+      scale = 1.0f / l_tot;
+      if (h == 0 && q < p.N)
+        p.lse[(int64_t)hh * p.lse_stride + q] = (m_run[t] + log2f(l_tot)) * 0.6931471805599453f;
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < ND; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dd = j * 32 + 8 * i + 4 * h;
+        float v[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) v[jj] = oacc[t][j][4 * i + jj] * scale;
+        T* dst = oh + q * D + dd;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = (f32x4){v[0], v[1], v[2], v[3]};
+        }
+        if constexpr (MODE == 1) {
+          const T* src = p.dout + (int64_t)hh * p.Np * D + q * D + dd;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) dot += v[jj] * to_f<T>(src[jj]);
+        }
+      }
+    if constexpr (MODE == 1) {
+      dot += __shfl_xor(dot, 32);
+      if (h == 0) p.delta[(int64_t)hh * p.Np + q] = (q < p.N) ? dot : 0.f;
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_d(const AttnFwd<T>& p, int mode, hipStream_t s) {
+  using G = FwdGeo<T, D>;
+  int hp = 1;
+  while (hp * 2 <= 4 && p.nh % (hp * 2) == 0) hp *= 2;
+  const int qb_rows = 4 * G::ROWS_W / hp;
+  const dim3 grid((unsigned)(p.Np / qb_rows), (unsigned)(p.nh / hp));
+  if (mode == 0)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, 0>), grid, dim3(NTHREADS), 0, s, p, hp);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, 1>), grid, dim3(NTHREADS), 0, s, p, hp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_attn_fwd(const AttnFwd<T>& p, int head_dim, int mode, hipStream_t s) {
+  if (head_dim == 64) return launch_fwd_d<T, 64>(p, mode, s);
+  if (head_dim == 128) return launch_fwd_d<T, 128>(p, mode, s);
+  return hipErrorInvalidValue;
+}
+
+template hipError_t launch_attn_fwd<bf16>(const AttnFwd<bf16>&, int, int, hipStream_t);
+template hipError_t launch_attn_fwd<float>(const AttnFwd<float>&, int, int, hipStream_t);
+
+}  // namespace upipe

@@ -1,0 +1,156 @@
+// Device helpers shared by the gfx950 kernels: element types, MFMA fragments,
+// LDS tile geometry.
+//
+// MFMA operand convention used throughout (v_mfma_f32_32x32x16_bf16 and
+// v_mfma_f32_32x32x2f32, both with a 32x32 fp32 accumulator):
+//   A operand: lane l supplies row m = l % 32 and the 8 k-values 8*(l/32)..+7
+//              of a 16-wide k step;
+//   B operand: lane l supplies column n = l % 32 and the same 8 k-values;
+//   C/D:       lane l holds column n = l % 32, rows 8*i + 4*(l/32) + j at
+//              accumulator index 4*i + j (i, j in 0..3).
+// A "Frag" is those 8 k-values of one lane. For bf16 one 32x32x16 MFMA
+// consumes a Frag pair; for fp32 eight 32x32x2 MFMAs do (instruction t takes
+// element t of each half-wave, so the two half-waves cover k = t and 8 + t).
+// Because a contraction does not care how k is numbered, a C tile whose rows
+// are the contraction index can feed the next MFMA directly as a B operand:
+// step s (16 rows) of the tile is accumulator elements 8*s .. 8*s+7, whose
+// physical rows are 16*s + 8*(e/4) + 4*(l/32) + (e%4) for element e. The
+// matching A operand then reads those same rows (two runs of 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+#define DEV __device__ __forceinline__
+
+DEV int lane_id() { return (int)(threadIdx.x & 63); }
+DEV int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+// 8 contiguous elements at p (16-byte aligned for bf16, 16-byte aligned halves for fp32).
+template <typename T> DEV Frag<T> ld_frag(const T* p);
+template <> DEV Frag<bf16> ld_frag<bf16>(const bf16* p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+template <> DEV Frag<float> ld_frag<float>(const float* p) {
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+
+// elements 0..3 from p0 and 4..7 from p1 (each run of 4 contiguous).
+template <typename T> DEV Frag<T> ld_frag2(const T* p0, const T* p1);
+template <> DEV Frag<bf16> ld_frag2<bf16>(const bf16* p0, const bf16* p1) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  Frag<bf16> f;
+  f.v = (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+template <> DEV Frag<float> ld_frag2<float>(const float* p0, const float* p1) {
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p0);
+  f.hi = *reinterpret_cast<const f32x4*>(p1);
+  return f;
+}
+
+// Accumulator elements 8*s .. 8*s+7 of a C tile as a B (or A) operand, times mul.
+template <typename T> DEV Frag<T> frag_from_acc(const f32x16& c, int s, float mul);
+template <> DEV Frag<bf16> frag_from_acc<bf16>(const f32x16& c, int s, float mul) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)(c[8 * s + e] * mul);
+  return f;
+}
+template <> DEV Frag<float> frag_from_acc<float>(const f32x16& c, int s, float mul) {
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.lo[e] = c[8 * s + e] * mul;
+    f.hi[e] = c[8 * s + 4 + e] * mul;
+  }
+  return f;
+}
+
+// c += A * B over one 16-wide k step.
+template <typename T> DEV void mma(f32x16& c, const Frag<T>& a, const Frag<T>& b);
+template <> DEV void mma<bf16>(f32x16& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+template <> DEV void mma<float>(f32x16& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[t], b.lo[t], c, 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[t], b.hi[t], c, 0, 0, 0);
+}
+
+DEV f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// ---- scalar conversions -------------------------------------------------
+template <typename T> DEV float to_f(T v);
+template <> DEV float to_f<float>(float v) { return v; }
+template <> DEV float to_f<bf16>(bf16 v) { return (float)v; }
+template <typename T> DEV T from_f(float v);
+template <> DEV float from_f<float>(float v) { return v; }
+template <> DEV bf16 from_f<bf16>(float v) { return (bf16)v; }
+
+// 16-byte vector of T: VEC elements.
+template <typename T> struct Vec16 { static constexpr int N = 16 / sizeof(T); };
+
+// Load VEC (=16/sizeof(T)) elements from 16-byte aligned p as floats.
+template <typename T> DEV void ld16_f(const T* p, float* out);
+template <> DEV void ld16_f<bf16>(const bf16* p, float* out) {
+  bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+}
+template <> DEV void ld16_f<float>(const float* p, float* out) {
+  f32x4 v = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = v[i];
+}
+template <typename T> DEV void st16_f(T* p, const float* in);
+template <> DEV void st16_f<bf16>(bf16* p, const float* in) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (bf16)in[i];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+template <> DEV void st16_f<float>(float* p, const float* in) {
+  f32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = in[i];
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// Raw 16-byte copy unit.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+DEV u32x4 ld_raw16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+DEV void st_raw16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+DEV u32x4 zero_raw16() { return (u32x4){0u, 0u, 0u, 0u}; }
+
+// LDS row stride (in elements) for a tile with `cols` columns: 16 bytes of
+// padding per row so consecutive rows start 4 banks apart.
+template <typename T> constexpr int lds_stride(int cols) { return cols + 16 / (int)sizeof(T); }
+
+DEV float wave_max_pair(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

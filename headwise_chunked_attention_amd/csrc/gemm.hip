@@ -1,0 +1,410 @@
+// Projection GEMMs of the chunk loop on gfx950 MFMA.
+//
+// gemm_nt: C = A B^T with both operands contiguous along k. Used for the
+//   chunk's Q/K/V projection (x Wq_c^T, with the per-head RMSNorm + RoPE
+//   epilogue), for y (+)= O_c Wo_c^T, for dO_c = dY Wo_c and for
+//   dx (+)= dq_c Wq_c. 128 x BN tile, 4 waves in 2 x 2, each wave 64 x BN/2 of
+//   32x32 MFMA tiles, k staged through LDS in 128-byte rows (double buffer).
+// gemm_tn: out += A^T B with both operands contiguous along the free dims and
+//   k = tokens; the weight gradients (dWq = dq^T x, dWo = dY^T O, ...). Each
+//   workgroup takes one 128 x BN output tile over one slice of the tokens
+//   (split-K), transposes its tiles into k-contiguous LDS rows on the way in
+//   and adds its partial sum into the fp32 output with atomics.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace upipe {
+
+namespace {
+
+constexpr int BM = 128;
+constexpr int NTHREADS = 256;
+
+template <typename T> struct GemmGeo {
+  static constexpr int BK = 128 / (int)sizeof(T);  // 128 bytes of k per row
+  static constexpr int SK = lds_stride<T>(BK);
+  static constexpr int VEC = 16 / (int)sizeof(T);
+};
+
+template <typename T, int BN>
+constexpr int gemm_smem_bytes() {
+  constexpr int main_bytes = 2 * (BM + BN) * GemmGeo<T>::SK * (int)sizeof(T);
+  constexpr int epi_bytes = BM * (BN + 4) * 4;
+  return main_bytes > epi_bytes ? main_bytes : epi_bytes;
+}
+
+// One 16-wide k step of a 2 x 2 wave grid over a BM x BN tile held in LDS as
+// As[m][k], Bs[n][k] (row stride SK).
+template <typename T, int BN>
+DEV void mma_tile_step(const T* As, const T* Bs, int SK, int ks, int wm, int wn,
+                       f32x16 (&acc)[2][BN / 64]) {
+  constexpr int NTW = BN / 64;
+  const int l = lane_id();
+  const int r = l & 31, h = l >> 5;
+  Frag<T> a[2], b[NTW];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) a[mt] = ld_frag(As + (wm * 64 + mt * 32 + r) * SK + ks * 16 + 8 * h);
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) b[nt] = ld_frag(Bs + (wn * (BN / 2) + nt * 32 + r) * SK + ks * 16 + 8 * h);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) mma(acc[mt][nt], a[mt], b[nt]);
+}
+
+// Accumulators -> fp32 LDS tile Cs[BM][BN + 4].
+template <int BN>
+DEV void acc_to_lds(float* Cs, int wm, int wn, const f32x16 (&acc)[2][BN / 64]) {
+  constexpr int NTW = BN / 64, SC = BN + 4;
+  const int l = lane_id();
+  const int col0 = wn * (BN / 2) + (l & 31), h = l >> 5;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          Cs[(wm * 64 + mt * 32 + 8 * i + 4 * h + j) * SC + col0 + nt * 32] = acc[mt][nt][4 * i + j];
+}
+
+template <typename T, int BN>
+DEV void nt_load_tile(const GemmNT<T>& p, const T* bptr, int64_t ldb, int64_t m0, int64_t nrow0,
+                      int64_t k0, u32x4 (&ra)[BM * 8 / NTHREADS], u32x4 (&rb)[BN * 8 / NTHREADS]) {
+  constexpr int VEC = GemmGeo<T>::VEC;
+  const int tid = threadIdx.x;
+  const T* abase = p.a + (k0 / p.a_kblk) * p.a_kblk_stride + (k0 % p.a_kblk);
+#pragma unroll
+  for (int i = 0; i < BM * 8 / NTHREADS; ++i) {
+    const int c = tid + i * NTHREADS;
+    const int row = c >> 3, cc = c & 7;
+    const int64_t m = m0 + row;
+    ra[i] = (m < p.M) ? ld_raw16(abase + m * p.lda + cc * VEC) : zero_raw16();
+  }
+#pragma unroll
+  for (int i = 0; i < BN * 8 / NTHREADS; ++i) {
+    const int c = tid + i * NTHREADS;
+    const int row = c >> 3, cc = c & 7;
+    rb[i] = ld_raw16(bptr + (nrow0 + row) * ldb + k0 + cc * VEC);
+  }
+}
+
+template <typename T, int BN>
+DEV void nt_store_tile(T* As, T* Bs, const u32x4 (&ra)[BM * 8 / NTHREADS],
+                       const u32x4 (&rb)[BN * 8 / NTHREADS]) {
+  constexpr int VEC = GemmGeo<T>::VEC, SK = GemmGeo<T>::SK;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < BM * 8 / NTHREADS; ++i) {
+    const int c = tid + i * NTHREADS;
+    st_raw16(As + (c >> 3) * SK + (c & 7) * VEC, ra[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < BN * 8 / NTHREADS; ++i) {
+    const int c = tid + i * NTHREADS;
+    st_raw16(Bs + (c >> 3) * SK + (c & 7) * VEC, rb[i]);
+  }
+}
+
+template <typename T, int BN, int EPI>
+__global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
+  constexpr int BK = GemmGeo<T>::BK, SK = GemmGeo<T>::SK, VEC = GemmGeo<T>::VEC;
+  constexpr int NTW = BN / 64, SC = BN + 4;
+  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<T, BN>()];
+  T* As = reinterpret_cast<T*>(smem);
+  T* Bs = As + 2 * BM * SK;
+
+  const int64_t ntn = p.N / BN;
+  const int64_t bid = blockIdx.x;
+  const int64_t mtile = bid / ntn, ntile = bid % ntn;
+  const int64_t m0 = mtile * BM, n0 = ntile * BN;
+  int seg = 0;
+  while (seg + 1 < p.nseg && n0 >= p.seg_end[seg]) ++seg;
+  const int64_t seg_begin = seg ? p.seg_end[seg - 1] : 0;
+  const T* bptr = p.b[seg];
+  const int64_t ldb = p.ldb[seg];
+  const int64_t nrow0 = n0 - seg_begin;
+
+  const int w = wave_id();
+  const int wm = w >> 1, wn = w & 1;
+  f32x16 acc[2][NTW];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = zero16();
+
+  u32x4 ra[BM * 8 / NTHREADS], rb[BN * 8 / NTHREADS];
+  const int64_t nk = p.K / BK;
+  nt_load_tile<T, BN>(p, bptr, ldb, m0, nrow0, 0, ra, rb);
+  nt_store_tile<T, BN>(As, Bs, ra, rb);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    if (kt + 1 < nk) nt_load_tile<T, BN>(p, bptr, ldb, m0, nrow0, (kt + 1) * BK, ra, rb);
+    // LDS holds [A0][A1][B0][B1]
+    const T* Ab = As + buf * BM * SK;
+    const T* Bb = Bs + buf * BN * SK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) mma_tile_step<T, BN>(Ab, Bb, SK, ks, wm, wn, acc);
+    if (kt + 1 < nk) nt_store_tile<T, BN>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra, rb);
+    __syncthreads();
+  }
+
+  float* Cs = reinterpret_cast<float*>(smem);
+  acc_to_lds<BN>(Cs, wm, wn, acc);
+  __syncthreads();
+  const int tid = threadIdx.x;
+
+  if constexpr (EPI == EPI_ACCUM) {
+    for (int c = tid; c < BM * BN / VEC; c += NTHREADS) {
+      const int row = c / (BN / VEC), cv = c % (BN / VEC);
+      const int64_t m = m0 + row;
+      if (m >= p.M) continue;
+      float v[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+      T* dst = p.c + m * p.ldc + n0 + cv * VEC;
+      if (p.accumulate) {
+        float old[VEC];
+        ld16_f<T>(dst, old);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] += old[e];
+      }
+      st16_f<T>(dst, v);
+    }
+  } else {
+    const HeadOut<T> ho = p.ho[seg];
+    const int64_t head = nrow0 / BN;
+    if (ho.pre) {
+      T* dst = ho.pre + head * p.Np * BN + m0 * BN;
+      for (int c = tid; c < BM * BN / VEC; c += NTHREADS) {
+        const int row = c / (BN / VEC), cv = c % (BN / VEC);
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+        st16_f<T>(dst + row * BN + cv * VEC, v);
+      }
+      __syncthreads();
+    }
+    if (ho.gamma || ho.rope) {
+      // two threads per row; thread half covers pairs [half*BN/4, half*BN/4 + BN/4)
+      const int row = tid >> 1, half = tid & 1;
+      float* cr = Cs + row * SC;
+      constexpr int PP = BN / 4;
+      if (ho.gamma) {
+        float ss = 0.f;
+#pragma unroll 4
+        for (int i = half * PP; i < half * PP + PP; ++i) ss += cr[i] * cr[i] + cr[i + BN / 2] * cr[i + BN / 2];
+        ss += __shfl_xor(ss, 1);
+        const float r = 1.0f / sqrtf(ss / (float)BN + p.eps);
+        for (int i = half * PP; i < half * PP + PP; ++i) {
+          cr[i] = to_f<T>(ho.gamma[i]) * (cr[i] * r);
+          cr[i + BN / 2] = to_f<T>(ho.gamma[i + BN / 2]) * (cr[i + BN / 2] * r);
+        }
+      }
+      if (ho.rope) {
+        const double pos = (double)(m0 + row);
+        for (int i = half * PP; i < half * PP + PP; ++i) {
+          const double omega = exp2(-(2.0 * i / BN) * p.log2_theta);
+          double sd, cd;
+          sincos(pos * omega, &sd, &cd);
+          const float c = (float)cd, s = (float)sd;
+          const float u = cr[i], wv = cr[i + BN / 2];
+          cr[i] = u * c - wv * s;
+          cr[i + BN / 2] = wv * c + u * s;
+        }
+      }
+      __syncthreads();
+    }
+    if (ho.rm) {
+      T* dst = ho.rm + head * p.Np * BN + m0 * BN;
+      for (int c = tid; c < BM * BN / VEC; c += NTHREADS) {
+        const int row = c / (BN / VEC), cv = c % (BN / VEC);
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+        st16_f<T>(dst + row * BN + cv * VEC, v);
+      }
+    }
+    if (ho.tr) {
+      T* dst = ho.tr + head * BN * p.Np + m0;
+      for (int c = tid; c < BN * (BM / VEC); c += NTHREADS) {
+        const int col = c / (BM / VEC), rv = c % (BM / VEC);
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] = Cs[(rv * VEC + e) * SC + col];
+        st16_f<T>(dst + col * p.Np + rv * VEC, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// split-K GEMM for weight gradients
+// ------------------------------------------------------------------------
+template <typename T> DEV void st_pair(T* p, float a, float b);
+template <> DEV void st_pair<bf16>(bf16* p, float a, float b) {
+  *reinterpret_cast<bf16x2*>(p) = (bf16x2){(bf16)a, (bf16)b};
+}
+template <> DEV void st_pair<float>(float* p, float a, float b) {
+  *reinterpret_cast<f32x2*>(p) = (f32x2){a, b};
+}
+
+// Units of (token pair, VEC columns): loads two 16-byte rows, stores VEC
+// transposed pairs into LDS rows [col][tok].
+template <typename T, int COLS>
+struct TnTile {
+  static constexpr int VEC = GemmGeo<T>::VEC, BK = GemmGeo<T>::BK;
+  static constexpr int UNITS = (BK / 2) * (COLS / VEC);
+  static constexpr int PER = (UNITS + NTHREADS - 1) / NTHREADS;
+};
+
+template <typename T, int COLS, typename AddrFn>
+DEV void tn_load(AddrFn addr, int64_t k0, int64_t K, float (&r)[TnTile<T, COLS>::PER][2][16 / sizeof(T)]) {
+  using G = TnTile<T, COLS>;
+  constexpr int VEC = G::VEC;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < G::PER; ++i) {
+    const int u = tid + i * NTHREADS;
+    if (u >= G::UNITS) break;
+    const int pr = u % (G::BK / 2), cc = u / (G::BK / 2);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t k = k0 + 2 * pr + t;
+      if (k < K) {
+        ld16_f<T>(addr(k, cc * VEC), r[i][t]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) r[i][t][e] = 0.f;
+      }
+    }
+  }
+}
+
+template <typename T, int COLS>
+DEV void tn_store(T* S, const float (&r)[TnTile<T, COLS>::PER][2][16 / sizeof(T)]) {
+  using G = TnTile<T, COLS>;
+  constexpr int VEC = G::VEC, SK = GemmGeo<T>::SK;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < G::PER; ++i) {
+    const int u = tid + i * NTHREADS;
+    if (u >= G::UNITS) break;
+    const int pr = u % (G::BK / 2), cc = u / (G::BK / 2);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) st_pair<T>(S + (cc * VEC + e) * SK + 2 * pr, r[i][0][e], r[i][1][e]);
+  }
+}
+
+template <typename T, int BN>
+__global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
+  constexpr int BK = GemmGeo<T>::BK, SK = GemmGeo<T>::SK;
+  constexpr int NTW = BN / 64, SC = BN + 4;
+  constexpr int VEC = GemmGeo<T>::VEC;
+  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<T, BN>()];
+  T* As = reinterpret_cast<T*>(smem);       // [2][BM][SK]
+  T* Bs = As + 2 * BM * SK;                 // [2][BN][SK]
+
+  const int64_t m0 = (int64_t)blockIdx.x * BM;
+  const int64_t n0 = (int64_t)blockIdx.y * BN;
+  const int64_t kb = (int64_t)blockIdx.z * p.ksplit;
+  const int64_t ke = (kb + p.ksplit < p.K) ? kb + p.ksplit : p.K;
+
+  auto aaddr = [&](int64_t k, int col) { return p.a + k * p.lda + m0 + col; };
+  auto baddr = [&](int64_t k, int col) {
+    const int64_t n = n0 + col;
+    return p.b + (n / p.b_nblk) * p.b_nblk_stride + k * p.ldb + (n % p.b_nblk);
+  };
+
+  const int w = wave_id();
+  const int wm = w >> 1, wn = w & 1;
+  f32x16 acc[2][NTW];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = zero16();
+
+  float ra[TnTile<T, BM>::PER][2][VEC];
+  float rb[TnTile<T, BN>::PER][2][VEC];
+  const int64_t nk = (ke - kb + BK - 1) / BK;
+  tn_load<T, BM>(aaddr, kb, ke, ra);
+  tn_load<T, BN>(baddr, kb, ke, rb);
+  tn_store<T, BM>(As, ra);
+  tn_store<T, BN>(Bs, rb);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    if (kt + 1 < nk) {
+      tn_load<T, BM>(aaddr, kb + (kt + 1) * BK, ke, ra);
+      tn_load<T, BN>(baddr, kb + (kt + 1) * BK, ke, rb);
+    }
+    const T* Ab = As + buf * BM * SK;
+    const T* Bb = Bs + buf * BN * SK;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) mma_tile_step<T, BN>(Ab, Bb, SK, ks, wm, wn, acc);
+    if (kt + 1 < nk) {
+      tn_store<T, BM>(As + (buf ^ 1) * BM * SK, ra);
+      tn_store<T, BN>(Bs + (buf ^ 1) * BN * SK, rb);
+    }
+    __syncthreads();
+  }
+
+  float* Cs = reinterpret_cast<float*>(smem);
+  acc_to_lds<BN>(Cs, wm, wn, acc);
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (p.ldn == 1) {
+    for (int c = tid; c < BM * BN; c += NTHREADS) {
+      const int row = c / BN, col = c % BN;
+      atomicAdd(p.out + (m0 + row) * p.ldm + (n0 + col), Cs[row * SC + col]);
+    }
+  } else {
+    for (int c = tid; c < BM * BN; c += NTHREADS) {
+      const int col = c / BM, row = c % BM;
+      atomicAdd(p.out + (m0 + row) * p.ldm + (n0 + col) * p.ldn, Cs[row * SC + col]);
+    }
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
+  const int64_t mt = (epi == EPI_HEADS ? p.Np : p.M + BM - 1) / BM;
+  const int64_t grid = mt * (p.N / bn);
+  if (grid <= 0) return hipSuccess;
+  if (epi == EPI_ACCUM && bn == 128)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_ACCUM>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else if (epi == EPI_ACCUM && bn == 64)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 64, EPI_ACCUM>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else if (epi == EPI_HEADS && bn == 128)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_HEADS>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else if (epi == EPI_HEADS && bn == 64)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 64, EPI_HEADS>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s) {
+  const dim3 grid((unsigned)(p.M / BM), (unsigned)(p.N / bn), (unsigned)((p.K + p.ksplit - 1) / p.ksplit));
+  if (bn == 128)
+    hipLaunchKernelGGL((gemm_tn_kernel<T, 128>), grid, dim3(NTHREADS), 0, s, p);
+  else if (bn == 64)
+    hipLaunchKernelGGL((gemm_tn_kernel<T, 64>), grid, dim3(NTHREADS), 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template hipError_t launch_gemm_nt<bf16>(const GemmNT<bf16>&, int, int, hipStream_t);
+template hipError_t launch_gemm_nt<float>(const GemmNT<float>&, int, int, hipStream_t);
+template hipError_t launch_gemm_tn<bf16>(const GemmTN<bf16>&, int, hipStream_t);
+template hipError_t launch_gemm_tn<float>(const GemmTN<float>&, int, hipStream_t);
+
+}  // namespace upipe

@@ -1,0 +1,136 @@
+// Host-side launch interface of the gfx950 kernels (argument blocks + launchers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+
+namespace upipe {
+
+enum { EPI_ACCUM = 0, EPI_HEADS = 1 };
+
+// Where one group of heads produced by a projection GEMM goes. A head is one
+// N-tile of the GEMM (BN == head_dim).
+template <typename T>
+struct HeadOut {
+  T* rm;           // [heads][Np][d] row-major, or null
+  T* tr;           // [heads][d][Np] transposed, or null
+  T* pre;          // [heads][Np][d] values before norm/RoPE, or null
+  const T* gamma;  // [d] RMSNorm weight (norm applied iff non-null)
+  int rope;        // rotate (i, i + d/2) pairs by pos * theta^(-2i/d)
+};
+
+// C[m][n] = sum_k A(m,k) B(n,k), both operands contiguous along k.
+//   A(m,k) = a + (k / a_kblk) * a_kblk_stride + m * lda + (k % a_kblk)
+//   B(n,k) = b[s] + (n - seg_begin(s)) * ldb[s] + k for the segment s holding n
+// EPI_ACCUM:  c[m * ldc + n] = (accumulate ? c : 0) + C   (rows m < M)
+// EPI_HEADS:  head-wise epilogue per segment (see HeadOut), rows m < Np.
+template <typename T>
+struct GemmNT {
+  const T* a;
+  int64_t lda;
+  int64_t a_kblk;
+  int64_t a_kblk_stride;
+  const T* b[3];
+  int64_t ldb[3];
+  int64_t seg_end[3];  // cumulative end of each segment along N
+  int nseg;
+  int64_t M, N, K;
+  T* c;
+  int64_t ldc;
+  int accumulate;
+  HeadOut<T> ho[3];
+  int64_t Np;
+  float eps;
+  double log2_theta;
+};
+
+// out[m*ldm + n*ldn] += sum_{k in split} A(k,m) B(k,n)   (fp32 atomics)
+//   A(k,m) = a + k * lda + m
+//   B(k,n) = b + (n / b_nblk) * b_nblk_stride + k * ldb + (n % b_nblk)
+template <typename T>
+struct GemmTN {
+  const T* a;
+  int64_t lda;
+  const T* b;
+  int64_t b_nblk;
+  int64_t b_nblk_stride;
+  int64_t ldb;
+  int64_t M, N, K;
+  int64_t ksplit;
+  float* out;
+  int64_t ldm, ldn;
+};
+
+// Causal GQA attention forward over one kv head and `nh` q heads.
+//   q, o   [nh][Np][D]     k [Np][D]     vt [D][Np]
+//   lse    [nh] rows of stride lse_stride (caller's [Hq][N]), fp32
+// mode 0: online softmax, writes o (normalised) and lse.
+// mode 1: reads lse, writes o and delta[h][i] = sum_d dO[h][i][d] * O[h][i][d].
+template <typename T>
+struct AttnFwd {
+  const T* q;
+  const T* k;
+  const T* vt;
+  T* o;
+  float* lse;
+  int64_t lse_stride;
+  const T* dout;  // mode 1
+  float* delta;   // mode 1, [nh][Np]
+  int64_t N, Np;
+  int nh;
+  float scale_log2;  // log2(e) / sqrt(D)
+};
+
+// Causal GQA attention backward over one kv head and `nh` q heads.
+//   q, dout [nh][Np][D]; k, v [Np][D]; lse [nh] rows of stride lse_stride;
+//   delta [nh][Np]; dq_acc [nh][Np][D] fp32 (atomically accumulated);
+//   dk_acc, dv_acc [Np][D] fp32 (written, or added to when accumulate).
+template <typename T>
+struct AttnBwd {
+  const T* q;
+  const T* k;
+  const T* v;
+  const T* dout;
+  const float* lse;
+  int64_t lse_stride;
+  const float* delta;
+  float* dq_acc;
+  float* dk_acc;
+  float* dv_acc;
+  int64_t N, Np;
+  int nh;
+  int accumulate;
+  float scale_log2;  // log2(e) / sqrt(D)
+  float scale;       // 1 / sqrt(D)
+};
+
+// Per-row gradient finish for heads stored [nh][Np][D]:
+//   g = rope^T(gacc) if rope; g = rmsnorm_bwd(u, gamma, g) if gamma (dgamma += ...);
+//   out = g in io dtype; rows >= N are written as zero.
+template <typename T>
+struct GradFinish {
+  const float* gacc;
+  const T* u;
+  const T* gamma;
+  float* dgamma;
+  T* out;
+  int rope;
+  int nh;
+  int64_t N, Np;
+  float eps;
+  double log2_theta;
+};
+
+template <typename T> hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s);
+template <typename T> hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s);
+template <typename T> hipError_t launch_attn_fwd(const AttnFwd<T>& p, int head_dim, int mode, hipStream_t s);
+template <typename T> hipError_t launch_attn_bwd(const AttnBwd<T>& p, int head_dim, hipStream_t s);
+template <typename T> hipError_t launch_grad_finish(const GradFinish<T>& p, int head_dim, hipStream_t s);
+template <typename T>
+hipError_t launch_transpose(const T* src, int64_t rows, int64_t cols, int64_t ld_src, T* dst,
+                            int64_t ld_dst, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+}  // namespace upipe

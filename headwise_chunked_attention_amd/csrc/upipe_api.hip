@@ -1,0 +1,539 @@
+// Host engine behind the C ABI: argument validation, the workspace plan and
+// the chunk loop that enqueues the gfx950 kernels.
+//
+// The chunk loop is the method itself: the heads one GPU owns are split into
+// chunks of `chunk_heads` query heads that run one after another; each chunk
+// recomputes its Q (and, at the first chunk of a kv group, that group's K and
+// V), runs attention over the full sequence, stores its partial result into
+// y, and the next chunk reuses the same buffers ("500 万トークンへの道 — Max
+// Ryabinin (Together AI) の Untied Ulysses", section "Untied Ulysses (UPipe) —
+// head 単位のチャンク化"; "Road to 5 Million Tokens", section "Primary
+// Contribution"). Only per-chunk buffers live in the workspace, so its size
+// grows with chunk_heads and not with the number of heads.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "upipe.h"
+#include "kernels.h"
+
+using namespace upipe;
+
+namespace {
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+constexpr int64_t ROW_PAD = 256;   // token rows of per-head buffers are padded to this
+constexpr size_t REGION_ALIGN = 256;
+
+struct Shape {
+  int64_t N, D, Np;
+  int Hq, Hkv, d, C, G, kvC;
+  bool norm;
+  int es;  // element size of the io dtype
+};
+
+// Workspace regions (byte offsets). Forward uses q, k (K then V^T follow), o.
+// Backward aliases: the dq of a chunk overwrites q, dk|dv overwrite k|v.
+struct Plan {
+  size_t q, uq, k, v, uk, vt, dout, o, delta, dq_acc, dk_acc, dv_acc, wo_t, wq_t, wkv_t;
+  size_t total;
+};
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t at = off;
+    off += (bytes + REGION_ALIGN - 1) / REGION_ALIGN * REGION_ALIGN;
+    return at;
+  }
+};
+
+Plan make_plan(const Shape& s, bool backward) {
+  Plan p;
+  memset(&p, 0, sizeof(p));
+  const size_t head = (size_t)s.Np * s.d;  // elements of one [Np][d] head buffer
+  Carver c;
+  p.q = c.take(head * s.C * s.es);
+  if (!backward) {
+    p.k = c.take(head * s.kvC * s.es);
+    p.vt = c.take(head * s.kvC * s.es);
+    p.o = c.take(head * s.C * s.es);
+    p.total = c.off;
+    return p;
+  }
+  if (s.norm) p.uq = c.take(head * s.C * s.es);
+  p.k = c.take(head * 2 * s.kvC * s.es);  // K then V, contiguous (dk|dv alias them)
+  p.v = p.k + head * s.kvC * s.es;
+  if (s.norm) p.uk = c.take(head * s.kvC * s.es);
+  p.vt = c.take(head * s.kvC * s.es);
+  p.dout = c.take(head * s.C * s.es);
+  p.o = c.take(head * s.C * s.es);
+  p.delta = c.take((size_t)s.Np * s.C * 4);
+  p.dq_acc = c.take(head * s.C * 4);
+  p.dk_acc = c.take(head * s.kvC * 4);
+  p.dv_acc = c.take(head * s.kvC * 4);
+  p.wo_t = c.take((size_t)s.C * s.d * s.D * s.es);
+  p.wq_t = c.take((size_t)s.C * s.d * s.D * s.es);
+  p.wkv_t = c.take((size_t)2 * s.kvC * s.d * s.D * s.es);
+  p.total = c.off;
+  return p;
+}
+
+int check_shape(int dtype, int64_t N, int64_t D, int Hq, int Hkv, int d, int C, Shape* out) {
+  if (dtype != UPIPE_F32 && dtype != UPIPE_BF16) return UPIPE_ERR_INVALID_ARG;
+  if (N < 1 || D < 1 || Hq < 1 || Hkv < 1 || C < 1 || d < 1) return UPIPE_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return UPIPE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return UPIPE_ERR_UNSUPPORTED;
+  if (D % 128 != 0) return UPIPE_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (Hq % C != 0) return UPIPE_ERR_UNSUPPORTED;
+  if (C % G != 0 && G % C != 0) return UPIPE_ERR_UNSUPPORTED;
+  if (N > ((int64_t)1 << 40) || D > ((int64_t)1 << 20)) return UPIPE_ERR_UNSUPPORTED;
+  Shape s;
+  s.N = N;
+  s.D = D;
+  s.Np = round_up(N, ROW_PAD);
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.d = d;
+  s.C = C;
+  s.G = G;
+  s.kvC = C > G ? C / G : 1;
+  s.norm = false;
+  s.es = dtype == UPIPE_BF16 ? 2 : 4;
+  *out = s;
+  return UPIPE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define HIP_TRY(x)                                 \
+  do {                                             \
+    if ((x) != hipSuccess) return UPIPE_ERR_HIP;   \
+  } while (0)
+
+template <typename T>
+GemmNT<T> gemm_base() {
+  GemmNT<T> g;
+  memset(&g, 0, sizeof(g));
+  g.nseg = 1;
+  return g;
+}
+
+// Projection of rows x[N][D] onto the heads described by up to 3 segments.
+template <typename T>
+int run_projection(const Shape& s, const T* x, int nseg, const T* const* w, const int* nheads,
+                   const HeadOut<T>* ho, float eps, double log2_theta, hipStream_t st) {
+  GemmNT<T> g = gemm_base<T>();
+  g.a = x;
+  g.lda = s.D;
+  g.a_kblk = s.D;
+  g.a_kblk_stride = 0;
+  int64_t n = 0;
+  for (int i = 0; i < nseg; ++i) {
+    g.b[i] = w[i];
+    g.ldb[i] = s.D;
+    n += (int64_t)nheads[i] * s.d;
+    g.seg_end[i] = n;
+    g.ho[i] = ho[i];
+  }
+  g.nseg = nseg;
+  g.M = s.N;
+  g.N = n;
+  g.K = s.D;
+  g.Np = s.Np;
+  g.eps = eps;
+  g.log2_theta = log2_theta;
+  HIP_TRY(launch_gemm_nt<T>(g, EPI_HEADS, s.d, st));
+  return UPIPE_OK;
+}
+
+// out[N][D] (+)= A_heads[nheads][Np][d] (as [N][nheads*d]) x B^T, B(n,k) = b + n*ldb + k
+template <typename T>
+int run_heads_times_wt(const Shape& s, const T* a_heads, int nheads, const T* b, int64_t ldb, T* out,
+                       int accumulate, hipStream_t st) {
+  GemmNT<T> g = gemm_base<T>();
+  g.a = a_heads;
+  g.lda = s.d;
+  g.a_kblk = s.d;
+  g.a_kblk_stride = s.Np * s.d;
+  g.b[0] = b;
+  g.ldb[0] = ldb;
+  g.seg_end[0] = s.D;
+  g.M = s.N;
+  g.N = s.D;
+  g.K = (int64_t)nheads * s.d;
+  g.c = out;
+  g.ldc = s.D;
+  g.accumulate = accumulate;
+  HIP_TRY(launch_gemm_nt<T>(g, EPI_ACCUM, 128, st));
+  return UPIPE_OK;
+}
+
+// Weight gradient out[m*ldm + n*ldn] += sum_tok rows[tok][m] * heads[n/d][tok][n%d]
+template <typename T>
+int run_weight_grad(const Shape& s, const T* rows, const T* heads, int nheads, float* out, int64_t ldm,
+                    int64_t ldn, hipStream_t st) {
+  GemmTN<T> g;
+  memset(&g, 0, sizeof(g));
+  g.a = rows;
+  g.lda = s.D;
+  g.b = heads;
+  g.b_nblk = s.d;
+  g.b_nblk_stride = s.Np * s.d;
+  g.ldb = s.d;
+  g.M = s.D;
+  g.N = (int64_t)nheads * s.d;
+  g.K = s.N;
+  const int bn = (g.N % 128 == 0) ? 128 : 64;
+  const int64_t tiles = (g.M / 128) * (g.N / bn);
+  int64_t splits = 1024 / (tiles > 0 ? tiles : 1);
+  if (splits < 1) splits = 1;
+  g.ksplit = round_up((s.N + splits - 1) / splits, 64);
+  g.out = out;
+  g.ldm = ldm;
+  g.ldn = ldn;
+  HIP_TRY(launch_gemm_tn<T>(g, bn, st));
+  return UPIPE_OK;
+}
+
+template <typename T>
+int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T* wk, const T* wv,
+                  const T* wo, const T* qn, const T* kn, float eps, T* y, float* lse, char* ws,
+                  hipStream_t st) {
+  const Plan pl = make_plan(s, false);
+  T* Q = reinterpret_cast<T*>(ws + pl.q);
+  T* K = reinterpret_cast<T*>(ws + pl.k);
+  T* Vt = reinterpret_cast<T*>(ws + pl.vt);
+  T* O = reinterpret_cast<T*>(ws + pl.o);
+  const double l2t = log2(theta);
+  const int64_t head = s.Np * s.d;
+  const int nh = s.C < s.G ? s.C : s.G;  // q heads of the chunk per kv head
+  for (int c0 = 0; c0 < s.Hq; c0 += s.C) {
+    const int g0 = c0 / s.G;
+    const bool new_kv = (c0 % s.G) == 0;
+    const T* w[3] = {wq + (int64_t)c0 * s.d * s.D, wk + (int64_t)g0 * s.d * s.D, wv + (int64_t)g0 * s.d * s.D};
+    const int nheads[3] = {s.C, s.kvC, s.kvC};
+    HeadOut<T> ho[3];
+    memset(ho, 0, sizeof(ho));
+    ho[0].rm = Q;
+    ho[0].gamma = qn;
+    ho[0].rope = 1;
+    ho[1].rm = K;
+    ho[1].gamma = kn;
+    ho[1].rope = 1;
+    ho[2].tr = Vt;
+    int rc = run_projection<T>(s, x, new_kv ? 3 : 1, w, nheads, ho, eps, l2t, st);
+    if (rc) return rc;
+    for (int j = 0; j < s.kvC; ++j) {
+      AttnFwd<T> a;
+      memset(&a, 0, sizeof(a));
+      a.q = Q + (int64_t)j * nh * head;
+      a.k = K + (int64_t)j * head;
+      a.vt = Vt + (int64_t)j * head;
+      a.o = O + (int64_t)j * nh * head;
+      a.lse = lse + (int64_t)(c0 + j * nh) * s.N;
+      a.lse_stride = s.N;
+      a.N = s.N;
+      a.Np = s.Np;
+      a.nh = nh;
+      a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.d));
+      HIP_TRY(launch_attn_fwd<T>(a, s.d, 0, st));
+    }
+    rc = run_heads_times_wt<T>(s, O, s.C, wo + (int64_t)c0 * s.d, (int64_t)s.Hq * s.d, y, c0 > 0, st);
+    if (rc) return rc;
+  }
+  return UPIPE_OK;
+}
+
+template <typename T>
+int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T* wk, const T* wv,
+                  const T* wo, const T* qn, const T* kn, float eps, const T* dy, const float* lse,
+                  T* dx, float* dwq, float* dwk, float* dwv, float* dwo, float* dqn, float* dkn,
+                  char* ws, hipStream_t st) {
+  const Plan pl = make_plan(s, true);
+  T* Q = reinterpret_cast<T*>(ws + pl.q);
+  T* Uq = s.norm ? reinterpret_cast<T*>(ws + pl.uq) : nullptr;
+  T* K = reinterpret_cast<T*>(ws + pl.k);
+  T* V = reinterpret_cast<T*>(ws + pl.v);
+  T* Uk = s.norm ? reinterpret_cast<T*>(ws + pl.uk) : nullptr;
+  T* Vt = reinterpret_cast<T*>(ws + pl.vt);
+  T* dO = reinterpret_cast<T*>(ws + pl.dout);
+  T* O = reinterpret_cast<T*>(ws + pl.o);
+  float* Delta = reinterpret_cast<float*>(ws + pl.delta);
+  float* dQa = reinterpret_cast<float*>(ws + pl.dq_acc);
+  float* dKa = reinterpret_cast<float*>(ws + pl.dk_acc);
+  float* dVa = reinterpret_cast<float*>(ws + pl.dv_acc);
+  T* WoT = reinterpret_cast<T*>(ws + pl.wo_t);
+  T* WqT = reinterpret_cast<T*>(ws + pl.wq_t);
+  T* WkvT = reinterpret_cast<T*>(ws + pl.wkv_t);
+  const double l2t = log2(theta);
+  const int64_t head = s.Np * s.d;
+  const int64_t Cd = (int64_t)s.C * s.d, kvd = (int64_t)s.kvC * s.d;
+  const int nh = s.C < s.G ? s.C : s.G;
+  const float scale = (float)(1.0 / sqrt((double)s.d));
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.d));
+
+  HIP_TRY(launch_fill_f32(dwq, (int64_t)s.Hq * s.d * s.D, 0.f, st));
+  HIP_TRY(launch_fill_f32(dwk, (int64_t)s.Hkv * s.d * s.D, 0.f, st));
+  HIP_TRY(launch_fill_f32(dwv, (int64_t)s.Hkv * s.d * s.D, 0.f, st));
+  HIP_TRY(launch_fill_f32(dwo, (int64_t)s.Hq * s.d * s.D, 0.f, st));
+  if (s.norm) {
+    HIP_TRY(launch_fill_f32(dqn, s.d, 0.f, st));
+    HIP_TRY(launch_fill_f32(dkn, s.d, 0.f, st));
+  }
+
+  for (int c0 = 0; c0 < s.Hq; c0 += s.C) {
+    const int g0 = c0 / s.G;
+    const bool new_kv = (c0 % s.G) == 0;
+    const bool last_kv = ((c0 + s.C) % s.G) == 0;
+    // weight slices transposed for the products that contract over their rows
+    HIP_TRY(launch_transpose<T>(wo + (int64_t)c0 * s.d, s.D, Cd, (int64_t)s.Hq * s.d, WoT, s.D, st));
+    HIP_TRY(launch_transpose<T>(wq + (int64_t)c0 * s.d * s.D, Cd, s.D, s.D, WqT, Cd, st));
+    if (new_kv) {
+      HIP_TRY(launch_transpose<T>(wk + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WkvT, 2 * kvd, st));
+      HIP_TRY(launch_transpose<T>(wv + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WkvT + kvd, 2 * kvd, st));
+    }
+    // recompute the chunk's projections
+    {
+      const T* w[3] = {wq + (int64_t)c0 * s.d * s.D, wk + (int64_t)g0 * s.d * s.D, wv + (int64_t)g0 * s.d * s.D};
+      const int nheads[3] = {s.C, s.kvC, s.kvC};
+      HeadOut<T> ho[3];
+      memset(ho, 0, sizeof(ho));
+      ho[0].rm = Q;
+      ho[0].pre = Uq;
+      ho[0].gamma = qn;
+      ho[0].rope = 1;
+      ho[1].rm = K;
+      ho[1].pre = Uk;
+      ho[1].gamma = kn;
+      ho[1].rope = 1;
+      ho[2].rm = V;
+      ho[2].tr = Vt;
+      int rc = run_projection<T>(s, x, new_kv ? 3 : 1, w, nheads, ho, eps, l2t, st);
+      if (rc) return rc;
+    }
+    // dO_c = dY Wo_c  (as dY (Wo_c^T)^T)
+    {
+      const T* w[1] = {WoT};
+      const int nheads[1] = {s.C};
+      HeadOut<T> ho[1];
+      memset(ho, 0, sizeof(ho));
+      ho[0].rm = dO;
+      int rc = run_projection<T>(s, dy, 1, w, nheads, ho, eps, l2t, st);
+      if (rc) return rc;
+    }
+    // recompute O_c from the saved LSE, and Delta = rowsum(dO o O)
+    for (int j = 0; j < s.kvC; ++j) {
+      AttnFwd<T> a;
+      memset(&a, 0, sizeof(a));
+      a.q = Q + (int64_t)j * nh * head;
+      a.k = K + (int64_t)j * head;
+      a.vt = Vt + (int64_t)j * head;
+      a.o = O + (int64_t)j * nh * head;
+      a.lse = const_cast<float*>(lse) + (int64_t)(c0 + j * nh) * s.N;
+      a.lse_stride = s.N;
+      a.dout = dO + (int64_t)j * nh * head;
+      a.delta = Delta + (int64_t)j * nh * s.Np;
+      a.N = s.N;
+      a.Np = s.Np;
+      a.nh = nh;
+      a.scale_log2 = scale_log2;
+      HIP_TRY(launch_attn_fwd<T>(a, s.d, 1, st));
+    }
+    // dWo[:, chunk] = dY^T O_c
+    int rc = run_weight_grad<T>(s, dy, O, s.C, dwo + (int64_t)c0 * s.d, (int64_t)s.Hq * s.d, 1, st);
+    if (rc) return rc;
+    // attention backward
+    HIP_TRY(launch_fill_f32(dQa, (int64_t)s.C * head, 0.f, st));
+    for (int j = 0; j < s.kvC; ++j) {
+      AttnBwd<T> b;
+      memset(&b, 0, sizeof(b));
+      b.q = Q + (int64_t)j * nh * head;
+      b.k = K + (int64_t)j * head;
+      b.v = V + (int64_t)j * head;
+      b.dout = dO + (int64_t)j * nh * head;
+      b.lse = lse + (int64_t)(c0 + j * nh) * s.N;
+      b.lse_stride = s.N;
+      b.delta = Delta + (int64_t)j * nh * s.Np;
+      b.dq_acc = dQa + (int64_t)j * nh * head;
+      b.dk_acc = dKa + (int64_t)j * head;
+      b.dv_acc = dVa + (int64_t)j * head;
+      b.N = s.N;
+      b.Np = s.Np;
+      b.nh = nh;
+      b.accumulate = new_kv ? 0 : 1;
+      b.scale_log2 = scale_log2;
+      b.scale = scale;
+      HIP_TRY(launch_attn_bwd<T>(b, s.d, st));
+    }
+    // dq: RoPE transpose (+ RMSNorm backward), into the Q buffer
+    {
+      GradFinish<T> f;
+      memset(&f, 0, sizeof(f));
+      f.gacc = dQa;
+      f.u = Uq;
+      f.gamma = qn;
+      f.dgamma = dqn;
+      f.out = Q;
+      f.rope = 1;
+      f.nh = s.C;
+      f.N = s.N;
+      f.Np = s.Np;
+      f.eps = eps;
+      f.log2_theta = l2t;
+      HIP_TRY(launch_grad_finish<T>(f, s.d, st));
+    }
+    rc = run_weight_grad<T>(s, x, Q, s.C, dwq + (int64_t)c0 * s.d * s.D, 1, s.D, st);
+    if (rc) return rc;
+    rc = run_heads_times_wt<T>(s, Q, s.C, WqT, Cd, dx, c0 > 0, st);
+    if (rc) return rc;
+    if (last_kv || s.C >= s.G) {
+      GradFinish<T> f;
+      memset(&f, 0, sizeof(f));
+      f.gacc = dKa;
+      f.u = Uk;
+      f.gamma = kn;
+      f.dgamma = dkn;
+      f.out = K;
+      f.rope = 1;
+      f.nh = s.kvC;
+      f.N = s.N;
+      f.Np = s.Np;
+      f.eps = eps;
+      f.log2_theta = l2t;
+      HIP_TRY(launch_grad_finish<T>(f, s.d, st));
+      GradFinish<T> fv;
+      memset(&fv, 0, sizeof(fv));
+      fv.gacc = dVa;
+      fv.out = V;
+      fv.nh = s.kvC;
+      fv.N = s.N;
+      fv.Np = s.Np;
+      HIP_TRY(launch_grad_finish<T>(fv, s.d, st));
+      rc = run_weight_grad<T>(s, x, K, s.kvC, dwk + (int64_t)g0 * s.d * s.D, 1, s.D, st);
+      if (rc) return rc;
+      rc = run_weight_grad<T>(s, x, V, s.kvC, dwv + (int64_t)g0 * s.d * s.D, 1, s.D, st);
+      if (rc) return rc;
+      rc = run_heads_times_wt<T>(s, K, 2 * s.kvC, WkvT, 2 * kvd, dx, 1, st);
+      if (rc) return rc;
+    }
+  }
+  return UPIPE_OK;
+}
+
+int check_common(int dtype, int64_t N, int64_t D, int Hq, int Hkv, int d, double theta, int C,
+                 const void* qn, const void* kn, float eps, Shape* s) {
+  int rc = check_shape(dtype, N, D, Hq, Hkv, d, C, s);
+  if (rc) return rc;
+  if (!(theta > 0.0) || !isfinite(theta)) return UPIPE_ERR_INVALID_ARG;
+  if ((qn == nullptr) != (kn == nullptr)) return UPIPE_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return UPIPE_ERR_INVALID_ARG;
+  s->norm = qn != nullptr;
+  return UPIPE_OK;
+}
+
+int check_ptrs(const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (ptrs[i] == nullptr) return UPIPE_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (!aligned(ptrs[i], 16)) return UPIPE_ERR_ALIGNMENT;
+  return UPIPE_OK;
+}
+
+int check_ws(const Shape& s, bool bwd, const void* ws, size_t bytes) {
+  if (ws == nullptr) return UPIPE_ERR_WORKSPACE;
+  if (!aligned(ws, REGION_ALIGN)) return UPIPE_ERR_ALIGNMENT;
+  if (bytes < make_plan(s, bwd).total) return UPIPE_ERR_WORKSPACE;
+  return UPIPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t upipe_attn_workspace_bytes(int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
+                                  int head_dim, int chunk_heads, int qk_norm, upipe_dtype_t dtype,
+                                  int backward) {
+  Shape s;
+  if (check_shape(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, chunk_heads, &s)) return 0;
+  s.norm = qk_norm != 0;
+  return make_plan(s, backward != 0).total;
+}
+
+int upipe_attn_fwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
+                   int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
+                   const void* wk, const void* wv, const void* wo, const void* q_norm_w,
+                   const void* k_norm_w, float norm_eps, void* y, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_common(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads,
+                        q_norm_w, k_norm_w, norm_eps, &s);
+  if (rc) return rc;
+  const void* ptrs[] = {x, wq, wk, wv, wo, y, lse};
+  if ((rc = check_ptrs(ptrs, 7))) return rc;
+  if (s.norm) {
+    const void* np[] = {q_norm_w, k_norm_w};
+    if ((rc = check_ptrs(np, 2))) return rc;
+  }
+  if ((rc = check_ws(s, false, workspace, workspace_bytes))) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == UPIPE_BF16)
+    return attn_fwd_impl<bf16>(s, rope_theta, (const bf16*)x, (const bf16*)wq, (const bf16*)wk,
+                               (const bf16*)wv, (const bf16*)wo, (const bf16*)q_norm_w,
+                               (const bf16*)k_norm_w, norm_eps, (bf16*)y, lse, ws, st);
+  return attn_fwd_impl<float>(s, rope_theta, (const float*)x, (const float*)wq, (const float*)wk,
+                              (const float*)wv, (const float*)wo, (const float*)q_norm_w,
+                              (const float*)k_norm_w, norm_eps, (float*)y, lse, ws, st);
+}
+
+int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
+                   int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
+                   const void* wk, const void* wv, const void* wo, const void* q_norm_w,
+                   const void* k_norm_w, float norm_eps, const void* dy, const float* lse, void* dx,
+                   float* dwq, float* dwk, float* dwv, float* dwo, float* dq_norm_w, float* dk_norm_w,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = check_common(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads,
+                        q_norm_w, k_norm_w, norm_eps, &s);
+  if (rc) return rc;
+  const void* ptrs[] = {x, wq, wk, wv, wo, dy, lse, dx, dwq, dwk, dwv, dwo};
+  if ((rc = check_ptrs(ptrs, 12))) return rc;
+  if (s.norm) {
+    const void* np[] = {q_norm_w, k_norm_w, dq_norm_w, dk_norm_w};
+    if ((rc = check_ptrs(np, 4))) return rc;
+  } else if (dq_norm_w != nullptr || dk_norm_w != nullptr) {
+    return UPIPE_ERR_INVALID_ARG;
+  }
+  if ((rc = check_ws(s, true, workspace, workspace_bytes))) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == UPIPE_BF16)
+    return attn_bwd_impl<bf16>(s, rope_theta, (const bf16*)x, (const bf16*)wq, (const bf16*)wk,
+                               (const bf16*)wv, (const bf16*)wo, (const bf16*)q_norm_w,
+                               (const bf16*)k_norm_w, norm_eps, (const bf16*)dy, lse, (bf16*)dx, dwq,
+                               dwk, dwv, dwo, dq_norm_w, dk_norm_w, ws, st);
+  return attn_bwd_impl<float>(s, rope_theta, (const float*)x, (const float*)wq, (const float*)wk,
+                              (const float*)wv, (const float*)wo, (const float*)q_norm_w,
+                              (const float*)k_norm_w, norm_eps, (const float*)dy, lse, (float*)dx, dwq,
+                              dwk, dwv, dwo, dq_norm_w, dk_norm_w, ws, st);
+}
+
+const char* upipe_strerror(int code) {
+  switch (code) {
+    case UPIPE_OK: return "success";
+    case UPIPE_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size or bad head counts)";
+    case UPIPE_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 64 or 128, d_model a multiple of 128, "
+                                       "chunk_heads must divide n_q_heads and divide or be a multiple of the GQA group)";
+    case UPIPE_ERR_WORKSPACE: return "workspace missing or smaller than upipe_attn_workspace_bytes()";
+    case UPIPE_ERR_ALIGNMENT: return "misaligned pointer (tensors need 16 bytes, the workspace 256 bytes)";
+    case UPIPE_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int upipe_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+/*
+ * upipe.h — C ABI of the headwise-chunked attention library for MI355X (gfx950).
+ *
+ * The operation: one GPU's share of a transformer attention layer under
+ * head-split context parallelism — the full sequence of N tokens and a subset
+ * of heads (n_q_heads query heads, n_kv_heads key/value heads). The heads are
+ * processed one small chunk of `chunk_heads` query heads at a time inside one
+ * caller-sized workspace that every chunk reuses: project the chunk's Q (and
+ * the K/V of its key/value group), run causal attention over the whole
+ * sequence, fold the chunk's share of the output projection into y, then move
+ * to the next chunk. This is the scheme the talk "Road to 5 Million Tokens:
+ * Breaking Barriers in Long Context Training" calls Untied Ulysses / UPipe
+ * (memeeeeeex.com article "500 万トークンへの道 — Max Ryabinin (Together AI) の
+ * Untied Ulysses", section "Untied Ulysses (UPipe) — head 単位のチャンク化";
+ * liquidgold.cc notes, section "Primary Contribution"). The pages give no
+ * formulas; the math is the textbook layer
+ *
+ *   q_h = rope(norm_q(x Wq_h^T)), k_g = rope(norm_k(x Wk_g^T)), v_g = x Wv_g^T
+ *   O_h = softmax(q_h k_g^T / sqrt(head_dim) + causal mask) v_g,  g = h / (Hq/Hkv)
+ *   y   = sum_h O_h Wo_h^T
+ *
+ * with rotate-half RoPE (pairs (i, i + d/2), angle p * theta^(-2i/d) at token
+ * index p, formed in fp64), optional per-head RMSNorm of q and k over head_dim
+ * before RoPE, and key j visible to query i iff j <= i.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates or frees device memory and keeps no state between calls.
+ *  - Layouts are row-major and contiguous, nn.Linear style [out][in]:
+ *      x, y, dy, dx  [N][D]               io dtype
+ *      wq            [Hq*d][D]            head h = rows h*d .. h*d+d-1
+ *      wk, wv        [Hkv*d][D]
+ *      wo            [D][Hq*d]            head h = columns h*d .. h*d+d-1
+ *      q_norm_w, k_norm_w  [d] io dtype, or both NULL (no q/k norm)
+ *      lse           [Hq][N] fp32, natural log of the softmax denominators
+ *      dwq, dwk, dwv, dwo  fp32, same shapes as the weights
+ *      dq_norm_w, dk_norm_w  [d] fp32 (required iff the norm weights are given)
+ *  - io dtype is UPIPE_F32 (float) or UPIPE_BF16 (bfloat16); accumulation is
+ *    always fp32.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    and the call returns without synchronising; outputs are valid once the
+ *    stream reaches that point. The workspace must not be touched by other
+ *    work until then. Calls with distinct workspaces and outputs may run
+ *    concurrently.
+ *  - Every output is overwritten, never accumulated into.
+ *  - Errors: a negative return code. Arguments are validated on the host
+ *    before anything is enqueued; on a validation error nothing is launched
+ *    and no output is touched. A failed kernel launch returns UPIPE_ERR_HIP
+ *    (outputs are then unspecified).
+ *
+ * Supported shapes: N >= 1; D a positive multiple of 128; head_dim 64 or 128;
+ * n_q_heads a multiple of n_kv_heads; chunk_heads divides n_q_heads and
+ * either divides or is a multiple of the group size G = n_q_heads/n_kv_heads.
+ * Tensors must be 16-byte aligned, the workspace 256-byte aligned.
+ */
+#ifndef UPIPE_H_
+#define UPIPE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { UPIPE_F32 = 0, UPIPE_BF16 = 1 } upipe_dtype_t;
+
+enum {
+  UPIPE_OK = 0,
+  UPIPE_ERR_INVALID_ARG = -1, /* a null pointer, a non-positive size, bad head counts */
+  UPIPE_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, D not a multiple of 128, bad chunking */
+  UPIPE_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than upipe_attn_workspace_bytes */
+  UPIPE_ERR_ALIGNMENT = -4,   /* a tensor not 16-B aligned or the workspace not 256-B aligned */
+  UPIPE_ERR_HIP = -5          /* a HIP launch failed */
+};
+
+/*
+ * Bytes of workspace that upipe_attn_fwd (backward = 0) or upipe_attn_bwd
+ * (backward = 1) needs for these sizes. Pure host arithmetic, no HIP call.
+ * Returns 0 when the arguments would be rejected by the entry point.
+ * The per-chunk part grows with chunk_heads, not with n_q_heads: this is the
+ * one small buffer that every chunk reuses (the method's memory saving).
+ */
+size_t upipe_attn_workspace_bytes(int64_t n_tokens, int64_t d_model, int n_q_heads,
+                                  int n_kv_heads, int head_dim, int chunk_heads,
+                                  int qk_norm, upipe_dtype_t dtype, int backward);
+
+/*
+ * Forward pass: y = attention layer(x) over the share, and lse for backward.
+ * Chunks of chunk_heads query heads run in order; each projects its Q (the
+ * first chunk of a kv group also projects that group's K and V), runs causal
+ * GQA flash attention, and adds O_c Wo_c^T into y (the first chunk writes y).
+ *   x [N][D], wq [Hq*d][D], wk/wv [Hkv*d][D], wo [D][Hq*d]  (io dtype, in)
+ *   q_norm_w, k_norm_w [d] or both NULL; norm_eps their epsilon
+ *   y [N][D] io dtype (out), lse [Hq][N] fp32 (out)
+ *   workspace: >= upipe_attn_workspace_bytes(..., backward = 0) bytes
+ */
+int upipe_attn_fwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads,
+                   int n_kv_heads, int head_dim, double rope_theta, int chunk_heads,
+                   const void* x, const void* wq, const void* wk, const void* wv,
+                   const void* wo, const void* q_norm_w, const void* k_norm_w,
+                   float norm_eps, void* y, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass for upstream gradient dy, given the lse that upipe_attn_fwd
+ * returned for the same inputs. Nothing else is kept from the forward:
+ * per chunk the projections and the attention output O are recomputed (O from
+ * the saved lse), then the attention backward and the projection gradients
+ * run, chunk by chunk, in the same reused workspace.
+ *   dy [N][D] io dtype (in), lse [Hq][N] fp32 (in)
+ *   dx [N][D] io dtype (out)
+ *   dwq, dwk, dwv, dwo fp32 (out), shapes of wq, wk, wv, wo
+ *   dq_norm_w, dk_norm_w [d] fp32 (out) iff q_norm_w/k_norm_w are given, else NULL
+ *   workspace: >= upipe_attn_workspace_bytes(..., backward = 1) bytes
+ */
+int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads,
+                   int n_kv_heads, int head_dim, double rope_theta, int chunk_heads,
+                   const void* x, const void* wq, const void* wk, const void* wv,
+                   const void* wo, const void* q_norm_w, const void* k_norm_w,
+                   float norm_eps, const void* dy, const float* lse, void* dx,
+                   float* dwq, float* dwk, float* dwv, float* dwo, float* dq_norm_w,
+                   float* dk_norm_w, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Static text for an error code. */
+const char* upipe_strerror(int code);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int upipe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UPIPE_H_ */

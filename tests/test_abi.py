@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, sizes the workspace as documented and rejects bad arguments before
+touching the GPU (no valid compute call is made here)."""
+import ctypes
+
+import pytest
+
+from headwise_chunked_attention_amd import api
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, ALIGN = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return api.load()
+
+
+def test_exports_every_header_symbol(lib):
+    names = api.header_symbols()
+    assert set(names) == {"upipe_attn_workspace_bytes", "upipe_attn_fwd", "upipe_attn_bwd",
+                          "upipe_strerror", "upipe_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.upipe_version() == 100
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, ALIGN, -5):
+        assert len(api.strerror(code)) > 5
+    assert "unknown" in api.strerror(-99)
+
+
+def _expected_ws(N, D, hq, hkv, d, C, norm, es, bwd):
+    """The documented layout: per-chunk buffers of Np = ceil(N/256)*256 rows."""
+    Np = (N + 255) // 256 * 256
+    G = hq // hkv
+    kvc = C // G if C > G else 1
+    head = Np * d
+    if not bwd:
+        return head * es * (2 * C + 2 * kvc)
+    t = head * es * (3 * C + 3 * kvc + (C + kvc if norm else 0))
+    t += Np * C * 4 + head * 4 * (C + 2 * kvc)
+    t += d * D * es * (2 * C + 2 * kvc)
+    return t
+
+
+@pytest.mark.parametrize("N,D,hq,hkv,d", [(2048, 512, 8, 2, 64), (131072, 4096, 4, 1, 128),
+                                          (1000, 128, 4, 1, 128), (524288, 5120, 8, 1, 128)])
+def test_workspace_formula(N, D, hq, hkv, d):
+    G = hq // hkv
+    for C in [c for c in (1, 2, 4, 8) if hq % c == 0 and (c % G == 0 or G % c == 0)]:
+        for dt, es in (("fp32", 4), ("bf16", 2)):
+            for norm in (False, True):
+                for bwd in (False, True):
+                    got = api.workspace_bytes(N, D, hq, hkv, d, C, norm, dt, bwd)
+                    assert got == _expected_ws(N, D, hq, hkv, d, C, norm, es, bwd), (C, dt, norm, bwd)
+
+
+def test_workspace_scales_with_chunk_not_heads():
+    # forward per-q-head part = 2 * Np * d * es * C; at C=1 of 8 heads it is 1/8 of C=8
+    f = {C: api.workspace_bytes(524288, 5120, 8, 1, 128, C, True, "bf16", False) for C in (1, 2, 4, 8)}
+    kv_part = 2 * 524288 * 128 * 2
+    per_q = {C: f[C] - kv_part for C in f}
+    assert per_q[8] == 8 * per_q[1] and per_q[4] == 4 * per_q[1]
+    assert 1 - per_q[1] / per_q[8] == pytest.approx(0.875)
+
+
+def test_workspace_rejects_bad_shapes():
+    assert api.workspace_bytes(100, 512, 8, 2, 96, 2, False, "bf16", False) == 0
+    assert api.workspace_bytes(100, 500, 8, 2, 64, 2, False, "bf16", False) == 0
+    assert api.workspace_bytes(100, 512, 8, 3, 64, 2, False, "bf16", False) == 0
+    assert api.workspace_bytes(100, 512, 12, 2, 64, 4, False, "bf16", False) == 0
+    assert api.workspace_bytes(0, 512, 8, 2, 64, 2, False, "bf16", False) == 0
+
+
+# Fake, never-dereferenced device addresses: every call below must fail validation.
+P = 1 << 20
+
+
+def _fwd(lib, **kw):
+    a = dict(dtype=1, N=256, D=512, hq=8, hkv=2, d=64, theta=5e5, C=2, x=P, wq=P, wk=P, wv=P, wo=P,
+             qn=None, kn=None, eps=1e-6, y=P, lse=P, ws=P, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.upipe_attn_fwd(a["dtype"], a["N"], a["D"], a["hq"], a["hkv"], a["d"], a["theta"], a["C"],
+                              a["x"], a["wq"], a["wk"], a["wv"], a["wo"], a["qn"], a["kn"], a["eps"],
+                              a["y"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_fwd_validation_errors(lib):
+    assert _fwd(lib, d=96) == UNSUPPORTED
+    assert _fwd(lib, D=500) == UNSUPPORTED
+    assert _fwd(lib, C=3) == UNSUPPORTED
+    assert _fwd(lib, hkv=3) == INVALID
+    assert _fwd(lib, N=0) == INVALID
+    assert _fwd(lib, dtype=7) == INVALID
+    assert _fwd(lib, theta=0.0) == INVALID
+    assert _fwd(lib, theta=float("nan")) == INVALID
+    assert _fwd(lib, x=None) == INVALID
+    assert _fwd(lib, lse=None) == INVALID
+    assert _fwd(lib, qn=P) == INVALID            # q norm without k norm
+    assert _fwd(lib, wq=P + 8) == ALIGN
+    assert _fwd(lib, ws=None) == WORKSPACE
+    assert _fwd(lib, ws=P + 128) == ALIGN
+    need = api.workspace_bytes(256, 512, 8, 2, 64, 2, False, "bf16", False)
+    assert _fwd(lib, wsb=need - 1) == WORKSPACE
+
+
+def test_bwd_validation_errors(lib):
+    def bwd(**kw):
+        a = dict(dtype=0, N=256, D=512, hq=8, hkv=2, d=64, theta=5e5, C=2, qn=None, kn=None, dqn=None,
+                 dkn=None, ws=P, wsb=1 << 40, dx=P)
+        a.update(kw)
+        return lib.upipe_attn_bwd(a["dtype"], a["N"], a["D"], a["hq"], a["hkv"], a["d"], a["theta"], a["C"],
+                                  P, P, P, P, P, a["qn"], a["kn"], 1e-6, P, P, a["dx"], P, P, P, P,
+                                  a["dqn"], a["dkn"], a["ws"], a["wsb"], None)
+    assert bwd(d=32) == UNSUPPORTED
+    assert bwd(dx=None) == INVALID
+    assert bwd(qn=P, kn=P) == INVALID             # norm weights without their gradients
+    assert bwd(dqn=P) == INVALID                  # gradients without norm weights
+    need = api.workspace_bytes(256, 512, 8, 2, 64, 2, False, "fp32", True)
+    assert bwd(wsb=need - 256) == WORKSPACE
+    assert bwd(ws=P + 16) == ALIGN

@@ -1,0 +1,66 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle,
+element by element on the same seeded inputs. Tolerances are the ones the
+layer's precision fixes: relative L2 <= 1e-5 for fp32 inputs and <= 2e-2 for
+bf16 inputs, per output tensor; LSE also max-abs."""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from gpu_util import Case, check_bwd, check_fwd  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(case, C, bwd=True, ref_fwd=None, ref_bwd=None):
+    print(f"case N={case.N} D={case.D} hq={case.hq} hkv={case.hkv} d={case.d} {case.dtype} "
+          f"norm={case.norm} C={C}", flush=True)
+    y, lse = case.gpu_fwd(C)
+    check_fwd(case, C, y, lse, ref_fwd)
+    if bwd:
+        check_bwd(case, C, case.gpu_bwd(C, lse), ref_bwd)
+
+
+def test_tiny_fp32_config():
+    """N=2048, d_model=512, 8 q / 2 kv heads, head_dim 64, theta 5e5, chunk_heads 2, fp32."""
+    _run(Case(2048, 512, 8, 2, 64, "fp32"), 2)
+
+
+@pytest.mark.parametrize("C", [1, 4, 8])
+def test_tiny_fp32_other_chunks(C):
+    _run(Case(2048, 512, 8, 2, 64, "fp32"), C)
+
+
+@pytest.mark.parametrize("N", [1, 7, 300, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_ragged(N, d):
+    _run(Case(N, 256, 4, 1, d, "fp32", seed=N), 2)
+
+
+def test_fp32_qk_norm_random_gamma():
+    _run(Case(700, 256, 8, 1, 128, "fp32", theta=1e6, norm="random", seed=3), 2)
+
+
+def test_fp32_qk_norm_c8():
+    _run(Case(513, 384, 8, 2, 64, "fp32", theta=1e6, norm="random", seed=4), 8)
+
+
+def test_bf16_tiny_layout():
+    _run(Case(2048, 512, 8, 2, 64, "bf16"), 2)
+
+
+@pytest.mark.parametrize("C", [1, 2, 4])
+def test_bf16_llama_share_reduced_n(C):
+    """Llama3-8B share layout (d_model 4096, 4 q / 1 kv, head_dim 128) at N=2304."""
+    _run(Case(2304, 4096, 4, 1, 128, "bf16"), C)
+
+
+@pytest.mark.parametrize("C", [1, 8])
+def test_bf16_qwen_share_reduced_n(C):
+    """Qwen3-32B-shaped share (d_model 5120, 8 q / 1 kv, q/k RMSNorm, theta 1e6) at N=1536."""
+    _run(Case(1536, 5120, 8, 1, 128, "bf16", theta=1e6, norm="random", seed=2), C)
