@@ -1,0 +1,217 @@
+"""Benchmark: fwd+bwd of the headwise-chunked attention layer on one MI355X.
+
+One "step" is one forward plus one backward of the whole hot path (every
+chunk: projections, RoPE, causal GQA attention, output projection, and the
+backward with its recompute) over the Llama3-8B one-GPU Ulysses share:
+N = 131072 tokens, d_model 4096, 4 q heads / 1 kv head, head_dim 128, bf16,
+RoPE theta 5e5, causal; inputs x ~ N(0,1), W ~ N(0, 0.02), dY ~ N(0,1),
+seeded, generated on the host and resident in HBM before timing starts.
+
+Printed (one JSON line): model TFLOP/s of the step at the headline chunk size
+(chunk_heads=1 unless --chunk is given) and its fraction of the bf16 dense
+MFMA peak; the workspace bytes per chunk size; a chunk-size sweep; per-kernel
+event timings; the roofline entry of the dominant kernel (attention
+backward); and the CPU fp64 oracle timed on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--chunk 1] [--no-sweep] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "causal attn fwd+bwd TFLOP/s (frac of bf16 MFMA peak) + peak workspace GB vs chunk"
+
+WORKLOAD = dict(name="llama3-8b-ulysses-share-131k", n_tokens=131072, d_model=4096, n_q_heads=4,
+                n_kv_heads=1, head_dim=128, rope_theta=5e5, dtype="bf16", chunks=(1, 2, 4))
+
+# HBM traffic of the attention-backward kernel from rocprofv3 counters
+# (FETCH_SIZE + WRITE_SIZE, KiB per dispatch, scaled by the copy-kernel
+# calibration). None until measured on the current kernel.
+ATTN_BWD_TRAFFIC_BYTES = None
+
+
+def model_flops(N, D, hq, hkv, d):
+    """Algorithmic fwd+bwd flops: attention core 14*d per visible pair per q head
+    (fwd QK^T + PV = 4d, bwd S, dP, dV, dK, dQ = 10d) plus the four projections
+    (fwd 2*N*D*d per head for q, k, v, o; bwd twice that)."""
+    pairs = N * (N + 1) / 2
+    return 14.0 * d * hq * pairs + 12.0 * N * D * d * (hq + hkv)
+
+
+def cpu_baseline(w, sample_n=2048):
+    """Time the oracle's full fwd+bwd on a bounded sample: the same layer shape
+    (d_model, heads, head_dim) at sample_n tokens. Reports model TFLOP/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from headwise_chunked_attention_amd.synth import LayerInputs
+
+    inp = LayerInputs(sample_n, w["d_model"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"], "bf16", seed=0)
+    t0 = time.perf_counter()
+    oracle.layer_fwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, w["n_q_heads"], w["n_kv_heads"], w["head_dim"],
+                     w["rope_theta"], 1)
+    oracle.layer_bwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, inp.dy, w["n_q_heads"], w["n_kv_heads"],
+                     w["head_dim"], w["rope_theta"], 1)
+    dt = time.perf_counter() - t0
+    fl = model_flops(sample_n, w["d_model"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"])
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full fp64 fwd+bwd (layer_fwd + layer_bwd, which recomputes the fwd) at N={sample_n} "
+                      f"with the workload's d_model/heads/head_dim, chunk_heads=1; {dt:.1f} s; "
+                      f"rate = model flops of that sample / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=1)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--n-tokens", type=int, default=None, help="override N (not the headline workload)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU's Ulysses share: multi-GPU runs (all-to-all over RCCL) are not part "
+              "of this build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from headwise_chunked_attention_amd import api
+    from headwise_chunked_attention_amd.synth import LayerInputs
+
+    w = dict(WORKLOAD)
+    if args.n_tokens:
+        w["n_tokens"] = args.n_tokens
+        w["name"] = f"llama3-8b-ulysses-share-{args.n_tokens}"
+    N, D, hq, hkv, d, theta = (w[k] for k in ("n_tokens", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
+                                              "rope_theta"))
+    dev = torch.device("cuda:0")
+    api.load()
+    t0 = time.perf_counter()
+    inp = LayerInputs(N, D, hq, hkv, d, "bf16", seed=0)
+    t = {k: torch.from_numpy(getattr(inp, k)).to(dev).to(torch.bfloat16)
+         for k in ("x", "dy", "wq", "wk", "wv", "wo")}
+    del inp
+    torch.cuda.synchronize()
+    print(f"# inputs generated and resident in HBM in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    fl = model_flops(N, D, hq, hkv, d)
+    stream = torch.cuda.current_stream(dev)
+
+    def run_chunk(C, steps, warmup, profile):
+        kw = dict(n_q_heads=hq, n_kv_heads=hkv, head_dim=d, rope_theta=theta, chunk_heads=C)
+        ws_f = api.workspace_bytes(N, D, hq, hkv, d, C, False, "bf16", False)
+        ws_b = api.workspace_bytes(N, D, hq, hkv, d, C, False, "bf16", True)
+        ws = api.alloc_workspace(max(ws_f, ws_b), dev)
+        y = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((hq, N), dtype=torch.float32, device=dev)
+        f32 = torch.float32
+        out = (torch.empty((N, D), dtype=torch.bfloat16, device=dev),
+               torch.empty(t["wq"].shape, dtype=f32, device=dev), torch.empty(t["wk"].shape, dtype=f32, device=dev),
+               torch.empty(t["wv"].shape, dtype=f32, device=dev), torch.empty(t["wo"].shape, dtype=f32, device=dev),
+               None, None)
+
+        def step():
+            api.attn_fwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], y=y, lse=lse, workspace=ws, **kw)
+            api.attn_bwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], t["dy"], lse, out=out, workspace=ws, **kw)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        mem0 = torch.cuda.memory_allocated(dev)
+        free0, _ = torch.cuda.mem_get_info(dev)
+        if profile:
+            api.profile_start()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        prof = api.profile_stop() if profile else None
+        free1, _ = torch.cuda.mem_get_info(dev)
+        assert torch.cuda.memory_allocated(dev) == mem0, "the library must not allocate"
+        res = {"chunk_heads": C, "ms_per_step": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+               "ws_fwd_gb": ws_f / 1e9, "ws_bwd_gb": ws_b / 1e9, "hidden_alloc_bytes": int(free0 - free1)}
+        del ws, y, lse, out
+        torch.cuda.empty_cache()
+        return res, prof
+
+    head, prof = run_chunk(args.chunk, args.steps, args.warmup, profile=True)
+    sweep = []
+    if not args.no_sweep:
+        for C in w["chunks"]:
+            if C == args.chunk:
+                sweep.append(head)
+                continue
+            r, _ = run_chunk(C, max(2, args.steps // 2), 1, profile=False)
+            sweep.append(r)
+            print(f"# chunk {C}: {r['ms_per_step']:.2f} ms/step, {r['tflops']:.1f} TFLOP/s", file=sys.stderr,
+                  flush=True)
+
+    kernels = {}
+    for k, v in prof.items():
+        if v["launches"]:
+            kernels[k] = {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["launches"] / args.steps,
+                          "avg_launch_ms": v["ms"] / v["launches"],
+                          "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None}
+    ab = prof["attn_bwd"]
+    achieved = ab["flops"] / ab["launches"] / (ab["ms"] / ab["launches"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": ATTN_BWD_TRAFFIC_BYTES,
+                "kernel": "attn_bwd_kernel<bf16,128>",
+                "algorithmic_flops_per_launch": ab["flops"] / ab["launches"],
+                "avg_launch_ms": ab["ms"] / ab["launches"]}
+
+    cpu = None
+    if not args.no_cpu:
+        try:
+            cpu = cpu_baseline(w)
+        except MemoryError:
+            cpu = None
+
+    line = {
+        "metric": METRIC,
+        "value": head["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded host Gaussian inputs, random-init weights; no dataset)",
+        "config": {"workload": w["name"], "n_tokens": N, "d_model": D, "n_q_heads": hq, "n_kv_heads": hkv,
+                   "head_dim": d, "rope_theta": theta, "causal": True, "chunk_heads": args.chunk,
+                   "parallelism": "one GPU's Ulysses head share (no collectives)"},
+        "frac_of_peak": head["tflops"] / PEAK_BF16_TFLOPS,
+        "model_flops_per_step": fl,
+        "workspace_gb": {"fwd": head["ws_fwd_gb"], "bwd": head["ws_bwd_gb"]},
+        "chunk_sweep": sweep,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,6 +51,10 @@ def load():
     lib.upipe_strerror.restype = ctypes.c_char_p
     lib.upipe_version.argtypes = []
     lib.upipe_version.restype = i32
+    lib.upipe_profile_start.argtypes = []
+    lib.upipe_profile_start.restype = i32
+    lib.upipe_profile_stop.argtypes = [vp, vp, vp, i32]
+    lib.upipe_profile_stop.restype = i32
     _lib = lib
     return lib
 
@@ -194,3 +198,26 @@ def attn_bwd(x, wq, wk, wv, wo, dy, lse, *, n_q_heads, n_kv_heads, head_dim, rop
     if rc != 0:
         raise UpipeError(rc, "upipe_attn_bwd")
     return dx, dwq, dwk, dwv, dwo, dqn, dkn
+
+
+KERNEL_KINDS = ("projection", "out_gemm", "attn_fwd", "attn_recompute", "attn_bwd", "wgrad", "other")
+
+
+def profile_start():
+    """Start per-kernel event timing inside the library (see upipe_profile_start)."""
+    rc = load().upipe_profile_start()
+    if rc != 0:
+        raise UpipeError(rc, "upipe_profile_start")
+
+
+def profile_stop():
+    """Stop timing; returns {kind: {"ms": total, "launches": n, "flops": f}}."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    fl = (ctypes.c_double * n)()
+    rc = load().upipe_profile_stop(ctypes.cast(ms, ctypes.c_void_p), ctypes.cast(cnt, ctypes.c_void_p),
+                                   ctypes.cast(fl, ctypes.c_void_p), n)
+    if rc != 0:
+        raise UpipeError(rc, "upipe_profile_stop")
+    return {k: {"ms": ms[i], "launches": int(cnt[i]), "flops": fl[i]} for i, k in enumerate(KERNEL_KINDS)}

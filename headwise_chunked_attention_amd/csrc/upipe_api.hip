@@ -14,6 +14,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <vector>
+
 #include "upipe.h"
 #include "kernels.h"
 
@@ -108,6 +110,47 @@ int check_shape(int dtype, int64_t N, int64_t D, int Hq, int Hkv, int d, int C, 
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// ---- opt-in per-kernel timing ------------------------------------------
+struct ProfRec {
+  int kind;
+  double flops;
+  hipEvent_t a, b;
+};
+struct Profiler {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler g_prof;
+
+// Enqueue one kernel through `launch`, bracketed by events when timing is on.
+template <class F>
+hipError_t timed(int kind, double flops, hipStream_t st, F&& launch) {
+  if (!g_prof.on) return launch();
+  hipEvent_t a = g_prof.get(), b = g_prof.get();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, st);
+  g_prof.recs.push_back({kind, flops, a, b});
+  return e;
+}
+
+// Visible (query, key) pairs of causal attention over N tokens.
+double causal_pairs(int64_t N) { return 0.5 * (double)N * (double)(N + 1); }
+
 #define HIP_TRY(x)                                 \
   do {                                             \
     if ((x) != hipSuccess) return UPIPE_ERR_HIP;   \
@@ -145,7 +188,8 @@ int run_projection(const Shape& s, const T* x, int nseg, const T* const* w, cons
   g.Np = s.Np;
   g.eps = eps;
   g.log2_theta = log2_theta;
-  HIP_TRY(launch_gemm_nt<T>(g, EPI_HEADS, s.d, st));
+  HIP_TRY(timed(UPIPE_KERNEL_PROJECTION, 2.0 * g.M * g.N * g.K, st,
+                [&] { return launch_gemm_nt<T>(g, EPI_HEADS, s.d, st); }));
   return UPIPE_OK;
 }
 
@@ -167,7 +211,8 @@ int run_heads_times_wt(const Shape& s, const T* a_heads, int nheads, const T* b,
   g.c = out;
   g.ldc = s.D;
   g.accumulate = accumulate;
-  HIP_TRY(launch_gemm_nt<T>(g, EPI_ACCUM, 128, st));
+  HIP_TRY(timed(UPIPE_KERNEL_OUT_GEMM, 2.0 * g.M * g.N * g.K, st,
+                [&] { return launch_gemm_nt<T>(g, EPI_ACCUM, 128, st); }));
   return UPIPE_OK;
 }
 
@@ -194,7 +239,7 @@ int run_weight_grad(const Shape& s, const T* rows, const T* heads, int nheads, f
   g.out = out;
   g.ldm = ldm;
   g.ldn = ldn;
-  HIP_TRY(launch_gemm_tn<T>(g, bn, st));
+  HIP_TRY(timed(UPIPE_KERNEL_WGRAD, 2.0 * g.M * g.N * g.K, st, [&] { return launch_gemm_tn<T>(g, bn, st); }));
   return UPIPE_OK;
 }
 
@@ -239,7 +284,8 @@ int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       a.Np = s.Np;
       a.nh = nh;
       a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.d));
-      HIP_TRY(launch_attn_fwd<T>(a, s.d, 0, st));
+      HIP_TRY(timed(UPIPE_KERNEL_ATTN_FWD, 4.0 * s.d * nh * causal_pairs(s.N), st,
+                    [&] { return launch_attn_fwd<T>(a, s.d, 0, st); }));
     }
     rc = run_heads_times_wt<T>(s, O, s.C, wo + (int64_t)c0 * s.d, (int64_t)s.Hq * s.d, y, c0 > 0, st);
     if (rc) return rc;
@@ -275,13 +321,13 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   const float scale = (float)(1.0 / sqrt((double)s.d));
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.d));
 
-  HIP_TRY(launch_fill_f32(dwq, (int64_t)s.Hq * s.d * s.D, 0.f, st));
-  HIP_TRY(launch_fill_f32(dwk, (int64_t)s.Hkv * s.d * s.D, 0.f, st));
-  HIP_TRY(launch_fill_f32(dwv, (int64_t)s.Hkv * s.d * s.D, 0.f, st));
-  HIP_TRY(launch_fill_f32(dwo, (int64_t)s.Hq * s.d * s.D, 0.f, st));
+  HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dwq, (int64_t)s.Hq * s.d * s.D, 0.f, st); }));
+  HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dwk, (int64_t)s.Hkv * s.d * s.D, 0.f, st); }));
+  HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dwv, (int64_t)s.Hkv * s.d * s.D, 0.f, st); }));
+  HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dwo, (int64_t)s.Hq * s.d * s.D, 0.f, st); }));
   if (s.norm) {
-    HIP_TRY(launch_fill_f32(dqn, s.d, 0.f, st));
-    HIP_TRY(launch_fill_f32(dkn, s.d, 0.f, st));
+    HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dqn, s.d, 0.f, st); }));
+    HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dkn, s.d, 0.f, st); }));
   }
 
   for (int c0 = 0; c0 < s.Hq; c0 += s.C) {
@@ -289,11 +335,11 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
     const bool new_kv = (c0 % s.G) == 0;
     const bool last_kv = ((c0 + s.C) % s.G) == 0;
     // weight slices transposed for the products that contract over their rows
-    HIP_TRY(launch_transpose<T>(wo + (int64_t)c0 * s.d, s.D, Cd, (int64_t)s.Hq * s.d, WoT, s.D, st));
-    HIP_TRY(launch_transpose<T>(wq + (int64_t)c0 * s.d * s.D, Cd, s.D, s.D, WqT, Cd, st));
+    HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wo + (int64_t)c0 * s.d, s.D, Cd, (int64_t)s.Hq * s.d, WoT, s.D, st); }));
+    HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wq + (int64_t)c0 * s.d * s.D, Cd, s.D, s.D, WqT, Cd, st); }));
     if (new_kv) {
-      HIP_TRY(launch_transpose<T>(wk + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WkvT, 2 * kvd, st));
-      HIP_TRY(launch_transpose<T>(wv + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WkvT + kvd, 2 * kvd, st));
+      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wk + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WkvT, 2 * kvd, st); }));
+      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wv + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WkvT + kvd, 2 * kvd, st); }));
     }
     // recompute the chunk's projections
     {
@@ -340,13 +386,14 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       a.Np = s.Np;
       a.nh = nh;
       a.scale_log2 = scale_log2;
-      HIP_TRY(launch_attn_fwd<T>(a, s.d, 1, st));
+      HIP_TRY(timed(UPIPE_KERNEL_ATTN_RECOMPUTE, 4.0 * s.d * nh * causal_pairs(s.N), st,
+                    [&] { return launch_attn_fwd<T>(a, s.d, 1, st); }));
     }
     // dWo[:, chunk] = dY^T O_c
     int rc = run_weight_grad<T>(s, dy, O, s.C, dwo + (int64_t)c0 * s.d, (int64_t)s.Hq * s.d, 1, st);
     if (rc) return rc;
     // attention backward
-    HIP_TRY(launch_fill_f32(dQa, (int64_t)s.C * head, 0.f, st));
+    HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dQa, (int64_t)s.C * head, 0.f, st); }));
     for (int j = 0; j < s.kvC; ++j) {
       AttnBwd<T> b;
       memset(&b, 0, sizeof(b));
@@ -366,7 +413,8 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       b.accumulate = new_kv ? 0 : 1;
       b.scale_log2 = scale_log2;
       b.scale = scale;
-      HIP_TRY(launch_attn_bwd<T>(b, s.d, st));
+      HIP_TRY(timed(UPIPE_KERNEL_ATTN_BWD, 10.0 * s.d * nh * causal_pairs(s.N), st,
+                    [&] { return launch_attn_bwd<T>(b, s.d, st); }));
     }
     // dq: RoPE transpose (+ RMSNorm backward), into the Q buffer
     {
@@ -383,7 +431,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       f.Np = s.Np;
       f.eps = eps;
       f.log2_theta = l2t;
-      HIP_TRY(launch_grad_finish<T>(f, s.d, st));
+      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_grad_finish<T>(f, s.d, st); }));
     }
     rc = run_weight_grad<T>(s, x, Q, s.C, dwq + (int64_t)c0 * s.d * s.D, 1, s.D, st);
     if (rc) return rc;
@@ -403,7 +451,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       f.Np = s.Np;
       f.eps = eps;
       f.log2_theta = l2t;
-      HIP_TRY(launch_grad_finish<T>(f, s.d, st));
+      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_grad_finish<T>(f, s.d, st); }));
       GradFinish<T> fv;
       memset(&fv, 0, sizeof(fv));
       fv.gacc = dVa;
@@ -411,7 +459,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       fv.nh = s.kvC;
       fv.N = s.N;
       fv.Np = s.Np;
-      HIP_TRY(launch_grad_finish<T>(fv, s.d, st));
+      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_grad_finish<T>(fv, s.d, st); }));
       rc = run_weight_grad<T>(s, x, K, s.kvC, dwk + (int64_t)g0 * s.d * s.D, 1, s.D, st);
       if (rc) return rc;
       rc = run_weight_grad<T>(s, x, V, s.kvC, dwv + (int64_t)g0 * s.d * s.D, 1, s.D, st);
@@ -535,5 +583,34 @@ const char* upipe_strerror(int code) {
 }
 
 int upipe_version(void) { return 100; }
+
+int upipe_profile_start(void) {
+  g_prof.on = true;
+  return UPIPE_OK;
+}
+
+int upipe_profile_stop(double* total_ms, int64_t* launches, double* flops, int n_kinds) {
+  g_prof.on = false;
+  for (int k = 0; k < n_kinds; ++k) {
+    if (total_ms) total_ms[k] = 0.0;
+    if (launches) launches[k] = 0;
+    if (flops) flops[k] = 0.0;
+  }
+  int rc = UPIPE_OK;
+  for (const ProfRec& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      rc = UPIPE_ERR_HIP;
+    } else if (r.kind < n_kinds) {
+      if (total_ms) total_ms[r.kind] += ms;
+      if (launches) launches[r.kind] += 1;
+      if (flops) flops[r.kind] += r.flops;
+    }
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  return rc;
+}
 
 }  // extern "C"

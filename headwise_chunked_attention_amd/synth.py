@@ -20,21 +20,33 @@ sampled rows of a very long sequence without holding the whole of x.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
-ROW_BLOCK = 65536
+ROW_BLOCK = 8192
+GEN_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 TENSOR_IDS = {"x": 0, "wq": 1, "wk": 2, "wv": 3, "wo": 4, "dy": 5, "q_norm": 6, "k_norm": 7}
 
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    r = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
-    # NaN never occurs in these draws; keep the branch-free form.
-    return r.view(np.float32)
+    """Round float32 values to the nearest bf16 (ties to even); returns a new float32 array."""
+    out = np.array(a, dtype=np.float32, copy=True, order="C")
+    _round_bf16_inplace(out)
+    return out
+
+
+def _round_bf16_inplace(a: np.ndarray, rows_per_pass: int = 4096) -> None:
+    """In-place round-to-nearest-even of a C-contiguous float32 array to bf16 values."""
+    flat = a.reshape(a.shape[0], -1) if a.ndim > 1 else a.reshape(1, -1)
+    for r0 in range(0, flat.shape[0], rows_per_pass):
+        u = flat[r0:r0 + rows_per_pass].view(np.uint32)
+        lsb = (u >> np.uint32(16)) & np.uint32(1)
+        u += np.uint32(0x7FFF)
+        u += lsb
+        u &= np.uint32(0xFFFF0000)
 
 
 def _block_rng(seed: int, tensor_id: int, block: int) -> np.random.Generator:
@@ -50,23 +62,38 @@ def gen_rows(name: str, rows: int, cols: int, std: float, dtype: str, seed: int 
     if row_stop is None:
         row_stop = rows
     assert 0 <= row_start <= row_stop <= rows
+    if dtype not in ("bf16", "fp32"):
+        raise ValueError(f"unknown dtype {dtype}")
     tid = TENSOR_IDS[name]
     out = np.empty((row_stop - row_start, cols), dtype=np.float32)
     b0 = row_start // ROW_BLOCK
     b1 = (row_stop + ROW_BLOCK - 1) // ROW_BLOCK
-    for b in range(b0, b1):
+
+    def fill(b):
         lo = b * ROW_BLOCK
         hi = min(rows, lo + ROW_BLOCK)
-        blk = _block_rng(seed, tid, b).standard_normal((hi - lo, cols), dtype=np.float32)
-        if std != 1.0:
-            blk *= np.float32(std)
         s0 = max(lo, row_start)
         s1 = min(hi, row_stop)
-        out[s0 - row_start:s1 - row_start] = blk[s0 - lo:s1 - lo]
-    if dtype == "bf16":
-        out = round_to_bf16(out)
-    elif dtype != "fp32":
-        raise ValueError(f"unknown dtype {dtype}")
+        dst = out[s0 - row_start:s1 - row_start]
+        rng = _block_rng(seed, tid, b)
+        if s0 == lo and s1 == hi:
+            rng.standard_normal((hi - lo, cols), dtype=np.float32, out=dst)
+        else:
+            dst[...] = rng.standard_normal((hi - lo, cols), dtype=np.float32)[s0 - lo:s1 - lo]
+        if std != 1.0:
+            dst *= np.float32(std)
+        if dtype == "bf16":
+            _round_bf16_inplace(dst)
+
+    # blocks are independent streams, so they can be drawn on several threads
+    # (numpy's generators release the GIL while filling)
+    nblk = b1 - b0
+    if nblk > 1 and (row_stop - row_start) * cols >= (1 << 22):
+        with ThreadPoolExecutor(max_workers=min(GEN_THREADS, nblk)) as ex:
+            list(ex.map(fill, range(b0, b1)))
+    else:
+        for b in range(b0, b1):
+            fill(b)
     return out
 
 

@@ -26,7 +26,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library
- *    never allocates or frees device memory and keeps no state between calls.
+ *    never allocates or frees device memory and keeps no state between calls
+ *    (apart from the opt-in kernel timing declared at the end).
  *  - Layouts are row-major and contiguous, nn.Linear style [out][in]:
  *      x, y, dy, dx  [N][D]               io dtype
  *      wq            [Hq*d][D]            head h = rows h*d .. h*d+d-1
@@ -123,6 +124,30 @@ int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n
                    float* dwq, float* dwk, float* dwv, float* dwo, float* dq_norm_w,
                    float* dk_norm_w, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * Optional per-kernel timing (for benchmarks and profilers; off by default).
+ * While enabled, every kernel the library enqueues is bracketed by two
+ * hipEvents on the caller's stream, and its algorithmic work (flops of the
+ * exact math it implements: 2*M*N*K for a GEMM, 4*d per visible (query, key)
+ * pair per head for attention forward, 10*d for attention backward) is noted.
+ * upipe_profile_stop waits for the recorded events, writes per-kind totals
+ * (milliseconds, launch counts, flops) into arrays of n_kinds entries, and
+ * turns timing off. Process-wide state: do not profile concurrent calls from
+ * several threads. Returns UPIPE_OK or UPIPE_ERR_HIP.
+ */
+enum {
+  UPIPE_KERNEL_PROJECTION = 0,   /* Q/K/V and dO projection GEMMs (+ norm/RoPE epilogue) */
+  UPIPE_KERNEL_OUT_GEMM = 1,     /* y (+)= O Wo^T and dx (+)= dq Wq style GEMMs */
+  UPIPE_KERNEL_ATTN_FWD = 2,     /* causal attention forward (online softmax) */
+  UPIPE_KERNEL_ATTN_RECOMPUTE = 3, /* backward's forward recompute from the saved LSE */
+  UPIPE_KERNEL_ATTN_BWD = 4,     /* causal attention backward (dQ, dK, dV) */
+  UPIPE_KERNEL_WGRAD = 5,        /* split-K weight-gradient GEMMs */
+  UPIPE_KERNEL_OTHER = 6,        /* RoPE/RMSNorm backward, transposes, fills */
+  UPIPE_KERNEL_KINDS = 7
+};
+int upipe_profile_start(void);
+int upipe_profile_stop(double* total_ms, int64_t* launches, double* flops, int n_kinds);
 
 /* Static text for an error code. */
 const char* upipe_strerror(int code);

@@ -18,7 +18,7 @@ def lib():
 def test_exports_every_header_symbol(lib):
     names = api.header_symbols()
     assert set(names) == {"upipe_attn_workspace_bytes", "upipe_attn_fwd", "upipe_attn_bwd",
-                          "upipe_strerror", "upipe_version"}
+                          "upipe_strerror", "upipe_version", "upipe_profile_start", "upipe_profile_stop"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.upipe_version() == 100
@@ -117,3 +117,10 @@ def test_bwd_validation_errors(lib):
     need = api.workspace_bytes(256, 512, 8, 2, 64, 2, False, "fp32", True)
     assert bwd(wsb=need - 256) == WORKSPACE
     assert bwd(ws=P + 16) == ALIGN
+
+
+def test_profile_stop_without_launches_is_empty(lib):
+    api.profile_start()
+    res = api.profile_stop()
+    assert set(res) == set(api.KERNEL_KINDS)
+    assert all(v["launches"] == 0 and v["ms"] == 0.0 for v in res.values())

@@ -390,10 +390,17 @@ def test_bf16_rounding_pins():
 
 
 def test_generator_blocks_regenerate():
-    full = synth.gen_rows("x", 70000, 8, 1.0, "bf16", seed=0)
-    part = synth.gen_rows("x", 70000, 8, 1.0, "bf16", seed=0, row_start=65530, row_stop=65540)
-    assert np.array_equal(full[65530:65540], part)
-    idx = np.array([69999, 3, 65536, 65535])
-    assert np.array_equal(synth.gen_rows_at("x", 70000, 8, 1.0, "bf16", 0, idx), full[idx])
-    other = synth.gen_rows("wq", 70000, 8, 1.0, "bf16", seed=0)
+    n = 3 * synth.ROW_BLOCK + 100
+    b = synth.ROW_BLOCK
+    full = synth.gen_rows("x", n, 8, 1.0, "bf16", seed=0)
+    part = synth.gen_rows("x", n, 8, 1.0, "bf16", seed=0, row_start=b - 6, row_stop=b + 4)
+    assert np.array_equal(full[b - 6:b + 4], part)
+    idx = np.array([n - 1, 3, b, b - 1, 2 * b + 5])
+    assert np.array_equal(synth.gen_rows_at("x", n, 8, 1.0, "bf16", 0, idx), full[idx])
+    # threaded generation of a large tensor equals block-by-block generation
+    big = synth.gen_rows("dy", 4 * b, 1024, 1.0, "bf16", seed=3)
+    for k in range(4):
+        blk = synth.gen_rows("dy", 4 * b, 1024, 1.0, "bf16", seed=3, row_start=k * b + 1, row_stop=(k + 1) * b)
+        assert np.array_equal(big[k * b + 1:(k + 1) * b], blk)
+    other = synth.gen_rows("wq", n, 8, 1.0, "bf16", seed=0)
     assert not np.array_equal(full, other)
