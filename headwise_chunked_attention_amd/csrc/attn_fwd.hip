@@ -9,8 +9,9 @@
 // one query column and 16 keys of each 32x32 tile. Row statistics of the
 // softmax are then an in-lane reduction plus one exchange between the two
 // half-waves, and P^T feeds O^T = V^T P^T straight from the accumulators
-// (see common.h). K tiles are staged [key][d] and V^T tiles [d][key] in LDS,
-// double buffered, prefetched through registers one tile ahead.
+// (see common.h). K and V tiles are row-major copies [key][d] in LDS, double
+// buffered and prefetched through registers one tile ahead; V^T operands are
+// column reads (LDS transpose reads).
 //
 // Workgroup: 4 waves x (32*NQT) query rows. `hp` heads of the same kv head
 // are packed per workgroup (GQA): the K/V tile in LDS then serves hp heads.
@@ -33,14 +34,13 @@ template <typename T, int D>
 struct FwdGeo {
   static constexpr int NQT = (sizeof(T) == 4 && D == 128) ? 1 : 2;  // 32-query tiles per wave
   static constexpr int ROWS_W = 32 * NQT;
-  static constexpr int SKD = lds_stride<T>(D);   // K tile row stride
-  static constexpr int SVT = lds_stride<T>(BC);  // V^T tile row stride
+  static constexpr int SKD = lds_stride<T>(D);   // K and V tile row stride
   static constexpr int K_ELEMS = BC * SKD;
-  static constexpr int V_ELEMS = D * SVT;
+  static constexpr int V_ELEMS = BC * SKD;
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int KCH = BC * D / VEC / NTHREADS;  // 16-byte chunks per thread (K)
-  static constexpr int VCH = D * BC / VEC / NTHREADS;  // (V^T)
+  static constexpr int VCH = KCH;                      // (V)
 };
 
 template <typename T, int D>
@@ -48,16 +48,12 @@ DEV void load_kv(const AttnFwd<T>& p, int64_t k0, u32x4 (&rk)[FwdGeo<T, D>::KCH]
                  u32x4 (&rv)[FwdGeo<T, D>::VCH]) {
   using G = FwdGeo<T, D>;
   const int tid = threadIdx.x;
-  constexpr int KC_ROW = D / G::VEC, VC_ROW = BC / G::VEC;
+  constexpr int KC_ROW = D / G::VEC;
 #pragma unroll
   for (int i = 0; i < G::KCH; ++i) {
     const int c = tid + i * NTHREADS;
     rk[i] = ld_raw16(p.k + (k0 + c / KC_ROW) * D + (c % KC_ROW) * G::VEC);
-  }
-#pragma unroll
-  for (int i = 0; i < G::VCH; ++i) {
-    const int c = tid + i * NTHREADS;
-    rv[i] = ld_raw16(p.vt + (int64_t)(c / VC_ROW) * p.Np + k0 + (c % VC_ROW) * G::VEC);
+    rv[i] = ld_raw16(p.v + (k0 + c / KC_ROW) * D + (c % KC_ROW) * G::VEC);
   }
 }
 
@@ -65,18 +61,14 @@ template <typename T, int D>
 DEV void store_kv(T* stage, const u32x4 (&rk)[FwdGeo<T, D>::KCH], const u32x4 (&rv)[FwdGeo<T, D>::VCH]) {
   using G = FwdGeo<T, D>;
   const int tid = threadIdx.x;
-  constexpr int KC_ROW = D / G::VEC, VC_ROW = BC / G::VEC;
+  constexpr int KC_ROW = D / G::VEC;
   T* Ks = stage;
   T* Vs = stage + G::K_ELEMS;
 #pragma unroll
   for (int i = 0; i < G::KCH; ++i) {
     const int c = tid + i * NTHREADS;
     st_raw16(Ks + (c / KC_ROW) * G::SKD + (c % KC_ROW) * G::VEC, rk[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < G::VCH; ++i) {
-    const int c = tid + i * NTHREADS;
-    st_raw16(Vs + (c / VC_ROW) * G::SVT + (c % VC_ROW) * G::VEC, rv[i]);
+    st_raw16(Vs + (c / KC_ROW) * G::SKD + (c % KC_ROW) * G::VEC, rv[i]);
   }
 }
 
@@ -198,10 +190,11 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(const AttnFwd<T> p, 
           Frag<T> pf[NQT];
 #pragma unroll
           for (int t = 0; t < NQT; ++t) pf[t] = frag_from_acc<T>(sacc[kt][t], s2, 1.0f);
+          const int row0 = kt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
           for (int j = 0; j < ND; ++j) {
-            const T* vrow = Vs + (j * 32 + r) * G::SVT + kt * 32 + 16 * s2 + 4 * h;
-            const Frag<T> a = ld_frag2(vrow, vrow + 8);
+            const Frag<T> a = frag_from_col4<T>(ld_col4<T>(Vs, G::SKD, row0, j * 32),
+                                                ld_col4<T>(Vs, G::SKD, row0 + 8, j * 32));
 #pragma unroll
             for (int t = 0; t < NQT; ++t) mma(oacc[t][j], a, pf[t]);
           }

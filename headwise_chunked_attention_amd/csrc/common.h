@@ -154,3 +154,42 @@ template <typename T> constexpr int lds_stride(int cols) { return cols + 16 / (i
 
 DEV float wave_max_pair(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- column reads from row-major LDS tiles -------------------------------
+// For lane l, the four values X[k0 + j][c0 + 16*((l >> 4) & 1) + (l & 15)],
+// j = 0..3, of a row-major tile X (row stride S elements) in LDS: a column
+// segment of 4 rows. On gfx950 this is one ds_read_b64_tr_b16 for bf16:
+// within each 16-lane group, lane L points at the 4 elements
+// X[k0 + L/4][cbase + 4*(L%4) .. +3], and the hardware hands lane i the
+// column cbase + i of that 4 x 16 block (verified on the device).
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> DEV typename Vec4<T>::type ld_col4(const T* X, int S, int k0, int c0);
+template <> DEV bf16x4 ld_col4<bf16>(const bf16* X, int S, int k0, int c0) {
+  const int l = lane_id(), L = l & 15;
+  const bf16* p = X + (k0 + (L >> 2)) * S + c0 + 16 * ((l >> 4) & 1) + 4 * (L & 3);
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+template <> DEV f32x4 ld_col4<float>(const float* X, int S, int k0, int c0) {
+  const int l = lane_id();
+  const float* p = X + k0 * S + c0 + 16 * ((l >> 4) & 1) + (l & 15);
+  return (f32x4){p[0], p[S], p[2 * S], p[3 * S]};
+}
+
+template <typename T> DEV Frag<T> frag_from_col4(typename Vec4<T>::type lo, typename Vec4<T>::type hi);
+template <> DEV Frag<bf16> frag_from_col4<bf16>(bf16x4 a, bf16x4 b) {
+  Frag<bf16> f;
+  f.v = (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+template <> DEV Frag<float> frag_from_col4<float>(f32x4 a, f32x4 b) {
+  Frag<float> f;
+  f.lo = a;
+  f.hi = b;
+  return f;
+}

@@ -64,7 +64,7 @@ struct GemmTN {
 };
 
 // Causal GQA attention forward over one kv head and `nh` q heads.
-//   q, o   [nh][Np][D]     k [Np][D]     vt [D][Np]
+//   q, o   [nh][Np][D]     k, v [Np][D]
 //   lse    [nh] rows of stride lse_stride (caller's [Hq][N]), fp32
 // mode 0: online softmax, writes o (normalised) and lse.
 // mode 1: reads lse, writes o and delta[h][i] = sum_d dO[h][i][d] * O[h][i][d].
@@ -72,7 +72,7 @@ template <typename T>
 struct AttnFwd {
   const T* q;
   const T* k;
-  const T* vt;
+  const T* v;
   T* o;
   float* lse;
   int64_t lse_stride;

@@ -35,10 +35,10 @@ struct Shape {
   int es;  // element size of the io dtype
 };
 
-// Workspace regions (byte offsets). Forward uses q, k (K then V^T follow), o.
+// Workspace regions (byte offsets). Forward uses q, k|v, o.
 // Backward aliases: the dq of a chunk overwrites q, dk|dv overwrite k|v.
 struct Plan {
-  size_t q, uq, k, v, uk, vt, dout, o, delta, dq_acc, dk_acc, dv_acc, wo_t, wq_t, wkv_t;
+  size_t q, uq, k, v, uk, dout, o, delta, dq_acc, dk_acc, dv_acc, wo_t, wq_t, wkv_t;
   size_t total;
 };
 
@@ -57,18 +57,15 @@ Plan make_plan(const Shape& s, bool backward) {
   const size_t head = (size_t)s.Np * s.d;  // elements of one [Np][d] head buffer
   Carver c;
   p.q = c.take(head * s.C * s.es);
+  p.k = c.take(head * 2 * s.kvC * s.es);  // K then V, contiguous (backward: dk|dv alias them)
+  p.v = p.k + head * s.kvC * s.es;
   if (!backward) {
-    p.k = c.take(head * s.kvC * s.es);
-    p.vt = c.take(head * s.kvC * s.es);
     p.o = c.take(head * s.C * s.es);
     p.total = c.off;
     return p;
   }
   if (s.norm) p.uq = c.take(head * s.C * s.es);
-  p.k = c.take(head * 2 * s.kvC * s.es);  // K then V, contiguous (dk|dv alias them)
-  p.v = p.k + head * s.kvC * s.es;
   if (s.norm) p.uk = c.take(head * s.kvC * s.es);
-  p.vt = c.take(head * s.kvC * s.es);
   p.dout = c.take(head * s.C * s.es);
   p.o = c.take(head * s.C * s.es);
   p.delta = c.take((size_t)s.Np * s.C * 4);
@@ -250,7 +247,7 @@ int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   const Plan pl = make_plan(s, false);
   T* Q = reinterpret_cast<T*>(ws + pl.q);
   T* K = reinterpret_cast<T*>(ws + pl.k);
-  T* Vt = reinterpret_cast<T*>(ws + pl.vt);
+  T* V = reinterpret_cast<T*>(ws + pl.v);
   T* O = reinterpret_cast<T*>(ws + pl.o);
   const double l2t = log2(theta);
   const int64_t head = s.Np * s.d;
@@ -268,7 +265,7 @@ int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
     ho[1].rm = K;
     ho[1].gamma = kn;
     ho[1].rope = 1;
-    ho[2].tr = Vt;
+    ho[2].rm = V;
     int rc = run_projection<T>(s, x, new_kv ? 3 : 1, w, nheads, ho, eps, l2t, st);
     if (rc) return rc;
     for (int j = 0; j < s.kvC; ++j) {
@@ -276,7 +273,7 @@ int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       memset(&a, 0, sizeof(a));
       a.q = Q + (int64_t)j * nh * head;
       a.k = K + (int64_t)j * head;
-      a.vt = Vt + (int64_t)j * head;
+      a.v = V + (int64_t)j * head;
       a.o = O + (int64_t)j * nh * head;
       a.lse = lse + (int64_t)(c0 + j * nh) * s.N;
       a.lse_stride = s.N;
@@ -304,7 +301,6 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   T* K = reinterpret_cast<T*>(ws + pl.k);
   T* V = reinterpret_cast<T*>(ws + pl.v);
   T* Uk = s.norm ? reinterpret_cast<T*>(ws + pl.uk) : nullptr;
-  T* Vt = reinterpret_cast<T*>(ws + pl.vt);
   T* dO = reinterpret_cast<T*>(ws + pl.dout);
   T* O = reinterpret_cast<T*>(ws + pl.o);
   float* Delta = reinterpret_cast<float*>(ws + pl.delta);
@@ -356,7 +352,6 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       ho[1].gamma = kn;
       ho[1].rope = 1;
       ho[2].rm = V;
-      ho[2].tr = Vt;
       int rc = run_projection<T>(s, x, new_kv ? 3 : 1, w, nheads, ho, eps, l2t, st);
       if (rc) return rc;
     }
@@ -376,7 +371,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       memset(&a, 0, sizeof(a));
       a.q = Q + (int64_t)j * nh * head;
       a.k = K + (int64_t)j * head;
-      a.vt = Vt + (int64_t)j * head;
+      a.v = V + (int64_t)j * head;
       a.o = O + (int64_t)j * nh * head;
       a.lse = const_cast<float*>(lse) + (int64_t)(c0 + j * nh) * s.N;
       a.lse_stride = s.N;

@@ -35,7 +35,7 @@ def _expected_ws(N, D, hq, hkv, d, C, norm, es, bwd):
     head = Np * d
     if not bwd:
         return head * es * (2 * C + 2 * kvc)
-    t = head * es * (3 * C + 3 * kvc + (C + kvc if norm else 0))
+    t = head * es * (3 * C + 2 * kvc + (C + kvc if norm else 0))
     t += Np * C * 4 + head * 4 * (C + 2 * kvc)
     t += d * D * es * (2 * C + 2 * kvc)
     return t
