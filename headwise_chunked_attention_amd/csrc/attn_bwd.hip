@@ -141,7 +141,7 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
 
   prefetch(0);
   commit();
-  __syncthreads();
+  lds_barrier();
 
   for (int64_t it = 0; it < total; ++it) {
     const int hh = (int)(it / nqt);
@@ -194,7 +194,7 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       dSs[(qt * 32 + 8 * (e >> 2) + 4 * h + (e & 3)) * G::SDS + krel] = from_f<T>(dpacc[e]);
-    __syncthreads();
+    lds_barrier();
     if (it + 1 < total) commit();
     // dQ[q][d] += sum over the block's keys of dS[q][key] K[key][d]
     {
@@ -220,7 +220,7 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // Sum the QT partial dK/dV of each key tile through LDS, then write rows of
@@ -236,14 +236,14 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
 #pragma unroll
             for (int e = 0; e < 16; ++e) red[((kt * ND + j) * 16 + e) * 64 + l] = acc[j][e];
         }
-        __syncthreads();
+        lds_barrier();
         if (qt == 0) {
 #pragma unroll
           for (int j = 0; j < ND; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[j][e] += red[((kt * ND + j) * 16 + e) * 64 + l];
         }
-        __syncthreads();
+        lds_barrier();
       }
     }
   }

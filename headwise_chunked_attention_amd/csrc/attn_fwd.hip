@@ -13,7 +13,7 @@
 // buffered and prefetched through registers one tile ahead; V^T operands are
 // column reads (LDS transpose reads).
 //
-// Workgroup: 4 waves x (32*NQT) query rows. `hp` heads of the same kv head
+// Workgroup: 8 waves x (32*NQT) query rows (two waves per SIMD). `hp` heads of the same kv head
 // are packed per workgroup (GQA): the K/V tile in LDS then serves hp heads.
 // Mode 0 (training forward): online softmax; writes O and LSE.
 // Mode 1 (backward recompute): LSE is given; writes O and
@@ -28,11 +28,12 @@ namespace upipe {
 namespace {
 
 constexpr int BC = 64;  // keys per tile
-constexpr int NTHREADS = 256;
 
 template <typename T, int D>
 struct FwdGeo {
-  static constexpr int NQT = (sizeof(T) == 4 && D == 128) ? 1 : 2;  // 32-query tiles per wave
+  static constexpr int NW = 8;                 // waves per workgroup (2 per SIMD)
+  static constexpr int NTHREADS = 64 * NW;
+  static constexpr int NQT = 1;                // 32-query tiles per wave
   static constexpr int ROWS_W = 32 * NQT;
   static constexpr int SKD = lds_stride<T>(D);   // K and V tile row stride
   static constexpr int K_ELEMS = BC * SKD;
@@ -40,6 +41,7 @@ struct FwdGeo {
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int KCH = BC * D / VEC / NTHREADS;  // 16-byte chunks per thread (K)
+  static_assert((BC * D / VEC) % NTHREADS == 0, "tile chunks");
   static constexpr int VCH = KCH;                      // (V)
 };
 
@@ -51,7 +53,7 @@ DEV void load_kv(const AttnFwd<T>& p, int64_t k0, u32x4 (&rk)[FwdGeo<T, D>::KCH]
   constexpr int KC_ROW = D / G::VEC;
 #pragma unroll
   for (int i = 0; i < G::KCH; ++i) {
-    const int c = tid + i * NTHREADS;
+    const int c = tid + i * G::NTHREADS;
     rk[i] = ld_raw16(p.k + (k0 + c / KC_ROW) * D + (c % KC_ROW) * G::VEC);
     rv[i] = ld_raw16(p.v + (k0 + c / KC_ROW) * D + (c % KC_ROW) * G::VEC);
   }
@@ -66,21 +68,21 @@ DEV void store_kv(T* stage, const u32x4 (&rk)[FwdGeo<T, D>::KCH], const u32x4 (&
   T* Vs = stage + G::K_ELEMS;
 #pragma unroll
   for (int i = 0; i < G::KCH; ++i) {
-    const int c = tid + i * NTHREADS;
+    const int c = tid + i * G::NTHREADS;
     st_raw16(Ks + (c / KC_ROW) * G::SKD + (c % KC_ROW) * G::VEC, rk[i]);
     st_raw16(Vs + (c / KC_ROW) * G::SKD + (c % KC_ROW) * G::VEC, rv[i]);
   }
 }
 
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(const AttnFwd<T> p, int hp) {
+__global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(const AttnFwd<T> p, int hp) {
   using G = FwdGeo<T, D>;
   constexpr int NQT = G::NQT, ND = D / 32, NS = D / 16;
   __shared__ __attribute__((aligned(16))) T smem[2 * G::STAGE];
 
   const int l = lane_id(), r = l & 31, h = l >> 5;
   const int w = wave_id();
-  const int qb_rows = 4 * G::ROWS_W / hp;  // query positions per workgroup
+  const int qb_rows = G::NW * G::ROWS_W / hp;  // query positions per workgroup
   const int64_t nqb = p.Np / qb_rows;
   const int64_t qb = nqb - 1 - (int64_t)blockIdx.x;  // longest rows first
   const int hh = (int)blockIdx.y * hp + (w % hp);
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(const AttnFwd<T> p, 
   u32x4 rk[G::KCH], rv[G::VCH];
   load_kv<T, D>(p, 0, rk, rv);
   store_kv<T, D>(smem, rk, rv);
-  __syncthreads();
+  lds_barrier();
 
   for (int64_t kt_i = 0; kt_i < ntiles; ++kt_i) {
     const int64_t k0 = kt_i * BC;
@@ -141,42 +143,48 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(const AttnFwd<T> p, 
         }
       }
       const bool diag = (k0 + BC - 1 > q0w);
+      if (diag) {
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
+          const int qrel = (int)(q0w - k0) + t * 32 + r;  // query minus tile start
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (kt * 32 + 8 * (e >> 2) + 4 * h + (e & 3) > qrel) sacc[kt][t][e] = -INFINITY;
+        }
+      }
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
-        const int64_t q = q0w + t * 32 + r;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float x = sacc[kt][t][e] * p.scale_log2;
-            if (diag) {
-              const int64_t key = k0 + kt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-              if (key > q) x = -INFINITY;
-            }
-            sacc[kt][t][e] = x;
-          }
         if constexpr (MODE == 0) {
+          // Online softmax with a lazily moved base: the running base m_run
+          // (log2 units) is raised only when a score exceeds it by more than
+          // 2^8, so exp2(s - m_run) <= 256 and the O/l rescale is skipped on
+          // most tiles. The final O / l and LSE = m_run + log2(l) are exact
+          // whatever base was used.
           float mx = -INFINITY;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][t][e]);
-          mx = wave_max_pair(mx);
-          const float m_new = fmaxf(m_run[t], mx);
-          const float base = (m_new == -INFINITY) ? 0.f : m_new;
-          const float alpha = fast_exp2(m_run[t] - base);
-          m_run[t] = m_new;
-          base_row[t] = base;
-          l_run[t] *= alpha;
+          mx = wave_max_pair(mx) * p.scale_log2;
+          const bool need = mx > m_run[t] + 8.0f;
+          if (__builtin_amdgcn_ballot_w64(need)) {
+            const float m_new = need ? mx : m_run[t];
+            const float alpha = fast_exp2(m_run[t] - m_new);
+            m_run[t] = m_new;
+            l_run[t] *= alpha;
 #pragma unroll
-          for (int j = 0; j < ND; ++j) oacc[t][j] *= alpha;
+            for (int j = 0; j < ND; ++j) oacc[t][j] *= alpha;
+          }
+          base_row[t] = m_run[t];
         }
         float psum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const float pe = fast_exp2(sacc[kt][t][e] - base_row[t]);
+            const float pe = fast_exp2(fmaf(sacc[kt][t][e], p.scale_log2, -base_row[t]));
             sacc[kt][t][e] = pe;
             psum += pe;
           }
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(const AttnFwd<T> p, 
         }
     }
     if (kt_i + 1 < ntiles) store_kv<T, D>(smem + (buf ^ 1) * G::STAGE, rk, rv);
-    __syncthreads();
+    lds_barrier();
   }
 
   // epilogue
@@ -249,12 +257,12 @@ hipError_t launch_fwd_d(const AttnFwd<T>& p, int mode, hipStream_t s) {
   using G = FwdGeo<T, D>;
   int hp = 1;
   while (hp * 2 <= 4 && p.nh % (hp * 2) == 0) hp *= 2;
-  const int qb_rows = 4 * G::ROWS_W / hp;
+  const int qb_rows = G::NW * G::ROWS_W / hp;
   const dim3 grid((unsigned)(p.Np / qb_rows), (unsigned)(p.nh / hp));
   if (mode == 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, 0>), grid, dim3(NTHREADS), 0, s, p, hp);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, 0>), grid, dim3(G::NTHREADS), 0, s, p, hp);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, 1>), grid, dim3(NTHREADS), 0, s, p, hp);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, 1>), grid, dim3(G::NTHREADS), 0, s, p, hp);
   return hipGetLastError();
 }
 

@@ -193,3 +193,13 @@ template <> DEV Frag<float> frag_from_col4<float>(f32x4 a, f32x4 b) {
   f.hi = b;
   return f;
 }
+
+// Workgroup barrier that orders LDS only. __syncthreads() also fences global
+// memory, which makes every wave wait for all of its outstanding global loads
+// and atomics at each barrier; the kernels here never exchange global data
+// between the threads of a workgroup, so an LDS-scoped fence is enough.
+DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}

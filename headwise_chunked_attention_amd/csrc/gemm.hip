@@ -140,7 +140,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   const int64_t nk = p.K / BK;
   nt_load_tile<T, BN>(p, bptr, ldb, m0, nrow0, 0, ra, rb);
   nt_store_tile<T, BN>(As, Bs, ra, rb);
-  __syncthreads();
+  lds_barrier();
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int buf = (int)(kt & 1);
     if (kt + 1 < nk) nt_load_tile<T, BN>(p, bptr, ldb, m0, nrow0, (kt + 1) * BK, ra, rb);
@@ -150,12 +150,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) mma_tile_step<T, BN>(Ab, Bb, SK, ks, wm, wn, acc);
     if (kt + 1 < nk) nt_store_tile<T, BN>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra, rb);
-    __syncthreads();
+    lds_barrier();
   }
 
   float* Cs = reinterpret_cast<float*>(smem);
   acc_to_lds<BN>(Cs, wm, wn, acc);
-  __syncthreads();
+  lds_barrier();
   const int tid = threadIdx.x;
 
   if constexpr (EPI == EPI_ACCUM) {
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
         for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
         st16_f<T>(dst + row * BN + cv * VEC, v);
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (ho.gamma || ho.rope) {
       // two threads per row; thread half covers pairs [half*BN/4, half*BN/4 + BN/4)
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
           cr[i + BN / 2] = wv * c + u * s;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
     if (ho.rm) {
       T* dst = ho.rm + head * p.Np * BN + m0 * BN;
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   tn_load<T, BN>(baddr, kb, ke, rb);
   tn_store<T, BM>(As, ra);
   tn_store<T, BN>(Bs, rb);
-  __syncthreads();
+  lds_barrier();
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int buf = (int)(kt & 1);
     if (kt + 1 < nk) {
@@ -350,12 +350,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
       tn_store<T, BM>(As + (buf ^ 1) * BM * SK, ra);
       tn_store<T, BN>(Bs + (buf ^ 1) * BN * SK, rb);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   float* Cs = reinterpret_cast<float*>(smem);
   acc_to_lds<BN>(Cs, wm, wn, acc);
-  __syncthreads();
+  lds_barrier();
   const int tid = threadIdx.x;
   if (p.ldn == 1) {
     for (int c = tid; c < BM * BN; c += NTHREADS) {
