@@ -33,10 +33,13 @@ METRIC = "causal attn fwd+bwd TFLOP/s (frac of bf16 MFMA peak) + peak workspace 
 WORKLOAD = dict(name="llama3-8b-ulysses-share-131k", n_tokens=131072, d_model=4096, n_q_heads=4,
                 n_kv_heads=1, head_dim=128, rope_theta=5e5, dtype="bf16", chunks=(1, 2, 4))
 
-# HBM traffic of the attention-backward kernel from rocprofv3 counters
-# (FETCH_SIZE + WRITE_SIZE, KiB per dispatch, scaled by the copy-kernel
-# calibration). None until measured on the current kernel.
-ATTN_BWD_TRAFFIC_BYTES = None
+KERNEL_NAMES = {"attn_fwd": "attn_fwd_kernel<bf16,128,0>", "attn_recompute": "attn_fwd_kernel<bf16,128,1>",
+                "attn_bwd_dkdv": "attn_bwd_dkdv_kernel<bf16,128>", "attn_bwd_dq": "attn_bwd_dq_kernel<bf16,128>"}
+
+# HBM bytes per launch of a kernel from rocprofv3 counters (FETCH_SIZE +
+# WRITE_SIZE, scaled by a plain copy of known size), measured on the kernel as
+# it now stands; absent (null) until measured again after a kernel change.
+TRAFFIC_BYTES = {}
 
 
 def model_flops(N, D, hq, hkv, d):
@@ -171,11 +174,13 @@ def main():
             kernels[k] = {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["launches"] / args.steps,
                           "avg_launch_ms": v["ms"] / v["launches"],
                           "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None}
-    ab = prof["attn_bwd"]
+    # dominant kernel of the step: the attention kernel kind with the most time
+    dom = max(("attn_fwd", "attn_recompute", "attn_bwd_dkdv", "attn_bwd_dq"), key=lambda k: prof[k]["ms"])
+    ab = prof[dom]
     achieved = ab["flops"] / ab["launches"] / (ab["ms"] / ab["launches"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": ATTN_BWD_TRAFFIC_BYTES,
-                "kernel": "attn_bwd_kernel<bf16,128>",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_BYTES.get(dom),
+                "kernel": KERNEL_NAMES[dom],
                 "algorithmic_flops_per_launch": ab["flops"] / ab["launches"],
                 "avg_launch_ms": ab["ms"] / ab["launches"]}
 

@@ -200,7 +200,8 @@ def attn_bwd(x, wq, wk, wv, wo, dy, lse, *, n_q_heads, n_kv_heads, head_dim, rop
     return dx, dwq, dwk, dwv, dwo, dqn, dkn
 
 
-KERNEL_KINDS = ("projection", "out_gemm", "attn_fwd", "attn_recompute", "attn_bwd", "wgrad", "other")
+KERNEL_KINDS = ("projection", "out_gemm", "attn_fwd", "attn_recompute", "attn_bwd_dkdv", "attn_bwd_dq", "wgrad",
+                "other")
 
 
 def profile_start():

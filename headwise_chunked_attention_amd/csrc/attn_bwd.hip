@@ -7,17 +7,22 @@
 // "recomputed", memeeeeeex.com article, section "Untied Ulysses (UPipe) —
 // head 単位のチャンク化").
 //
-// One workgroup owns a block of keys of one kv head and walks the query tiles
-// at or after its keys for every q head of the chunk that reads this kv head,
-// so dK and dV sum over the GQA group in registers:
-//   S  = Q K^T,  dP = dO V^T             (rows q, one key per lane)
-//   P  = exp(S/sqrt(d) - LSE),  dS = P (dP - Delta) / sqrt(d)
-//   dV^T += dO^T P,  dK^T += Q^T dS       (P and dS feed MFMA from registers)
-//   dQ  += dS K                           (dS staged through LDS, fp32 atomics)
-// Every LDS tile is a row-major copy of global memory (K, V of the key block
-// once; Q, dO per query tile, prefetched one tile ahead through registers);
-// the transposed operands (dO^T, Q^T, K as a column operand) are read with
-// gfx950's LDS transpose reads.
+// With P = exp(S/sqrt(d) - LSE) and dS = P (dP - Delta) / sqrt(d):
+//   dV = P^T dO,  dK = dS^T Q,  dQ = dS K.
+// Two kernels, no atomics:
+//  * dK/dV kernel, key-stationary: a workgroup owns a block of keys and walks
+//    the query tiles at or after it for every q head of the chunk reading this
+//    kv head, so dK and dV sum over the GQA group in registers. Per step it
+//    computes S = Q K^T and dP = dO V^T (rows q, one key per lane), then
+//    dV^T += dO^T P and dK^T += Q^T dS with P/dS fed from the accumulators.
+//  * dQ kernel, query-stationary (the forward's shape): a wave owns 32 queries
+//    and walks the key tiles up to them computing S^T = K Q^T, dP^T = V dO^T
+//    (one query per lane), then dQ^T += K^T dS^T.
+// The dQ kernel recomputes S and dP (4*d more flops per visible pair) but
+// writes dQ once instead of accumulating it with fp32 atomics, which on this
+// chip cost more than the whole rest of the backward.
+// Every LDS tile is a row-major copy of global memory; transposed operands
+// (dO^T, Q^T, K^T) are column reads with gfx950's LDS transpose reads.
 #include <math.h>
 
 #include "common.h"
@@ -27,12 +32,15 @@ namespace upipe {
 
 namespace {
 
-// Workgroup geometry: KT x QT waves. Wave w owns key tile w % KT (32 keys)
-// and query tile w / KT (32 queries) of each step, so a workgroup covers
-// BKEY = 32*KT keys and BQ = 32*QT queries per step. With 8 waves two waves
-// share each SIMD and hide each other's LDS and MFMA latency.
+// ---------------------------------------------------------------------------
+// dK / dV
+// ---------------------------------------------------------------------------
+// Workgroup geometry: KT x QT waves. Wave w owns key tile w % KT (32 keys) and
+// query tile w / KT (32 queries) of each step, so a workgroup covers
+// BKEY = 32*KT keys and BQ = 32*QT queries per step; with 8 waves two waves
+// share each SIMD. Q/dO tiles are double buffered in LDS.
 template <typename T, int D>
-struct BwdGeo {
+struct DkdvGeo {
   static constexpr bool BIG = (sizeof(T) == 4 && D == 128);  // fp32, head_dim 128: smaller block (LDS)
   static constexpr int KT = BIG ? 2 : 4;
   static constexpr int QT = BIG ? 1 : 2;
@@ -41,26 +49,23 @@ struct BwdGeo {
   static constexpr int BKEY = 32 * KT;
   static constexpr int BQ = 32 * QT;
   static constexpr int VEC = 16 / (int)sizeof(T);
-  static constexpr int SK = lds_stride<T>(D);      // K, V, Q, dO tiles [rows][D]
-  static constexpr int SDS = lds_stride<T>(BKEY);  // dS [BQ][BKEY]
+  static constexpr int SK = lds_stride<T>(D);  // every tile is [rows][D]
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = K_OFF + BKEY * SK;
-  static constexpr int Q_OFF = V_OFF + BKEY * SK;
-  static constexpr int DO_OFF = Q_OFF + BQ * SK;
-  static constexpr int DS_OFF = DO_OFF + BQ * SK;
-  static constexpr int T_ELEMS = DS_OFF + BQ * SDS;
-  static constexpr int RCH = D / VEC;            // 16-byte chunks per row
-  static constexpr int PER = BQ * RCH / NT;      // prefetch chunks per thread and tensor
-  static constexpr size_t SMEM = (size_t)T_ELEMS * sizeof(T) + 2 * BQ * sizeof(float);
+  static constexpr int BUF_OFF = V_OFF + BKEY * SK;  // two buffers of [Q | dO]
+  static constexpr int BUF_ELEMS = 2 * BQ * SK;
+  static constexpr int T_ELEMS = BUF_OFF + 2 * BUF_ELEMS;
+  static constexpr int RCH = D / VEC;         // 16-byte chunks per row
+  static constexpr int PER = BQ * RCH / NT;   // prefetch chunks per thread and tensor
+  static constexpr size_t SMEM = (size_t)T_ELEMS * sizeof(T) + 2 * 2 * BQ * sizeof(float);
   // end-of-kernel reduction of the QT partial dK/dV sums per key tile
   static constexpr size_t RED = (size_t)KT * 64 * 16 * (D / 32) * sizeof(float);
   static_assert((BQ * RCH) % NT == 0, "tile chunks");
   static_assert(QT == 1 || RED <= SMEM, "reduction buffer fits in LDS");
 };
 
-template <typename T, int D>
-DEV void load_tile(const T* base, int64_t row0, u32x4 (&r)[BwdGeo<T, D>::PER]) {
-  using G = BwdGeo<T, D>;
+template <typename T, int D, class G>
+DEV void load_rows(const T* base, int64_t row0, u32x4 (&r)[G::PER]) {
 #pragma unroll
   for (int i = 0; i < G::PER; ++i) {
     const int c = threadIdx.x + i * G::NT;
@@ -68,9 +73,8 @@ DEV void load_tile(const T* base, int64_t row0, u32x4 (&r)[BwdGeo<T, D>::PER]) {
   }
 }
 
-template <typename T, int D>
-DEV void store_tile(T* S, const u32x4 (&r)[BwdGeo<T, D>::PER]) {
-  using G = BwdGeo<T, D>;
+template <typename T, int D, class G>
+DEV void store_rows(T* S, const u32x4 (&r)[G::PER]) {
 #pragma unroll
   for (int i = 0; i < G::PER; ++i) {
     const int c = threadIdx.x + i * G::NT;
@@ -79,18 +83,14 @@ DEV void store_tile(T* S, const u32x4 (&r)[BwdGeo<T, D>::PER]) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const AttnBwd<T> p) {
-  using G = BwdGeo<T, D>;
+__global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(const AttnBwd<T> p) {
+  using G = DkdvGeo<T, D>;
   constexpr int BQ = G::BQ, BKEY = G::BKEY, ND = D / 32, NS = D / 16, SK = G::SK;
   extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
   T* sm = reinterpret_cast<T*>(dyn_smem);
   T* Ks = sm + G::K_OFF;
   T* Vs = sm + G::V_OFF;
-  T* Qs = sm + G::Q_OFF;
-  T* dOs = sm + G::DO_OFF;
-  T* dSs = sm + G::DS_OFF;
-  float* lse_s = reinterpret_cast<float*>(sm + G::T_ELEMS);
-  float* del_s = lse_s + BQ;
+  float* stat = reinterpret_cast<float*>(sm + G::T_ELEMS);  // [2 buffers][lse | delta][BQ]
 
   const int l = lane_id(), r = l & 31, h = l >> 5;
   const int w = wave_id();
@@ -100,7 +100,6 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
   const int krel = kt * 32 + r;                   // this lane's key within the block
   const int64_t kw = k0 + krel;
 
-  // K and V of the key block, row-major in LDS.
   for (int c = tid; c < BKEY * G::RCH; c += G::NT) {
     const int row = c / G::RCH, cc = c % G::RCH;
     st_raw16(Ks + row * SK + cc * G::VEC, ld_raw16(p.k + (k0 + row) * D + cc * G::VEC));
@@ -122,33 +121,36 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
   auto prefetch = [&](int64_t it) {
     const int hh = (int)(it / nqt);
     const int64_t q0 = k0 + (it % nqt) * BQ;
-    load_tile<T, D>(p.q + (int64_t)hh * p.Np * D, q0, rq);
-    load_tile<T, D>(p.dout + (int64_t)hh * p.Np * D, q0, rdo);
+    load_rows<T, D, G>(p.q + (int64_t)hh * p.Np * D, q0, rq);
+    load_rows<T, D, G>(p.dout + (int64_t)hh * p.Np * D, q0, rdo);
     if (tid < BQ) {
       const int64_t q = q0 + tid;
       rl = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : 0.f;
       rd = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] : 0.f;
     }
   };
-  auto commit = [&]() {
-    store_tile<T, D>(Qs, rq);
-    store_tile<T, D>(dOs, rdo);
+  auto commit = [&](int b) {
+    store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS, rq);
+    store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS + BQ * SK, rdo);
     if (tid < BQ) {
-      lse_s[tid] = rl;
-      del_s[tid] = rd;
+      stat[b * 2 * BQ + tid] = rl;
+      stat[b * 2 * BQ + BQ + tid] = rd;
     }
   };
 
   prefetch(0);
-  commit();
+  commit(0);
   lds_barrier();
 
   for (int64_t it = 0; it < total; ++it) {
-    const int hh = (int)(it / nqt);
+    const int b = (int)(it & 1);
     const int64_t q0 = k0 + (it % nqt) * BQ;
     if (it + 1 < total) prefetch(it + 1);
-    // rows of this wave's query tile, relative to the key block start
-    const int qrel0 = (int)(q0 - k0) + qt * 32;
+    const T* Qs = sm + G::BUF_OFF + b * G::BUF_ELEMS;
+    const T* dOs = Qs + BQ * SK;
+    const float* lse_s = stat + b * 2 * BQ;
+    const float* del_s = lse_s + BQ;
+    const int qrel0 = (int)(q0 - k0) + qt * 32;                            // wave's first row - block start
     const int qlim = (int)((p.N - q0 < (int64_t)BQ) ? (p.N - q0) : BQ);  // valid rows of the tile
 
     // S = Q K^T and dP = dO V^T (rows q of tile qt, lane = key of tile kt)
@@ -160,7 +162,6 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
       mma(sacc, ld_frag(Qs + (qt * 32 + r) * SK + s * 16 + 8 * h), kb);
       mma(dpacc, ld_frag(dOs + (qt * 32 + r) * SK + s * 16 + 8 * h), vb);
     }
-    // P = exp(S/sqrt(d) - LSE), dS = P (dP - Delta) / sqrt(d), in place
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = qt * 32 + 8 * i + 4 * h;  // tile row of accumulator element 4*i
@@ -170,13 +171,12 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
       for (int j = 0; j < 4; ++j) {
         const int e = 4 * i + j;
         const bool valid = (krel <= qrel0 + 8 * i + 4 * h + j) && (rr + j < qlim);
-        const float pe = valid ? fast_exp2(sacc[e] * p.scale_log2 - lv[j]) : 0.f;
+        const float pe = valid ? fast_exp2(fmaf(sacc[e], p.scale_log2, -lv[j])) : 0.f;
         sacc[e] = pe;
         dpacc[e] = pe * (dpacc[e] - dv4[j]) * p.scale;
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries: P/dS feed
-    // MFMA from the accumulators, dO^T/Q^T are column reads of LDS tiles.
+    // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries.
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const Frag<T> pb = frag_from_acc<T>(sacc, s2, 1.0f);
@@ -190,36 +190,7 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
         mma(dk[j], aq, sb);
       }
     }
-    // dS -> LDS [q][key]
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      dSs[(qt * 32 + 8 * (e >> 2) + 4 * h + (e & 3)) * G::SDS + krel] = from_f<T>(dpacc[e]);
-    lds_barrier();
-    if (it + 1 < total) commit();
-    // dQ[q][d] += sum over the block's keys of dS[q][key] K[key][d]
-    {
-      float* dqh = p.dq_acc + (int64_t)hh * p.Np * D;
-      for (int ti = w; ti < G::QT * ND; ti += G::NW) {
-        const int tq = ti % G::QT, jd = ti / G::QT;
-        f32x16 acc = zero16();
-#pragma unroll
-        for (int s = 0; s < BKEY / 16; ++s) {
-          const Frag<T> a = ld_frag(dSs + (tq * 32 + r) * G::SDS + s * 16 + 8 * h);
-          const Frag<T> b = frag_from_col4<T>(ld_col4<T>(Ks, SK, s * 16 + 8 * h, jd * 32),
-                                              ld_col4<T>(Ks, SK, s * 16 + 8 * h + 4, jd * 32));
-          mma(acc, a, b);
-        }
-        float* dst = dqh + (q0 + tq * 32 + 4 * h) * D + jd * 32 + r;
-        if (tq * 32 + 32 <= qlim) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) atomicAdd(dst + (8 * (e >> 2) + (e & 3)) * D, acc[e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (tq * 32 + 8 * (e >> 2) + 4 * h + (e & 3) < qlim) atomicAdd(dst + (8 * (e >> 2) + (e & 3)) * D, acc[e]);
-        }
-      }
-    }
+    if (it + 1 < total) commit(b ^ 1);
     lds_barrier();
   }
 
@@ -267,27 +238,177 @@ __global__ __launch_bounds__((BwdGeo<T, D>::NT)) void attn_bwd_kernel(const Attn
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+constexpr int BC = 64;  // keys per tile
+
 template <typename T, int D>
-hipError_t launch_bwd_d(const AttnBwd<T>& p, hipStream_t s) {
-  using G = BwdGeo<T, D>;
+struct DqGeo {
+  static constexpr int NW = 8;  // waves per workgroup, 32 queries each
+  static constexpr int NT = 64 * NW;
+  static constexpr int SK = lds_stride<T>(D);
+  static constexpr int STAGE = 2 * BC * SK;  // K tile then V tile
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int RCH = D / VEC;
+  static constexpr int KCH = BC * RCH / NT;  // 16-byte chunks per thread and tensor
+  static_assert((BC * RCH) % NT == 0, "tile chunks");
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const AttnBwd<T> p, int hp) {
+  using G = DqGeo<T, D>;
+  constexpr int ND = D / 32, NS = D / 16, SK = G::SK;
+  extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
+  T* smem = reinterpret_cast<T*>(dyn_smem);
+
+  const int l = lane_id(), r = l & 31, h = l >> 5;
+  const int w = wave_id();
+  const int qb_rows = G::NW * 32 / hp;  // query positions per workgroup
+  const int64_t nqb = p.Np / qb_rows;
+  const int64_t qb = nqb - 1 - (int64_t)blockIdx.x;  // longest rows first
+  const int hh = (int)blockIdx.y * hp + (w % hp);
+  const int64_t qs = qb * qb_rows;
+  const int64_t q0w = qs + (int64_t)(w / hp) * 32;
+  const int64_t q = q0w + r;  // this lane's query
+
+  // Q and dO of this lane's query as B operands (k = head dim), resident.
+  const int64_t hoff = (int64_t)hh * p.Np * D;
+  Frag<T> qf[NS], df[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qf[s] = ld_frag(p.q + hoff + q * D + s * 16 + 8 * h);
+    df[s] = ld_frag(p.dout + hoff + q * D + s * 16 + 8 * h);
+  }
+  const float lse2 = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : 0.f;
+  const float dlt = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] : 0.f;
+  f32x16 dq[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) dq[j] = zero16();
+
+  auto load = [&](int64_t k0, u32x4(&rk)[G::KCH], u32x4(&rv)[G::KCH]) {
+#pragma unroll
+    for (int i = 0; i < G::KCH; ++i) {
+      const int c = threadIdx.x + i * G::NT;
+      rk[i] = ld_raw16(p.k + (k0 + c / G::RCH) * D + (c % G::RCH) * G::VEC);
+      rv[i] = ld_raw16(p.v + (k0 + c / G::RCH) * D + (c % G::RCH) * G::VEC);
+    }
+  };
+  auto store = [&](T* st, const u32x4(&rk)[G::KCH], const u32x4(&rv)[G::KCH]) {
+#pragma unroll
+    for (int i = 0; i < G::KCH; ++i) {
+      const int c = threadIdx.x + i * G::NT;
+      st_raw16(st + (c / G::RCH) * SK + (c % G::RCH) * G::VEC, rk[i]);
+      st_raw16(st + BC * SK + (c / G::RCH) * SK + (c % G::RCH) * G::VEC, rv[i]);
+    }
+  };
+
+  const int64_t ntiles = (qs + qb_rows) / BC;
+  u32x4 rk[G::KCH], rv[G::KCH];
+  load(0, rk, rv);
+  store(smem, rk, rv);
+  lds_barrier();
+  for (int64_t kt_i = 0; kt_i < ntiles; ++kt_i) {
+    const int64_t k0 = kt_i * BC;
+    const int buf = (int)(kt_i & 1);
+    if (kt_i + 1 < ntiles) load(k0 + BC, rk, rv);
+    const T* Ks = smem + buf * G::STAGE;
+    const T* Vs = Ks + BC * SK;
+    if (k0 <= q0w + 31) {  // some key of the tile is visible to this wave
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        sacc[kt] = zero16();
+        dpacc[kt] = zero16();
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          mma(sacc[kt], ld_frag(Ks + (kt * 32 + r) * SK + s * 16 + 8 * h), qf[s]);
+          mma(dpacc[kt], ld_frag(Vs + (kt * 32 + r) * SK + s * 16 + 8 * h), df[s]);
+        }
+      const int qrel = (int)(q - k0);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const bool valid = kt * 32 + 8 * (e >> 2) + 4 * h + (e & 3) <= qrel;
+          const float pe = valid ? fast_exp2(fmaf(sacc[kt][e], p.scale_log2, -lse2)) : 0.f;
+          dpacc[kt][e] = pe * (dpacc[kt][e] - dlt) * p.scale;
+        }
+      // dQ^T += K^T dS^T (contraction over the tile's keys = accumulator rows)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const Frag<T> sb = frag_from_acc<T>(dpacc[kt], s2, 1.0f);
+          const int row0 = kt * 32 + 16 * s2 + 4 * h;
+#pragma unroll
+          for (int j = 0; j < ND; ++j) {
+            const Frag<T> a = frag_from_col4<T>(ld_col4<T>(Ks, SK, row0, j * 32), ld_col4<T>(Ks, SK, row0 + 8, j * 32));
+            mma(dq[j], a, sb);
+          }
+        }
+    }
+    if (kt_i + 1 < ntiles) store(smem + (buf ^ 1) * G::STAGE, rk, rv);
+    lds_barrier();
+  }
+  // dQ rows of this lane's query: C tiles hold rows = head dim.
+  float* dst = p.dq + hoff + q * D;
+#pragma unroll
+  for (int j = 0; j < ND; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f32x4*>(dst + j * 32 + 8 * i + 4 * h) =
+          (f32x4){dq[j][4 * i], dq[j][4 * i + 1], dq[j][4 * i + 2], dq[j][4 * i + 3]};
+}
+
+template <typename T, int D>
+hipError_t launch_dkdv_d(const AttnBwd<T>& p, hipStream_t s) {
+  using G = DkdvGeo<T, D>;
   const dim3 grid((unsigned)((p.N + G::BKEY - 1) / G::BKEY));
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_kernel<T, D>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<T, D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::SMEM);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_kernel<T, D>), grid, dim3(G::NT), G::SMEM, s, p);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), grid, dim3(G::NT), G::SMEM, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_dq_d(const AttnBwd<T>& p, hipStream_t s) {
+  using G = DqGeo<T, D>;
+  int hp = 1;
+  while (hp * 2 <= 4 && p.nh % (hp * 2) == 0) hp *= 2;
+  const int qb_rows = G::NW * 32 / hp;
+  const dim3 grid((unsigned)(p.Np / qb_rows), (unsigned)(p.nh / hp));
+  const size_t smem = (size_t)2 * G::STAGE * sizeof(T);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<T, D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), grid, dim3(G::NT), smem, s, p, hp);
   return hipGetLastError();
 }
 
 }  // namespace
 
 template <typename T>
-hipError_t launch_attn_bwd(const AttnBwd<T>& p, int head_dim, hipStream_t s) {
-  if (head_dim == 64) return launch_bwd_d<T, 64>(p, s);
-  if (head_dim == 128) return launch_bwd_d<T, 128>(p, s);
+hipError_t launch_attn_bwd_dkdv(const AttnBwd<T>& p, int head_dim, hipStream_t s) {
+  if (head_dim == 64) return launch_dkdv_d<T, 64>(p, s);
+  if (head_dim == 128) return launch_dkdv_d<T, 128>(p, s);
   return hipErrorInvalidValue;
 }
 
-template hipError_t launch_attn_bwd<bf16>(const AttnBwd<bf16>&, int, hipStream_t);
-template hipError_t launch_attn_bwd<float>(const AttnBwd<float>&, int, hipStream_t);
+template <typename T>
+hipError_t launch_attn_bwd_dq(const AttnBwd<T>& p, int head_dim, hipStream_t s) {
+  if (head_dim == 64) return launch_dq_d<T, 64>(p, s);
+  if (head_dim == 128) return launch_dq_d<T, 128>(p, s);
+  return hipErrorInvalidValue;
+}
+
+template hipError_t launch_attn_bwd_dkdv<bf16>(const AttnBwd<bf16>&, int, hipStream_t);
+template hipError_t launch_attn_bwd_dkdv<float>(const AttnBwd<float>&, int, hipStream_t);
+template hipError_t launch_attn_bwd_dq<bf16>(const AttnBwd<bf16>&, int, hipStream_t);
+template hipError_t launch_attn_bwd_dq<float>(const AttnBwd<float>&, int, hipStream_t);
 
 }  // namespace upipe

@@ -85,8 +85,9 @@ struct AttnFwd {
 
 // Causal GQA attention backward over one kv head and `nh` q heads.
 //   q, dout [nh][Np][D]; k, v [Np][D]; lse [nh] rows of stride lse_stride;
-//   delta [nh][Np]; dq_acc [nh][Np][D] fp32 (atomically accumulated);
-//   dk_acc, dv_acc [Np][D] fp32 (written, or added to when accumulate).
+//   delta [nh][Np] (= rowsum(dO o O));
+//   dk_acc, dv_acc [Np][D] fp32: written, or added to when accumulate (dK/dV kernel);
+//   dq [nh][Np][D] fp32: written (dQ kernel).
 template <typename T>
 struct AttnBwd {
   const T* q;
@@ -96,7 +97,7 @@ struct AttnBwd {
   const float* lse;
   int64_t lse_stride;
   const float* delta;
-  float* dq_acc;
+  float* dq;
   float* dk_acc;
   float* dv_acc;
   int64_t N, Np;
@@ -126,7 +127,8 @@ struct GradFinish {
 template <typename T> hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s);
 template <typename T> hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s);
 template <typename T> hipError_t launch_attn_fwd(const AttnFwd<T>& p, int head_dim, int mode, hipStream_t s);
-template <typename T> hipError_t launch_attn_bwd(const AttnBwd<T>& p, int head_dim, hipStream_t s);
+template <typename T> hipError_t launch_attn_bwd_dkdv(const AttnBwd<T>& p, int head_dim, hipStream_t s);
+template <typename T> hipError_t launch_attn_bwd_dq(const AttnBwd<T>& p, int head_dim, hipStream_t s);
 template <typename T> hipError_t launch_grad_finish(const GradFinish<T>& p, int head_dim, hipStream_t s);
 template <typename T>
 hipError_t launch_transpose(const T* src, int64_t rows, int64_t cols, int64_t ld_src, T* dst,

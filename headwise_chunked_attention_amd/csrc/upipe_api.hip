@@ -387,8 +387,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
     // dWo[:, chunk] = dY^T O_c
     int rc = run_weight_grad<T>(s, dy, O, s.C, dwo + (int64_t)c0 * s.d, (int64_t)s.Hq * s.d, 1, st);
     if (rc) return rc;
-    // attention backward
-    HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dQa, (int64_t)s.C * head, 0.f, st); }));
+    // attention backward: dK/dV (key-stationary) and dQ (query-stationary)
     for (int j = 0; j < s.kvC; ++j) {
       AttnBwd<T> b;
       memset(&b, 0, sizeof(b));
@@ -399,7 +398,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       b.lse = lse + (int64_t)(c0 + j * nh) * s.N;
       b.lse_stride = s.N;
       b.delta = Delta + (int64_t)j * nh * s.Np;
-      b.dq_acc = dQa + (int64_t)j * nh * head;
+      b.dq = dQa + (int64_t)j * nh * head;
       b.dk_acc = dKa + (int64_t)j * head;
       b.dv_acc = dVa + (int64_t)j * head;
       b.N = s.N;
@@ -408,8 +407,10 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       b.accumulate = new_kv ? 0 : 1;
       b.scale_log2 = scale_log2;
       b.scale = scale;
-      HIP_TRY(timed(UPIPE_KERNEL_ATTN_BWD, 10.0 * s.d * nh * causal_pairs(s.N), st,
-                    [&] { return launch_attn_bwd<T>(b, s.d, st); }));
+      HIP_TRY(timed(UPIPE_KERNEL_ATTN_BWD_DKDV, 8.0 * s.d * nh * causal_pairs(s.N), st,
+                    [&] { return launch_attn_bwd_dkdv<T>(b, s.d, st); }));
+      HIP_TRY(timed(UPIPE_KERNEL_ATTN_BWD_DQ, 6.0 * s.d * nh * causal_pairs(s.N), st,
+                    [&] { return launch_attn_bwd_dq<T>(b, s.d, st); }));
     }
     // dq: RoPE transpose (+ RMSNorm backward), into the Q buffer
     {

@@ -130,21 +130,23 @@ int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n
  * While enabled, every kernel the library enqueues is bracketed by two
  * hipEvents on the caller's stream, and its algorithmic work (flops of the
  * exact math it implements: 2*M*N*K for a GEMM, 4*d per visible (query, key)
- * pair per head for attention forward, 10*d for attention backward) is noted.
+ * pair per head for attention forward, 8*d for the dK/dV kernel and 6*d for
+ * the dQ kernel of the attention backward) is noted.
  * upipe_profile_stop waits for the recorded events, writes per-kind totals
  * (milliseconds, launch counts, flops) into arrays of n_kinds entries, and
  * turns timing off. Process-wide state: do not profile concurrent calls from
  * several threads. Returns UPIPE_OK or UPIPE_ERR_HIP.
  */
 enum {
-  UPIPE_KERNEL_PROJECTION = 0,   /* Q/K/V and dO projection GEMMs (+ norm/RoPE epilogue) */
-  UPIPE_KERNEL_OUT_GEMM = 1,     /* y (+)= O Wo^T and dx (+)= dq Wq style GEMMs */
-  UPIPE_KERNEL_ATTN_FWD = 2,     /* causal attention forward (online softmax) */
-  UPIPE_KERNEL_ATTN_RECOMPUTE = 3, /* backward's forward recompute from the saved LSE */
-  UPIPE_KERNEL_ATTN_BWD = 4,     /* causal attention backward (dQ, dK, dV) */
-  UPIPE_KERNEL_WGRAD = 5,        /* split-K weight-gradient GEMMs */
-  UPIPE_KERNEL_OTHER = 6,        /* RoPE/RMSNorm backward, transposes, fills */
-  UPIPE_KERNEL_KINDS = 7
+  UPIPE_KERNEL_PROJECTION = 0,      /* Q/K/V and dO projection GEMMs (+ norm/RoPE epilogue) */
+  UPIPE_KERNEL_OUT_GEMM = 1,        /* y (+)= O Wo^T and dx (+)= dq Wq style GEMMs */
+  UPIPE_KERNEL_ATTN_FWD = 2,        /* causal attention forward (online softmax) */
+  UPIPE_KERNEL_ATTN_RECOMPUTE = 3,  /* backward's forward recompute from the saved LSE */
+  UPIPE_KERNEL_ATTN_BWD_DKDV = 4,   /* attention backward, key-stationary: dK, dV (8*d per pair) */
+  UPIPE_KERNEL_ATTN_BWD_DQ = 5,     /* attention backward, query-stationary: dQ (6*d per pair) */
+  UPIPE_KERNEL_WGRAD = 6,           /* split-K weight-gradient GEMMs */
+  UPIPE_KERNEL_OTHER = 7,           /* RoPE/RMSNorm backward, transposes, fills */
+  UPIPE_KERNEL_KINDS = 8
 };
 int upipe_profile_start(void);
 int upipe_profile_stop(double* total_ms, int64_t* launches, double* flops, int n_kinds);
