@@ -39,7 +39,10 @@ KERNEL_NAMES = {"attn_fwd": "attn_fwd_kernel<bf16,128,0>", "attn_recompute": "at
 # HBM bytes per launch of a kernel from rocprofv3 counters (FETCH_SIZE +
 # WRITE_SIZE, scaled by a plain copy of known size), measured on the kernel as
 # it now stands; absent (null) until measured again after a kernel change.
-TRAFFIC_BYTES = {}
+TRAFFIC_BYTES = {
+    # profiles/attn_bwd_dkdv_llama131k_c1_traffic.md (FETCH_SIZE x2.000 + WRITE_SIZE x1.000)
+    "attn_bwd_dkdv": 23.16e9,
+}
 
 
 def model_flops(N, D, hq, hkv, d):
@@ -50,7 +53,7 @@ def model_flops(N, D, hq, hkv, d):
     return 14.0 * d * hq * pairs + 12.0 * N * D * d * (hq + hkv)
 
 
-def cpu_baseline(w, sample_n=2048):
+def cpu_baseline(w, sample_n=8192):
     """Time the oracle's full fwd+bwd on a bounded sample: the same layer shape
     (d_model, heads, head_dim) at sample_n tokens. Reports model TFLOP/s."""
     import numpy as np
@@ -83,6 +86,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--n-tokens", type=int, default=None, help="override N (not the headline workload)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) so that "
+                         "profiler byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU's Ulysses share: multi-GPU runs (all-to-all over RCCL) are not part "
@@ -103,6 +109,14 @@ def main():
                                               "rope_theta"))
     dev = torch.device("cuda:0")
     api.load()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print("# calibration copy: 3 x (1 GiB read + 1 GiB written)", file=sys.stderr, flush=True)
+        del src, dst
     t0 = time.perf_counter()
     inp = LayerInputs(N, D, hq, hkv, d, "bf16", seed=0)
     t = {k: torch.from_numpy(getattr(inp, k)).to(dev).to(torch.bfloat16)
