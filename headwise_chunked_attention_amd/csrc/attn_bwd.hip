@@ -49,11 +49,11 @@ struct DkdvGeo {
   static constexpr int BKEY = 32 * KT;
   static constexpr int BQ = 32 * QT;
   static constexpr int VEC = 16 / (int)sizeof(T);
-  static constexpr int SK = lds_stride<T>(D);  // every tile is [rows][D]
+  using L = Tile<T, D>;  // every tile is [rows][D]
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + BKEY * SK;
-  static constexpr int BUF_OFF = V_OFF + BKEY * SK;  // two buffers of [Q | dO]
-  static constexpr int BUF_ELEMS = 2 * BQ * SK;
+  static constexpr int V_OFF = K_OFF + L::ELEMS(BKEY);
+  static constexpr int BUF_OFF = V_OFF + L::ELEMS(BKEY);  // two buffers of [Q | dO]
+  static constexpr int BUF_ELEMS = 2 * L::ELEMS(BQ);
   static constexpr int T_ELEMS = BUF_OFF + 2 * BUF_ELEMS;
   static constexpr int RCH = D / VEC;         // 16-byte chunks per row
   static constexpr int PER = BQ * RCH / NT;   // prefetch chunks per thread and tensor
@@ -78,14 +78,15 @@ DEV void store_rows(T* S, const u32x4 (&r)[G::PER]) {
 #pragma unroll
   for (int i = 0; i < G::PER; ++i) {
     const int c = threadIdx.x + i * G::NT;
-    st_raw16(S + (c / G::RCH) * G::SK + (c % G::RCH) * G::VEC, r[i]);
+    st_raw16(S + G::L::idx(c / G::RCH, (c % G::RCH) * G::VEC), r[i]);
   }
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(const AttnBwd<T> p) {
   using G = DkdvGeo<T, D>;
-  constexpr int BQ = G::BQ, BKEY = G::BKEY, ND = D / 32, NS = D / 16, SK = G::SK;
+  constexpr int BQ = G::BQ, BKEY = G::BKEY, ND = D / 32, NS = D / 16;
+  using L = typename G::L;
   extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
   T* sm = reinterpret_cast<T*>(dyn_smem);
   T* Ks = sm + G::K_OFF;
@@ -102,8 +103,8 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
 
   for (int c = tid; c < BKEY * G::RCH; c += G::NT) {
     const int row = c / G::RCH, cc = c % G::RCH;
-    st_raw16(Ks + row * SK + cc * G::VEC, ld_raw16(p.k + (k0 + row) * D + cc * G::VEC));
-    st_raw16(Vs + row * SK + cc * G::VEC, ld_raw16(p.v + (k0 + row) * D + cc * G::VEC));
+    st_raw16(Ks + L::idx(row, cc * G::VEC), ld_raw16(p.k + (k0 + row) * D + cc * G::VEC));
+    st_raw16(Vs + L::idx(row, cc * G::VEC), ld_raw16(p.v + (k0 + row) * D + cc * G::VEC));
   }
   f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -118,9 +119,8 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
 
   u32x4 rq[G::PER], rdo[G::PER];
   float rl = 0.f, rd = 0.f;
-  auto prefetch = [&](int64_t it) {
-    const int hh = (int)(it / nqt);
-    const int64_t q0 = k0 + (it % nqt) * BQ;
+  // (head, query tile) of a step, without 64-bit division in the loop
+  auto prefetch = [&](int hh, int64_t q0) {
     load_rows<T, D, G>(p.q + (int64_t)hh * p.Np * D, q0, rq);
     load_rows<T, D, G>(p.dout + (int64_t)hh * p.Np * D, q0, rdo);
     if (tid < BQ) {
@@ -131,23 +131,30 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   };
   auto commit = [&](int b) {
     store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS, rq);
-    store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS + BQ * SK, rdo);
+    store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS + L::ELEMS(BQ), rdo);
     if (tid < BQ) {
       stat[b * 2 * BQ + tid] = rl;
       stat[b * 2 * BQ + BQ + tid] = rd;
     }
   };
 
-  prefetch(0);
+  prefetch(0, k0);
   commit(0);
   lds_barrier();
 
+  int hh = 0;
+  int64_t q0 = k0;
   for (int64_t it = 0; it < total; ++it) {
     const int b = (int)(it & 1);
-    const int64_t q0 = k0 + (it % nqt) * BQ;
-    if (it + 1 < total) prefetch(it + 1);
+    int nh_next = hh;
+    int64_t q_next = q0 + BQ;
+    if (q_next >= qend) {
+      q_next = k0;
+      ++nh_next;
+    }
+    if (it + 1 < total) prefetch(nh_next, q_next);
     const T* Qs = sm + G::BUF_OFF + b * G::BUF_ELEMS;
-    const T* dOs = Qs + BQ * SK;
+    const T* dOs = Qs + L::ELEMS(BQ);
     const float* lse_s = stat + b * 2 * BQ;
     const float* del_s = lse_s + BQ;
     const int qrel0 = (int)(q0 - k0) + qt * 32;                            // wave's first row - block start
@@ -157,10 +164,10 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const Frag<T> kb = ld_frag(Ks + krel * SK + s * 16 + 8 * h);
-      const Frag<T> vb = ld_frag(Vs + krel * SK + s * 16 + 8 * h);
-      mma(sacc, ld_frag(Qs + (qt * 32 + r) * SK + s * 16 + 8 * h), kb);
-      mma(dpacc, ld_frag(dOs + (qt * 32 + r) * SK + s * 16 + 8 * h), vb);
+      const Frag<T> kb = ld_frag(Ks + L::idx(krel, s * 16 + 8 * h));
+      const Frag<T> vb = ld_frag(Vs + L::idx(krel, s * 16 + 8 * h));
+      mma(sacc, ld_frag(Qs + L::idx(qt * 32 + r, s * 16 + 8 * h)), kb);
+      mma(dpacc, ld_frag(dOs + L::idx(qt * 32 + r, s * 16 + 8 * h)), vb);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -184,14 +191,16 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       const int row0 = qt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
       for (int j = 0; j < ND; ++j) {
-        const Frag<T> ado = frag_from_col4<T>(ld_col4<T>(dOs, SK, row0, j * 32), ld_col4<T>(dOs, SK, row0 + 8, j * 32));
+        const Frag<T> ado = frag_from_col4<T>(ld_col4<L>(dOs, row0, j * 32), ld_col4<L>(dOs, row0 + 8, j * 32));
         mma(dv[j], ado, pb);
-        const Frag<T> aq = frag_from_col4<T>(ld_col4<T>(Qs, SK, row0, j * 32), ld_col4<T>(Qs, SK, row0 + 8, j * 32));
+        const Frag<T> aq = frag_from_col4<T>(ld_col4<L>(Qs, row0, j * 32), ld_col4<L>(Qs, row0 + 8, j * 32));
         mma(dk[j], aq, sb);
       }
     }
     if (it + 1 < total) commit(b ^ 1);
     lds_barrier();
+    hh = nh_next;
+    q0 = q_next;
   }
 
   // Sum the QT partial dK/dV of each key tile through LDS, then write rows of
@@ -247,8 +256,8 @@ template <typename T, int D>
 struct DqGeo {
   static constexpr int NW = 8;  // waves per workgroup, 32 queries each
   static constexpr int NT = 64 * NW;
-  static constexpr int SK = lds_stride<T>(D);
-  static constexpr int STAGE = 2 * BC * SK;  // K tile then V tile
+  using L = Tile<T, D>;
+  static constexpr int STAGE = 2 * L::ELEMS(BC);  // K tile then V tile
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int RCH = D / VEC;
   static constexpr int KCH = BC * RCH / NT;  // 16-byte chunks per thread and tensor
@@ -258,7 +267,8 @@ struct DqGeo {
 template <typename T, int D>
 __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const AttnBwd<T> p, int hp) {
   using G = DqGeo<T, D>;
-  constexpr int ND = D / 32, NS = D / 16, SK = G::SK;
+  constexpr int ND = D / 32, NS = D / 16;
+  using L = typename G::L;
   extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
   T* smem = reinterpret_cast<T*>(dyn_smem);
 
@@ -298,8 +308,8 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
 #pragma unroll
     for (int i = 0; i < G::KCH; ++i) {
       const int c = threadIdx.x + i * G::NT;
-      st_raw16(st + (c / G::RCH) * SK + (c % G::RCH) * G::VEC, rk[i]);
-      st_raw16(st + BC * SK + (c / G::RCH) * SK + (c % G::RCH) * G::VEC, rv[i]);
+      st_raw16(st + L::idx(c / G::RCH, (c % G::RCH) * G::VEC), rk[i]);
+      st_raw16(st + L::ELEMS(BC) + L::idx(c / G::RCH, (c % G::RCH) * G::VEC), rv[i]);
     }
   };
 
@@ -313,7 +323,7 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
     const int buf = (int)(kt_i & 1);
     if (kt_i + 1 < ntiles) load(k0 + BC, rk, rv);
     const T* Ks = smem + buf * G::STAGE;
-    const T* Vs = Ks + BC * SK;
+    const T* Vs = Ks + L::ELEMS(BC);
     if (k0 <= q0w + 31) {  // some key of the tile is visible to this wave
       f32x16 sacc[2], dpacc[2];
 #pragma unroll
@@ -325,8 +335,8 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          mma(sacc[kt], ld_frag(Ks + (kt * 32 + r) * SK + s * 16 + 8 * h), qf[s]);
-          mma(dpacc[kt], ld_frag(Vs + (kt * 32 + r) * SK + s * 16 + 8 * h), df[s]);
+          mma(sacc[kt], ld_frag(Ks + L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[s]);
+          mma(dpacc[kt], ld_frag(Vs + L::idx(kt * 32 + r, s * 16 + 8 * h)), df[s]);
         }
       const int qrel = (int)(q - k0);
 #pragma unroll
@@ -346,7 +356,7 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
           const int row0 = kt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
           for (int j = 0; j < ND; ++j) {
-            const Frag<T> a = frag_from_col4<T>(ld_col4<T>(Ks, SK, row0, j * 32), ld_col4<T>(Ks, SK, row0 + 8, j * 32));
+            const Frag<T> a = frag_from_col4<T>(ld_col4<L>(Ks, row0, j * 32), ld_col4<L>(Ks, row0 + 8, j * 32));
             mma(dq[j], a, sb);
           }
         }

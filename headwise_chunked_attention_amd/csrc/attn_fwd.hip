@@ -35,9 +35,9 @@ struct FwdGeo {
   static constexpr int NTHREADS = 64 * NW;
   static constexpr int NQT = 1;                // 32-query tiles per wave
   static constexpr int ROWS_W = 32 * NQT;
-  static constexpr int SKD = lds_stride<T>(D);   // K and V tile row stride
-  static constexpr int K_ELEMS = BC * SKD;
-  static constexpr int V_ELEMS = BC * SKD;
+  using L = Tile<T, D>;                          // K and V tiles [key][d]
+  static constexpr int K_ELEMS = L::ELEMS(BC);
+  static constexpr int V_ELEMS = L::ELEMS(BC);
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int KCH = BC * D / VEC / NTHREADS;  // 16-byte chunks per thread (K)
@@ -69,8 +69,8 @@ DEV void store_kv(T* stage, const u32x4 (&rk)[FwdGeo<T, D>::KCH], const u32x4 (&
 #pragma unroll
   for (int i = 0; i < G::KCH; ++i) {
     const int c = tid + i * G::NTHREADS;
-    st_raw16(Ks + (c / KC_ROW) * G::SKD + (c % KC_ROW) * G::VEC, rk[i]);
-    st_raw16(Vs + (c / KC_ROW) * G::SKD + (c % KC_ROW) * G::VEC, rv[i]);
+    st_raw16(Ks + G::L::idx(c / KC_ROW, (c % KC_ROW) * G::VEC), rk[i]);
+    st_raw16(Vs + G::L::idx(c / KC_ROW, (c % KC_ROW) * G::VEC), rv[i]);
   }
 }
 
@@ -137,7 +137,7 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
       for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const Frag<T> a = ld_frag(Ks + (kt * 32 + r) * G::SKD + s * 16 + 8 * h);
+          const Frag<T> a = ld_frag(Ks + G::L::idx(kt * 32 + r, s * 16 + 8 * h));
 #pragma unroll
           for (int t = 0; t < NQT; ++t) mma(sacc[kt][t], a, qf[t][s]);
         }
@@ -201,8 +201,8 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
           const int row0 = kt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
           for (int j = 0; j < ND; ++j) {
-            const Frag<T> a = frag_from_col4<T>(ld_col4<T>(Vs, G::SKD, row0, j * 32),
-                                                ld_col4<T>(Vs, G::SKD, row0 + 8, j * 32));
+            const Frag<T> a = frag_from_col4<T>(ld_col4<typename G::L>(Vs, row0, j * 32),
+                                                ld_col4<typename G::L>(Vs, row0 + 8, j * 32));
 #pragma unroll
             for (int t = 0; t < NQT; ++t) mma(oacc[t][j], a, pf[t]);
           }

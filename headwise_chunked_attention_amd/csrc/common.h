@@ -155,30 +155,60 @@ template <typename T> constexpr int lds_stride(int cols) { return cols + 16 / (i
 DEV float wave_max_pair(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// ---- column reads from row-major LDS tiles -------------------------------
+// ---- LDS tile layout --------------------------------------------------------
+// A row-major tile of COLS elements per row. bf16 tiles with 64 or 128 columns
+// are stored without padding and their 16-byte chunks are XOR-swizzled by row:
+// chunk c of row r lives at chunk position c ^ swz(r). swz is chosen so that
+// both access patterns of the kernels are free of bank conflicts:
+//   * 16-byte row reads of 16 consecutive rows at one chunk (MFMA operands);
+//   * column reads (ds_read_b64_tr_b16) touching 4 consecutive rows and 4
+//     consecutive chunks.
+// Other tiles keep 16 bytes of padding per row and no swizzle.
+template <typename T, int COLS>
+struct Tile {
+  static constexpr int ROW_BYTES = COLS * (int)sizeof(T);
+  static constexpr bool SWZ = sizeof(T) == 2 && (ROW_BYTES == 256 || ROW_BYTES == 128);
+  static constexpr int STRIDE = SWZ ? COLS : COLS + 16 / (int)sizeof(T);
+  static constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int ELEMS(int rows) { return rows * STRIDE; }
+  DEV static int swz(int row) {
+    if constexpr (ROW_BYTES == 256) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+  // element offset of (row, col); col may point inside a 16-byte chunk
+  DEV static int idx(int row, int col) {
+    if constexpr (!SWZ) return row * STRIDE + col;
+    else return row * STRIDE + (((col / E) ^ swz(row)) * E) + (col % E);
+  }
+};
+
+// ---- column reads from LDS tiles -------------------------------------------
 // For lane l, the four values X[k0 + j][c0 + 16*((l >> 4) & 1) + (l & 15)],
-// j = 0..3, of a row-major tile X (row stride S elements) in LDS: a column
-// segment of 4 rows. On gfx950 this is one ds_read_b64_tr_b16 for bf16:
-// within each 16-lane group, lane L points at the 4 elements
-// X[k0 + L/4][cbase + 4*(L%4) .. +3], and the hardware hands lane i the
-// column cbase + i of that 4 x 16 block (verified on the device).
+// j = 0..3, of a tile X in LDS: a column segment of 4 rows. On gfx950 this is
+// one ds_read_b64_tr_b16 for bf16: within each 16-lane group, lane L points at
+// the 4 elements X[k0 + L/4][cbase + 4*(L%4) .. +3], and the hardware hands
+// lane i the column cbase + i of that 4 x 16 block (verified on the device).
 template <typename T> struct Vec4;
 template <> struct Vec4<bf16> { typedef bf16x4 type; };
 template <> struct Vec4<float> { typedef f32x4 type; };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-template <typename T> DEV typename Vec4<T>::type ld_col4(const T* X, int S, int k0, int c0);
-template <> DEV bf16x4 ld_col4<bf16>(const bf16* X, int S, int k0, int c0) {
-  const int l = lane_id(), L = l & 15;
-  const bf16* p = X + (k0 + (L >> 2)) * S + c0 + 16 * ((l >> 4) & 1) + 4 * (L & 3);
+template <class L, typename T> DEV typename Vec4<T>::type ld_col4(const T* X, int k0, int c0);
+template <class L> DEV bf16x4 ld_col4_bf16(const bf16* X, int k0, int c0) {
+  const int l = lane_id(), Ln = l & 15;
+  const bf16* p = X + L::idx(k0 + (Ln >> 2), c0 + 16 * ((l >> 4) & 1) + 4 * (Ln & 3));
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
   return __builtin_bit_cast(bf16x4, v);
 }
-template <> DEV f32x4 ld_col4<float>(const float* X, int S, int k0, int c0) {
+template <class L> DEV f32x4 ld_col4_f32(const float* X, int k0, int c0) {
   const int l = lane_id();
-  const float* p = X + k0 * S + c0 + 16 * ((l >> 4) & 1) + (l & 15);
-  return (f32x4){p[0], p[S], p[2 * S], p[3 * S]};
+  const int c = c0 + 16 * ((l >> 4) & 1) + (l & 15);
+  return (f32x4){X[L::idx(k0, c)], X[L::idx(k0 + 1, c)], X[L::idx(k0 + 2, c)], X[L::idx(k0 + 3, c)]};
+}
+template <class L, typename T> DEV typename Vec4<T>::type ld_col4(const T* X, int k0, int c0) {
+  if constexpr (sizeof(T) == 2) return ld_col4_bf16<L>(X, k0, c0);
+  else return ld_col4_f32<L>(X, k0, c0);
 }
 
 template <typename T> DEV Frag<T> frag_from_col4(typename Vec4<T>::type lo, typename Vec4<T>::type hi);
@@ -203,3 +233,25 @@ DEV void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// ---- direct global -> LDS tile loads (bf16 swizzled tiles) ------------------
+// One wave instruction moves 64 x 16 bytes from global memory straight into
+// 1 KB of contiguous LDS (lane l lands at byte 16*l of the wave's LDS base):
+// for a swizzled tile that is rows [r0, r0 + 1024/ROW_BYTES) with lane l
+// filling physical chunk l % CPR of row r0 + l / CPR, so it fetches logical
+// chunk (l % CPR) ^ swz(row). No registers hold the data and the LDS writes
+// happen asynchronously; completion is tracked by vmcnt.
+template <class L, typename T>
+DEV void dma_tile_rows(const T* src, int64_t src_ld, T* lds_tile, int row0) {
+  static_assert(L::SWZ, "direct loads need the unpadded swizzled layout");
+  constexpr int CPR = L::ROW_BYTES / 16;  // 16-byte chunks per row
+  const int l = lane_id();
+  const int row = row0 + l / CPR;
+  const int chunk = (l % CPR) ^ L::swz(row);
+  const T* g = src + (int64_t)row * src_ld + chunk * L::E;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
+                                   (__attribute__((address_space(3))) void*)(lds_tile + row0 * L::STRIDE), 16, 0, 0);
+}
+
+// Wait for this wave's outstanding vector-memory operations (direct LDS loads included).
+DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0), expcnt(7), lgkmcnt(15)
