@@ -39,10 +39,7 @@ KERNEL_NAMES = {"attn_fwd": "attn_fwd_kernel<bf16,128,0>", "attn_recompute": "at
 # HBM bytes per launch of a kernel from rocprofv3 counters (FETCH_SIZE +
 # WRITE_SIZE, scaled by a plain copy of known size), measured on the kernel as
 # it now stands; absent (null) until measured again after a kernel change.
-TRAFFIC_BYTES = {
-    # profiles/attn_bwd_dkdv_llama131k_c1_traffic.md (FETCH_SIZE x2.000 + WRITE_SIZE x1.000)
-    "attn_bwd_dkdv": 23.16e9,
-}
+TRAFFIC_BYTES = {}
 
 
 def model_flops(N, D, hq, hkv, d):

@@ -117,12 +117,23 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   const int64_t nqt = (qend - k0) / BQ;  // k0 is a multiple of BQ
   const int64_t total = nqt * p.nh;
 
-  u32x4 rq[G::PER], rdo[G::PER];
+  constexpr bool DMA = L::SWZ;  // bf16: Q/dO tiles by direct global -> LDS loads
+  u32x4 rq[DMA ? 1 : G::PER], rdo[DMA ? 1 : G::PER];
   float rl = 0.f, rd = 0.f;
   // (head, query tile) of a step, without 64-bit division in the loop
-  auto prefetch = [&](int hh, int64_t q0) {
-    load_rows<T, D, G>(p.q + (int64_t)hh * p.Np * D, q0, rq);
-    load_rows<T, D, G>(p.dout + (int64_t)hh * p.Np * D, q0, rdo);
+  auto prefetch = [&](int hh, int64_t q0, int dst) {
+    if constexpr (DMA) {
+      constexpr int ROWS_PER_INST = 1024 / L::ROW_BYTES;
+      constexpr int INST = BQ / ROWS_PER_INST;
+      T* qd = sm + G::BUF_OFF + dst * G::BUF_ELEMS;
+      for (int i = w; i < INST; i += G::NW) {
+        dma_tile_rows<L>(p.q + (int64_t)hh * p.Np * D + q0 * D, D, qd, i * ROWS_PER_INST);
+        dma_tile_rows<L>(p.dout + (int64_t)hh * p.Np * D + q0 * D, D, qd + L::ELEMS(BQ), i * ROWS_PER_INST);
+      }
+    } else {
+      load_rows<T, D, G>(p.q + (int64_t)hh * p.Np * D, q0, rq);
+      load_rows<T, D, G>(p.dout + (int64_t)hh * p.Np * D, q0, rdo);
+    }
     if (tid < BQ) {
       const int64_t q = q0 + tid;
       rl = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : 0.f;
@@ -130,15 +141,19 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     }
   };
   auto commit = [&](int b) {
-    store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS, rq);
-    store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS + L::ELEMS(BQ), rdo);
+    if constexpr (DMA) {
+      wait_vmem();  // this wave's direct loads into buffer b have landed
+    } else {
+      store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS, rq);
+      store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS + L::ELEMS(BQ), rdo);
+    }
     if (tid < BQ) {
       stat[b * 2 * BQ + tid] = rl;
       stat[b * 2 * BQ + BQ + tid] = rd;
     }
   };
 
-  prefetch(0, k0);
+  prefetch(0, k0, 0);
   commit(0);
   lds_barrier();
 
@@ -152,7 +167,7 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       q_next = k0;
       ++nh_next;
     }
-    if (it + 1 < total) prefetch(nh_next, q_next);
+    if (it + 1 < total) prefetch(nh_next, q_next, b ^ 1);
     const T* Qs = sm + G::BUF_OFF + b * G::BUF_ELEMS;
     const T* dOs = Qs + L::ELEMS(BQ);
     const float* lse_s = stat + b * 2 * BQ;
@@ -313,15 +328,36 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
     }
   };
 
+  constexpr bool DMA = L::SWZ;  // bf16: K/V tiles by direct global -> LDS loads
+  auto dma = [&](int64_t k0, T* st) {
+    if constexpr (DMA) {
+      constexpr int ROWS_PER_INST = 1024 / L::ROW_BYTES;
+      constexpr int INST = BC / ROWS_PER_INST;
+      for (int i = w; i < INST; i += G::NW) {
+        dma_tile_rows<L>(p.k + k0 * D, D, st, i * ROWS_PER_INST);
+        dma_tile_rows<L>(p.v + k0 * D, D, st + L::ELEMS(BC), i * ROWS_PER_INST);
+      }
+    }
+  };
   const int64_t ntiles = (qs + qb_rows) / BC;
-  u32x4 rk[G::KCH], rv[G::KCH];
-  load(0, rk, rv);
-  store(smem, rk, rv);
+  u32x4 rk[DMA ? 1 : G::KCH], rv[DMA ? 1 : G::KCH];
+  if constexpr (DMA) {
+    dma(0, smem);
+    wait_vmem();
+  } else {
+    load(0, rk, rv);
+    store(smem, rk, rv);
+  }
   lds_barrier();
   for (int64_t kt_i = 0; kt_i < ntiles; ++kt_i) {
     const int64_t k0 = kt_i * BC;
     const int buf = (int)(kt_i & 1);
-    if (kt_i + 1 < ntiles) load(k0 + BC, rk, rv);
+    if (kt_i + 1 < ntiles) {
+      if constexpr (DMA)
+        dma(k0 + BC, smem + (buf ^ 1) * G::STAGE);
+      else
+        load(k0 + BC, rk, rv);
+    }
     const T* Ks = smem + buf * G::STAGE;
     const T* Vs = Ks + L::ELEMS(BC);
     if (k0 <= q0w + 31) {  // some key of the tile is visible to this wave
@@ -361,7 +397,12 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
           }
         }
     }
-    if (kt_i + 1 < ntiles) store(smem + (buf ^ 1) * G::STAGE, rk, rv);
+    if (kt_i + 1 < ntiles) {
+      if constexpr (DMA)
+        wait_vmem();
+      else
+        store(smem + (buf ^ 1) * G::STAGE, rk, rv);
+    }
     lds_barrier();
   }
   // dQ rows of this lane's query: C tiles hold rows = head dim.

@@ -74,6 +74,21 @@ DEV void store_kv(T* stage, const u32x4 (&rk)[FwdGeo<T, D>::KCH], const u32x4 (&
   }
 }
 
+// Issue the K and V tile starting at key k0 into an LDS stage with direct
+// global -> LDS loads (bf16): each wave moves its share of the rows.
+template <typename T, int D>
+DEV void dma_kv(const AttnFwd<T>& p, int64_t k0, T* stage) {
+  using G = FwdGeo<T, D>;
+  using L = typename G::L;
+  constexpr int ROWS_PER_INST = 1024 / L::ROW_BYTES;
+  constexpr int INST = BC / ROWS_PER_INST;  // per tensor
+  const int w = wave_id();
+  for (int i = w; i < INST; i += G::NW) {
+    dma_tile_rows<L>(p.k + k0 * D, D, stage, i * ROWS_PER_INST);
+    dma_tile_rows<L>(p.v + k0 * D, D, stage + G::K_ELEMS, i * ROWS_PER_INST);
+  }
+}
+
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(const AttnFwd<T> p, int hp) {
   using G = FwdGeo<T, D>;
@@ -115,15 +130,26 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
     for (int j = 0; j < ND; ++j) oacc[t][j] = zero16();
 
   const int64_t ntiles = (qs + qb_rows) / BC;
-  u32x4 rk[G::KCH], rv[G::VCH];
-  load_kv<T, D>(p, 0, rk, rv);
-  store_kv<T, D>(smem, rk, rv);
+  constexpr bool DMA = G::L::SWZ;  // bf16: direct global -> LDS loads
+  u32x4 rk[DMA ? 1 : G::KCH], rv[DMA ? 1 : G::VCH];
+  if constexpr (DMA) {
+    dma_kv<T, D>(p, 0, smem);
+    wait_vmem();
+  } else {
+    load_kv<T, D>(p, 0, rk, rv);
+    store_kv<T, D>(smem, rk, rv);
+  }
   lds_barrier();
 
   for (int64_t kt_i = 0; kt_i < ntiles; ++kt_i) {
     const int64_t k0 = kt_i * BC;
     const int buf = (int)(kt_i & 1);
-    if (kt_i + 1 < ntiles) load_kv<T, D>(p, k0 + BC, rk, rv);
+    if (kt_i + 1 < ntiles) {
+      if constexpr (DMA)
+        dma_kv<T, D>(p, k0 + BC, smem + (buf ^ 1) * G::STAGE);
+      else
+        load_kv<T, D>(p, k0 + BC, rk, rv);
+    }
     const T* Ks = smem + buf * G::STAGE;
     const T* Vs = Ks + G::K_ELEMS;
 
@@ -208,7 +234,12 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
           }
         }
     }
-    if (kt_i + 1 < ntiles) store_kv<T, D>(smem + (buf ^ 1) * G::STAGE, rk, rv);
+    if (kt_i + 1 < ntiles) {
+      if constexpr (DMA)
+        wait_vmem();
+      else
+        store_kv<T, D>(smem + (buf ^ 1) * G::STAGE, rk, rv);
+    }
     lds_barrier();
   }
 
