@@ -97,7 +97,7 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   const int w = wave_id();
   const int kt = w % G::KT, qt = w / G::KT;
   const int tid = threadIdx.x;
-  const int64_t k0 = (int64_t)blockIdx.x * BKEY;  // block 0 has the most query tiles
+  const int64_t k0 = xcd_remap(blockIdx.x, gridDim.x) * BKEY;  // block 0 has the most query tiles
   const int krel = kt * 32 + r;                   // this lane's key within the block
   const int64_t kw = k0 + krel;
 

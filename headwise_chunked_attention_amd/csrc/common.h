@@ -144,6 +144,19 @@ template <> DEV void st16_f<float>(float* p, const float* in) {
 
 // Raw 16-byte copy unit.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// VEC (=16/sizeof(T)) elements held in a raw 16-byte register value, as floats.
+template <typename T> DEV void raw16_to_f(u32x4 r, float* out);
+template <> DEV void raw16_to_f<bf16>(u32x4 r, float* out) {
+  const bf16x8 v = __builtin_bit_cast(bf16x8, r);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+}
+template <> DEV void raw16_to_f<float>(u32x4 r, float* out) {
+  const f32x4 v = __builtin_bit_cast(f32x4, r);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = v[i];
+}
 DEV u32x4 ld_raw16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 DEV void st_raw16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 DEV u32x4 zero_raw16() { return (u32x4){0u, 0u, 0u, 0u}; }
@@ -255,3 +268,19 @@ DEV void dma_tile_rows(const T* src, int64_t src_ld, T* lds_tile, int row0) {
 
 // Wait for this wave's outstanding vector-memory operations (direct LDS loads included).
 DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0), expcnt(7), lgkmcnt(15)
+
+// ---- XCD-aware block order ----------------------------------------------------
+// The dispatcher hands workgroup b to XCD b % 8, and each XCD has its own L2.
+// Blocks that share operands should run on the same XCD at the same time, so a
+// logical block index is assigned in groups of 8 consecutive logical blocks
+// per XCD: hardware block b (XCD b % 8, its (b / 8)-th block there) gets
+// logical block (slot / 8) * 64 + xcd * 8 + slot % 8. Every XCD still walks
+// the logical order from first to last (heavy-first schedules stay balanced).
+// Bijective on [0, n); a tail of fewer than 64 blocks keeps its index.
+DEV int64_t xcd_remap(int64_t b, int64_t n) {
+  constexpr int64_t X = 8, G = 8;
+  const int64_t full = n - n % (X * G);
+  if (b >= full) return b;
+  const int64_t xcd = b % X, slot = b / X;
+  return (slot / G) * (X * G) + xcd * G + (slot % G);
+}

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   T* Bs = As + 2 * BM * SK;
 
   const int64_t ntn = p.N / BN;
-  const int64_t bid = blockIdx.x;
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);  // n-tiles of one m-tile share an XCD's L2
   const int64_t mtile = bid / ntn, ntile = bid % ntn;
   const int64_t m0 = mtile * BM, n0 = ntile * BN;
   int seg = 0;
@@ -159,21 +159,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   const int tid = threadIdx.x;
 
   if constexpr (EPI == EPI_ACCUM) {
-    for (int c = tid; c < BM * BN / VEC; c += NTHREADS) {
+    // all loads of the old values first, then add and store (memory-level parallelism)
+    constexpr int CH = BM * BN / VEC / NTHREADS;
+    u32x4 old[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + i * NTHREADS;
+      const int row = c / (BN / VEC), cv = c % (BN / VEC);
+      const int64_t m = m0 + row;
+      old[i] = (p.accumulate && m < p.M) ? ld_raw16(p.c + m * p.ldc + n0 + cv * VEC) : zero_raw16();
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + i * NTHREADS;
       const int row = c / (BN / VEC), cv = c % (BN / VEC);
       const int64_t m = m0 + row;
       if (m >= p.M) continue;
-      float v[VEC];
+      float v[VEC], o[VEC];
+      raw16_to_f<T>(old[i], o);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
-      T* dst = p.c + m * p.ldc + n0 + cv * VEC;
-      if (p.accumulate) {
-        float old[VEC];
-        ld16_f<T>(dst, old);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) v[e] += old[e];
-      }
-      st16_f<T>(dst, v);
+      for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e] + o[e];
+      st16_f<T>(p.c + m * p.ldc + n0 + cv * VEC, v);
     }
   } else {
     const HeadOut<T> ho = p.ho[seg];
@@ -309,9 +315,13 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   T* As = reinterpret_cast<T*>(smem);       // [2][BM][SK]
   T* Bs = As + 2 * BM * SK;                 // [2][BN][SK]
 
-  const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int64_t n0 = (int64_t)blockIdx.y * BN;
-  const int64_t kb = (int64_t)blockIdx.z * p.ksplit;
+  // 1-D grid: m-tile fastest, so the blocks that read the same head tile (B)
+  // are consecutive logical blocks and run on one XCD together.
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t gm = p.M / BM, gn = p.N / BN;
+  const int64_t m0 = (bid % gm) * BM;
+  const int64_t n0 = ((bid / gm) % gn) * BN;
+  const int64_t kb = (bid / (gm * gn)) * p.ksplit;
   const int64_t ke = (kb + p.ksplit < p.K) ? kb + p.ksplit : p.K;
 
   auto aaddr = [&](int64_t k, int col) { return p.a + k * p.lda + m0 + col; };
@@ -392,7 +402,7 @@ hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s) {
-  const dim3 grid((unsigned)(p.M / BM), (unsigned)(p.N / bn), (unsigned)((p.K + p.ksplit - 1) / p.ksplit));
+  const dim3 grid((unsigned)((p.M / BM) * (p.N / bn) * ((p.K + p.ksplit - 1) / p.ksplit)));
   if (bn == 128)
     hipLaunchKernelGGL((gemm_tn_kernel<T, 128>), grid, dim3(NTHREADS), 0, s, p);
   else if (bn == 64)
