@@ -8,8 +8,9 @@
 // gemm_tn: out += A^T B with both operands contiguous along the free dims and
 //   k = tokens; the weight gradients (dWq = dq^T x, dWo = dY^T O, ...). Each
 //   workgroup takes one 128 x BN output tile over one slice of the tokens
-//   (split-K), transposes its tiles into k-contiguous LDS rows on the way in
-//   and adds its partial sum into the fp32 output with atomics.
+//   (split-K), keeps its token-major tiles row-major in LDS, reads the MFMA
+//   operands as columns, and adds its partial sum into the fp32 output with
+//   atomics.
 #include <math.h>
 
 #include "common.h"
@@ -251,69 +252,58 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
 // ------------------------------------------------------------------------
 // split-K GEMM for weight gradients
 // ------------------------------------------------------------------------
-template <typename T> DEV void st_pair(T* p, float a, float b);
-template <> DEV void st_pair<bf16>(bf16* p, float a, float b) {
-  *reinterpret_cast<bf16x2*>(p) = (bf16x2){(bf16)a, (bf16)b};
-}
-template <> DEV void st_pair<float>(float* p, float a, float b) {
-  *reinterpret_cast<f32x2*>(p) = (f32x2){a, b};
-}
-
-// Units of (token pair, VEC columns): loads two 16-byte rows, stores VEC
-// transposed pairs into LDS rows [col][tok].
+// A token-major tile [BK tokens][COLS] kept row-major in LDS (Tile layout):
+// the global loads are coalesced (consecutive lanes take consecutive 16-byte
+// chunks of a row) and the MFMA operands, which need 8 consecutive tokens for
+// one column, are column reads (LDS transpose reads for bf16).
 template <typename T, int COLS>
 struct TnTile {
-  static constexpr int VEC = GemmGeo<T>::VEC, BK = GemmGeo<T>::BK;
-  static constexpr int UNITS = (BK / 2) * (COLS / VEC);
-  static constexpr int PER = (UNITS + NTHREADS - 1) / NTHREADS;
+  using L = Tile<T, COLS>;
+  static constexpr int VEC = 16 / (int)sizeof(T), BK = GemmGeo<T>::BK;
+  static constexpr int RCH = COLS / VEC;        // 16-byte chunks per row
+  static constexpr int PER = BK * RCH / NTHREADS;  // chunks per thread
+  static_assert((BK * RCH) % NTHREADS == 0, "tile chunks");
 };
 
 template <typename T, int COLS, typename AddrFn>
-DEV void tn_load(AddrFn addr, int64_t k0, int64_t K, float (&r)[TnTile<T, COLS>::PER][2][16 / sizeof(T)]) {
+DEV void tn_load(AddrFn addr, int64_t k0, int64_t K, u32x4 (&r)[TnTile<T, COLS>::PER]) {
   using G = TnTile<T, COLS>;
-  constexpr int VEC = G::VEC;
-  const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < G::PER; ++i) {
-    const int u = tid + i * NTHREADS;
-    if (u >= G::UNITS) break;
-    const int pr = u % (G::BK / 2), cc = u / (G::BK / 2);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t k = k0 + 2 * pr + t;
-      if (k < K) {
-        ld16_f<T>(addr(k, cc * VEC), r[i][t]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) r[i][t][e] = 0.f;
-      }
-    }
+    const int c = threadIdx.x + i * NTHREADS;
+    const int64_t k = k0 + c / G::RCH;
+    r[i] = (k < K) ? ld_raw16(addr(k, (c % G::RCH) * G::VEC)) : zero_raw16();
   }
 }
 
 template <typename T, int COLS>
-DEV void tn_store(T* S, const float (&r)[TnTile<T, COLS>::PER][2][16 / sizeof(T)]) {
+DEV void tn_store(T* S, const u32x4 (&r)[TnTile<T, COLS>::PER]) {
   using G = TnTile<T, COLS>;
-  constexpr int VEC = G::VEC, SK = GemmGeo<T>::SK;
-  const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < G::PER; ++i) {
-    const int u = tid + i * NTHREADS;
-    if (u >= G::UNITS) break;
-    const int pr = u % (G::BK / 2), cc = u / (G::BK / 2);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) st_pair<T>(S + (cc * VEC + e) * SK + 2 * pr, r[i][0][e], r[i][1][e]);
+    const int c = threadIdx.x + i * NTHREADS;
+    st_raw16(S + G::L::idx(c / G::RCH, (c % G::RCH) * G::VEC), r[i]);
   }
 }
 
 template <typename T, int BN>
+constexpr int tn_smem_bytes() {
+  constexpr int BK = GemmGeo<T>::BK;
+  constexpr int main_bytes = 2 * (Tile<T, BM>::ELEMS(BK) + Tile<T, BN>::ELEMS(BK)) * (int)sizeof(T);
+  constexpr int epi_bytes = BM * (BN + 4) * 4;
+  return main_bytes > epi_bytes ? main_bytes : epi_bytes;
+}
+
+template <typename T, int BN>
 __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
-  constexpr int BK = GemmGeo<T>::BK, SK = GemmGeo<T>::SK;
+  constexpr int BK = GemmGeo<T>::BK;
   constexpr int NTW = BN / 64, SC = BN + 4;
-  constexpr int VEC = GemmGeo<T>::VEC;
-  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<T, BN>()];
-  T* As = reinterpret_cast<T*>(smem);       // [2][BM][SK]
-  T* Bs = As + 2 * BM * SK;                 // [2][BN][SK]
+  using LA = Tile<T, BM>;
+  using LB = Tile<T, BN>;
+  constexpr int A_EL = LA::ELEMS(BK), B_EL = LB::ELEMS(BK);
+  __shared__ __attribute__((aligned(16))) char smem[tn_smem_bytes<T, BN>()];
+  T* As = reinterpret_cast<T*>(smem);  // [2][BK tokens][BM]
+  T* Bs = As + 2 * A_EL;               // [2][BK tokens][BN]
 
   // 1-D grid: m-tile fastest, so the blocks that read the same head tile (B)
   // are consecutive logical blocks and run on one XCD together.
@@ -332,14 +322,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
 
   const int w = wave_id();
   const int wm = w >> 1, wn = w & 1;
+  const int h = lane_id() >> 5;
   f32x16 acc[2][NTW];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = zero16();
 
-  float ra[TnTile<T, BM>::PER][2][VEC];
-  float rb[TnTile<T, BN>::PER][2][VEC];
+  u32x4 ra[TnTile<T, BM>::PER], rb[TnTile<T, BN>::PER];
   const int64_t nk = (ke - kb + BK - 1) / BK;
   tn_load<T, BM>(aaddr, kb, ke, ra);
   tn_load<T, BN>(baddr, kb, ke, rb);
@@ -352,13 +342,30 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
       tn_load<T, BM>(aaddr, kb + (kt + 1) * BK, ke, ra);
       tn_load<T, BN>(baddr, kb + (kt + 1) * BK, ke, rb);
     }
-    const T* Ab = As + buf * BM * SK;
-    const T* Bb = Bs + buf * BN * SK;
+    const T* Ab = As + buf * A_EL;
+    const T* Bb = Bs + buf * B_EL;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) mma_tile_step<T, BN>(Ab, Bb, SK, ks, wm, wn, acc);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int k0 = ks * 16 + 8 * h;  // tokens 8h..8h+7 of the step
+      Frag<T> a[2], b[NTW];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int c0 = wm * 64 + mt * 32;
+        a[mt] = frag_from_col4<T>(ld_col4<LA>(Ab, k0, c0), ld_col4<LA>(Ab, k0 + 4, c0));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int c0 = wn * (BN / 2) + nt * 32;
+        b[nt] = frag_from_col4<T>(ld_col4<LB>(Bb, k0, c0), ld_col4<LB>(Bb, k0 + 4, c0));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) mma(acc[mt][nt], a[mt], b[nt]);
+    }
     if (kt + 1 < nk) {
-      tn_store<T, BM>(As + (buf ^ 1) * BM * SK, ra);
-      tn_store<T, BN>(Bs + (buf ^ 1) * BN * SK, rb);
+      tn_store<T, BM>(As + (buf ^ 1) * A_EL, ra);
+      tn_store<T, BN>(Bs + (buf ^ 1) * B_EL, rb);
     }
     lds_barrier();
   }
