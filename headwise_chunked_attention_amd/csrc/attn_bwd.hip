@@ -25,6 +25,8 @@
 // (dO^T, Q^T, K^T) are column reads with gfx950's LDS transpose reads.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -50,11 +52,13 @@ struct DkdvGeo {
   static constexpr int BQ = 32 * QT;
   static constexpr int VEC = 16 / (int)sizeof(T);
   using L = Tile<T, D>;  // every tile is [rows][D]
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + L::ELEMS(BKEY);
-  static constexpr int BUF_OFF = V_OFF + L::ELEMS(BKEY);  // two buffers of [Q | dO]
+  // the two [Q | dO] buffers first: every per-step tile address is then a
+  // per-lane register plus an immediate offset below 64 KB
+  static constexpr int BUF_OFF = 0;
   static constexpr int BUF_ELEMS = 2 * L::ELEMS(BQ);
-  static constexpr int T_ELEMS = BUF_OFF + 2 * BUF_ELEMS;
+  static constexpr int K_OFF = BUF_OFF + 2 * BUF_ELEMS;
+  static constexpr int V_OFF = K_OFF + L::ELEMS(BKEY);
+  static constexpr int T_ELEMS = V_OFF + L::ELEMS(BKEY);
   static constexpr int RCH = D / VEC;         // 16-byte chunks per row
   static constexpr int PER = BQ * RCH / NT;   // prefetch chunks per thread and tensor
   static constexpr size_t SMEM = (size_t)T_ELEMS * sizeof(T) + 2 * 2 * BQ * sizeof(float);
@@ -136,8 +140,8 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     }
     if (tid < BQ) {
       const int64_t q = q0 + tid;
-      rl = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : 0.f;
-      rd = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] : 0.f;
+      rl = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : INFINITY;
+      rd = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] * p.scale : 0.f;
     }
   };
   auto commit = [&](int b) {
@@ -159,21 +163,24 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
 
   int hh = 0;
   int64_t q0 = k0;
-  for (int64_t it = 0; it < total; ++it) {
-    const int b = (int)(it & 1);
+  // One step on LDS buffer B (a compile-time constant, so the step's LDS
+  // addresses need no per-step arithmetic).
+  auto step = [&](auto bc, int64_t it) {
+    constexpr int B = decltype(bc)::value;
     int nh_next = hh;
     int64_t q_next = q0 + BQ;
     if (q_next >= qend) {
       q_next = k0;
       ++nh_next;
     }
-    if (it + 1 < total) prefetch(nh_next, q_next, b ^ 1);
-    const T* Qs = sm + G::BUF_OFF + b * G::BUF_ELEMS;
+    if (it + 1 < total) prefetch(nh_next, q_next, B ^ 1);
+    const T* Qs = sm + G::BUF_OFF + B * G::BUF_ELEMS;
     const T* dOs = Qs + L::ELEMS(BQ);
-    const float* lse_s = stat + b * 2 * BQ;
+    const float* lse_s = stat + B * 2 * BQ;
     const float* del_s = lse_s + BQ;
-    const int qrel0 = (int)(q0 - k0) + qt * 32;                            // wave's first row - block start
-    const int qlim = (int)((p.N - q0 < (int64_t)BQ) ? (p.N - q0) : BQ);  // valid rows of the tile
+    const int qrel0 = (int)(q0 - k0) + qt * 32;  // wave's first row - block start
+    // wave-uniform: only tiles that cross the diagonal need the causal mask
+    const bool diag = qrel0 < kt * 32 + 32;
 
     // S = Q K^T and dP = dO V^T (rows q of tile qt, lane = key of tile kt)
     f32x16 sacc = zero16(), dpacc = zero16();
@@ -184,19 +191,27 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       mma(sacc, ld_frag(Qs + L::idx(qt * 32 + r, s * 16 + 8 * h)), kb);
       mma(dpacc, ld_frag(dOs + L::idx(qt * 32 + r, s * 16 + 8 * h)), vb);
     }
+    // P = exp2(S * scale*log2(e) - LSE*log2(e)); dS = P (dP scale - Delta scale),
+    // the same expression as in the dQ kernel, so both see the same bf16 dS.
+    // Rows past the end of the sequence carry LSE = +inf, so their P is 0
+    // without a mask.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = qt * 32 + 8 * i + 4 * h;  // tile row of accumulator element 4*i
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + rr);
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(del_s + rr);
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + qt * 32 + 8 * i + 4 * h);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = 4 * i + j;
-        const bool valid = (krel <= qrel0 + 8 * i + 4 * h + j) && (rr + j < qlim);
-        const float pe = valid ? fast_exp2(fmaf(sacc[e], p.scale_log2, -lv[j])) : 0.f;
-        sacc[e] = pe;
-        dpacc[e] = pe * (dpacc[e] - dv4[j]) * p.scale;
-      }
+      for (int j = 0; j < 4; ++j) sacc[4 * i + j] = fast_exp2(fmaf(sacc[4 * i + j], p.scale_log2, -lv[j]));
+    }
+    if (diag) {
+      // element e is query row qrel0 + 8(e/4) + 4h + e%4; keep keys at or before it
+      const int dk0 = krel - qrel0 - 4 * h;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = (dk0 <= 8 * (e / 4) + e % 4) ? sacc[e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(del_s + qt * 32 + 8 * i + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dpacc[4 * i + j] = sacc[4 * i + j] * fmaf(dpacc[4 * i + j], p.scale, -dv4[j]);
     }
     // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries.
 #pragma unroll
@@ -212,10 +227,14 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
         mma(dk[j], aq, sb);
       }
     }
-    if (it + 1 < total) commit(b ^ 1);
+    if (it + 1 < total) commit(B ^ 1);
     lds_barrier();
     hh = nh_next;
     q0 = q_next;
+  };
+  for (int64_t it = 0; it < total; it += 2) {
+    step(std::integral_constant<int, 0>(), it);
+    if (it + 1 < total) step(std::integral_constant<int, 1>(), it + 1);
   }
 
   // Sum the QT partial dK/dV of each key tile through LDS, then write rows of
@@ -305,8 +324,9 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
     qf[s] = ld_frag(p.q + hoff + q * D + s * 16 + 8 * h);
     df[s] = ld_frag(p.dout + hoff + q * D + s * 16 + 8 * h);
   }
-  const float lse2 = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : 0.f;
-  const float dlt = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] : 0.f;
+  // past the end of the sequence LSE = +inf makes P = 0
+  const float lse2 = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : INFINITY;
+  const float dlt = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] * p.scale : 0.f;
   f32x16 dq[ND];
 #pragma unroll
   for (int j = 0; j < ND; ++j) dq[j] = zero16();
@@ -349,9 +369,10 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
     store(smem, rk, rv);
   }
   lds_barrier();
-  for (int64_t kt_i = 0; kt_i < ntiles; ++kt_i) {
+  // one key tile on LDS stage BUF (a compile-time constant: immediate LDS offsets)
+  auto step = [&](auto bc, int64_t kt_i) {
+    constexpr int buf = decltype(bc)::value;
     const int64_t k0 = kt_i * BC;
-    const int buf = (int)(kt_i & 1);
     if (kt_i + 1 < ntiles) {
       if constexpr (DMA)
         dma(k0 + BC, smem + (buf ^ 1) * G::STAGE);
@@ -374,15 +395,23 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
           mma(sacc[kt], ld_frag(Ks + L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[s]);
           mma(dpacc[kt], ld_frag(Vs + L::idx(kt * 32 + r, s * 16 + 8 * h)), df[s]);
         }
-      const int qrel = (int)(q - k0);
+      // P = exp2(S * scale*log2(e) - LSE*log2(e)); dS = P (dP scale - Delta scale)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const bool valid = kt * 32 + 8 * (e >> 2) + 4 * h + (e & 3) <= qrel;
-          const float pe = valid ? fast_exp2(fmaf(sacc[kt][e], p.scale_log2, -lse2)) : 0.f;
-          dpacc[kt][e] = pe * (dpacc[kt][e] - dlt) * p.scale;
-        }
+        for (int e = 0; e < 16; ++e) sacc[kt][e] = fast_exp2(fmaf(sacc[kt][e], p.scale_log2, -lse2));
+      if (k0 + BC - 1 > q0w) {  // wave-uniform: the tile crosses this wave's diagonal
+        // element e of key tile kt is key kt*32 + 8(e/4) + 4h + e%4 of the tile
+        const int qrel = (int)(q - k0) - 4 * h;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[kt][e] = (kt * 32 + 8 * (e >> 2) + (e & 3) <= qrel) ? sacc[kt][e] : 0.f;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dpacc[kt][e] = sacc[kt][e] * fmaf(dpacc[kt][e], p.scale, -dlt);
       // dQ^T += K^T dS^T (contraction over the tile's keys = accumulator rows)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -404,6 +433,10 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
         store(smem + (buf ^ 1) * G::STAGE, rk, rv);
     }
     lds_barrier();
+  };
+  for (int64_t kt_i = 0; kt_i < ntiles; kt_i += 2) {
+    step(std::integral_constant<int, 0>(), kt_i);
+    if (kt_i + 1 < ntiles) step(std::integral_constant<int, 1>(), kt_i + 1);
   }
   // dQ rows of this lane's query: C tiles hold rows = head dim.
   float* dst = p.dq + hoff + q * D;
