@@ -20,6 +20,8 @@
 //   Delta_i = dO_i . O_i, the row term of the softmax backward.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -141,9 +143,16 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
   }
   lds_barrier();
 
-  for (int64_t kt_i = 0; kt_i < ntiles; ++kt_i) {
+  // bf16: P is packed straight into MFMA operands and its row sum taken with
+  // dot2 on the packed pairs (the sum of exactly the values that multiply V).
+  // The softmax base moves only when a lane's row sum leaves [0, 2^16] (or is
+  // not finite, as on the first tile where the base is -inf): then the row
+  // max of the tile becomes the base and O, l are rescaled. Every P stays
+  // <= 2^16, and O / l and LSE = base + log2(l) do not depend on the base.
+  constexpr float P_LIMIT = 65536.f;
+  auto step = [&](auto bc, int64_t kt_i) {
+    constexpr int buf = decltype(bc)::value;  // LDS stage (immediate offsets)
     const int64_t k0 = kt_i * BC;
-    const int buf = (int)(kt_i & 1);
     if (kt_i + 1 < ntiles) {
       if constexpr (DMA)
         dma_kv<T, D>(p, k0 + BC, smem + (buf ^ 1) * G::STAGE);
@@ -168,8 +177,7 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
           for (int t = 0; t < NQT; ++t) mma(sacc[kt][t], a, qf[t][s]);
         }
       }
-      const bool diag = (k0 + BC - 1 > q0w);
-      if (diag) {
+      if (k0 + BC - 1 > q0w) {  // the tile crosses this wave's diagonal
 #pragma unroll
         for (int t = 0; t < NQT; ++t) {
           const int qrel = (int)(q0w - k0) + t * 32 + r;  // query minus tile start
@@ -180,57 +188,98 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
               if (kt * 32 + 8 * (e >> 2) + 4 * h + (e & 3) > qrel) sacc[kt][t][e] = -INFINITY;
         }
       }
+      Frag<T> pf[2][2][NQT];  // P^T as B operands [key half][16-key step][query tile]
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
-        if constexpr (MODE == 0) {
-          // Online softmax with a lazily moved base: the running base m_run
-          // (log2 units) is raised only when a score exceeds it by more than
-          // 2^8, so exp2(s - m_run) <= 256 and the O/l rescale is skipped on
-          // most tiles. The final O / l and LSE = m_run + log2(l) are exact
-          // whatever base was used.
-          float mx = -INFINITY;
+        if constexpr (sizeof(T) == 2) {
+          // P = exp2(S scale log2(e) - base), packed; returns the lane's row sum (mode 0)
+          auto make_p = [&](float base) {
+            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+            float ps[2] = {0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                  const float x0 = fast_exp2(fmaf(sacc[kt][t][8 * s2 + e], p.scale_log2, -base));
+                  const float x1 = fast_exp2(fmaf(sacc[kt][t][8 * s2 + e + 1], p.scale_log2, -base));
+                  const bf16x2 pr = {(bf16)x0, (bf16)x1};
+                  pf[kt][s2][t].v[e] = pr[0];
+                  pf[kt][s2][t].v[e + 1] = pr[1];
+                  if constexpr (MODE == 0) ps[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[(e >> 1) & 1], false);
+                }
+            return ps[0] + ps[1];
+          };
+          if constexpr (MODE == 0) {
+            float psum = make_p(m_run[t]);
+            if (__builtin_amdgcn_ballot_w64(!(psum <= P_LIMIT))) {
+              float mx = -INFINITY;
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][t][e]);
+              // key 0 is visible to every query, so after the first tile m_new is finite
+              const float m_new = fmaxf(m_run[t], wave_max_pair(mx) * p.scale_log2);
+              const float alpha = fast_exp2(m_run[t] - m_new);
+              m_run[t] = m_new;
+              l_run[t] *= alpha;
+#pragma unroll
+              for (int j = 0; j < ND; ++j) oacc[t][j] *= alpha;
+              psum = make_p(m_run[t]);
+            }
+            l_run[t] += psum;
+          } else {
+            make_p(base_row[t]);
+          }
+        } else {
+          if constexpr (MODE == 0) {
+            // fp32: lazily moved base, raised when a score exceeds it by more than 2^8
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][t][e]);
+            mx = wave_max_pair(mx) * p.scale_log2;
+            const bool need = mx > m_run[t] + 8.0f;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+              const float m_new = need ? mx : m_run[t];
+              const float alpha = fast_exp2(m_run[t] - m_new);
+              m_run[t] = m_new;
+              l_run[t] *= alpha;
+#pragma unroll
+              for (int j = 0; j < ND; ++j) oacc[t][j] *= alpha;
+            }
+            base_row[t] = m_run[t];
+          }
+          float psum = 0.f;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][t][e]);
-          mx = wave_max_pair(mx) * p.scale_log2;
-          const bool need = mx > m_run[t] + 8.0f;
-          if (__builtin_amdgcn_ballot_w64(need)) {
-            const float m_new = need ? mx : m_run[t];
-            const float alpha = fast_exp2(m_run[t] - m_new);
-            m_run[t] = m_new;
-            l_run[t] *= alpha;
+            for (int e = 0; e < 16; ++e) {
+              const float pe = fast_exp2(fmaf(sacc[kt][t][e], p.scale_log2, -base_row[t]));
+              sacc[kt][t][e] = pe;
+              psum += pe;
+            }
+          l_run[t] += psum;
 #pragma unroll
-            for (int j = 0; j < ND; ++j) oacc[t][j] *= alpha;
-          }
-          base_row[t] = m_run[t];
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) pf[kt][s2][t] = frag_from_acc<T>(sacc[kt][t], s2, 1.0f);
         }
-        float psum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float pe = fast_exp2(fmaf(sacc[kt][t][e], p.scale_log2, -base_row[t]));
-            sacc[kt][t][e] = pe;
-            psum += pe;
-          }
-        l_run[t] += psum;
       }
       // O^T += V^T P^T
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          Frag<T> pf[NQT];
-#pragma unroll
-          for (int t = 0; t < NQT; ++t) pf[t] = frag_from_acc<T>(sacc[kt][t], s2, 1.0f);
           const int row0 = kt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
           for (int j = 0; j < ND; ++j) {
             const Frag<T> a = frag_from_col4<T>(ld_col4<typename G::L>(Vs, row0, j * 32),
                                                 ld_col4<typename G::L>(Vs, row0 + 8, j * 32));
 #pragma unroll
-            for (int t = 0; t < NQT; ++t) mma(oacc[t][j], a, pf[t]);
+            for (int t = 0; t < NQT; ++t) mma(oacc[t][j], a, pf[kt][s2][t]);
           }
         }
     }
@@ -241,6 +290,10 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
         store_kv<T, D>(smem + (buf ^ 1) * G::STAGE, rk, rv);
     }
     lds_barrier();
+  };
+  for (int64_t kt_i = 0; kt_i < ntiles; kt_i += 2) {
+    step(std::integral_constant<int, 0>(), kt_i);
+    if (kt_i + 1 < ntiles) step(std::integral_constant<int, 1>(), kt_i + 1);
   }
 
   // epilogue
