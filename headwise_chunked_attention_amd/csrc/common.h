@@ -254,6 +254,28 @@ DEV void lds_barrier() {
 // filling physical chunk l % CPR of row r0 + l / CPR, so it fetches logical
 // chunk (l % CPR) ^ swz(row). No registers hold the data and the LDS writes
 // happen asynchronously; completion is tracked by vmcnt.
+//
+// The instruction is issued from inline assembly on purpose. Issued through
+// the compiler builtin, every later LDS transpose read gets a conservative
+// vmcnt(0) wait in front of it (the compiler cannot tell that the read does
+// not touch the bytes in flight), which stalls each step until the next tile
+// has arrived. Callers load only into LDS stages that no wave reads in the
+// meantime and wait for vmcnt(0) before the barrier that publishes the stage.
+// M0 (the LDS base of the instruction) is saved and restored around it; the
+// s_nop is the wait state required between an M0 write and an LDS DMA.
+DEV void lds_dma16(const void* gptr, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds_addr)
+      : "memory");
+}
+
 template <class L, typename T>
 DEV void dma_tile_rows(const T* src, int64_t src_ld, T* lds_tile, int row0) {
   static_assert(L::SWZ, "direct loads need the unpadded swizzled layout");
@@ -262,8 +284,8 @@ DEV void dma_tile_rows(const T* src, int64_t src_ld, T* lds_tile, int row0) {
   const int row = row0 + l / CPR;
   const int chunk = (l % CPR) ^ L::swz(row);
   const T* g = src + (int64_t)row * src_ld + chunk * L::E;
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
-                                   (__attribute__((address_space(3))) void*)(lds_tile + row0 * L::STRIDE), 16, 0, 0);
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)(lds_tile + row0 * L::STRIDE);
+  lds_dma16(g, __builtin_amdgcn_readfirstlane(lds));
 }
 
 // Wait for this wave's outstanding vector-memory operations (direct LDS loads included).

@@ -137,6 +137,21 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = zero16();
 
+  const int tid = threadIdx.x;
+  // EPI_ACCUM: the old values of the output tile are fetched before the
+  // k loop (K is short here, so their latency would otherwise be exposed)
+  constexpr int CH = EPI == EPI_ACCUM ? BM * BN / VEC / NTHREADS : 1;
+  u32x4 old[CH];
+  if constexpr (EPI == EPI_ACCUM) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + i * NTHREADS;
+      const int row = c / (BN / VEC), cv = c % (BN / VEC);
+      const int64_t m = m0 + row;
+      old[i] = (p.accumulate && m < p.M) ? ld_raw16(p.c + m * p.ldc + n0 + cv * VEC) : zero_raw16();
+    }
+  }
+
   u32x4 ra[BM * 8 / NTHREADS], rb[BN * 8 / NTHREADS];
   const int64_t nk = p.K / BK;
   nt_load_tile<T, BN>(p, bptr, ldb, m0, nrow0, 0, ra, rb);
@@ -157,19 +172,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   float* Cs = reinterpret_cast<float*>(smem);
   acc_to_lds<BN>(Cs, wm, wn, acc);
   lds_barrier();
-  const int tid = threadIdx.x;
 
   if constexpr (EPI == EPI_ACCUM) {
-    // all loads of the old values first, then add and store (memory-level parallelism)
-    constexpr int CH = BM * BN / VEC / NTHREADS;
-    u32x4 old[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + i * NTHREADS;
-      const int row = c / (BN / VEC), cv = c % (BN / VEC);
-      const int64_t m = m0 + row;
-      old[i] = (p.accumulate && m < p.M) ? ld_raw16(p.c + m * p.ldc + n0 + cv * VEC) : zero_raw16();
-    }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + i * NTHREADS;
