@@ -140,8 +140,9 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     }
     if (tid < BQ) {
       const int64_t q = q0 + tid;
-      rl = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : INFINITY;
-      rd = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] * p.scale : 0.f;
+      // negated: they start the S and dP accumulators
+      rl = (q < p.N) ? -p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : -INFINITY;
+      rd = (q < p.N) ? -p.delta[(int64_t)hh * p.Np + q] : 0.f;
     }
   };
   auto commit = [&](int b) {
@@ -182,8 +183,22 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     // wave-uniform: only tiles that cross the diagonal need the causal mask
     const bool diag = qrel0 < kt * 32 + 32;
 
-    // S = Q K^T and dP = dO V^T (rows q of tile qt, lane = key of tile kt)
-    f32x16 sacc = zero16(), dpacc = zero16();
+    // S - LSE and dP - Delta (log2 units and 1/sqrt(d) scale come with the
+    // pre-scaled q and dout): the accumulators start at -LSE and -Delta of
+    // their query rows (element 4i+j is row 8i + 4h + j of the wave's 32),
+    // so the MFMAs do the subtraction. Rows past the end of the sequence
+    // carry LSE = +inf, so their P is 0 without a mask.
+    f32x16 sacc, dpacc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + qt * 32 + 8 * i + 4 * h);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(del_s + qt * 32 + 8 * i + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sacc[4 * i + j] = lv[j];
+        dpacc[4 * i + j] = dv4[j];
+      }
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const Frag<T> kb = ld_frag(Ks + L::idx(krel, s * 16 + 8 * h));
@@ -191,16 +206,10 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       mma(sacc, ld_frag(Qs + L::idx(qt * 32 + r, s * 16 + 8 * h)), kb);
       mma(dpacc, ld_frag(dOs + L::idx(qt * 32 + r, s * 16 + 8 * h)), vb);
     }
-    // P = exp2(S * scale*log2(e) - LSE*log2(e)); dS = P (dP scale - Delta scale),
-    // the same expression as in the dQ kernel, so both see the same bf16 dS.
-    // Rows past the end of the sequence carry LSE = +inf, so their P is 0
-    // without a mask.
+    // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d), the same values the dQ
+    // kernel forms
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + qt * 32 + 8 * i + 4 * h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sacc[4 * i + j] = fast_exp2(fmaf(sacc[4 * i + j], p.scale_log2, -lv[j]));
-    }
+    for (int e = 0; e < 16; ++e) sacc[e] = fast_exp2(sacc[e]);
     if (diag) {
       // element e is query row qrel0 + 8(e/4) + 4h + e%4; keep keys at or before it
       const int dk0 = krel - qrel0 - 4 * h;
@@ -208,11 +217,7 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       for (int e = 0; e < 16; ++e) sacc[e] = (dk0 <= 8 * (e / 4) + e % 4) ? sacc[e] : 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(del_s + qt * 32 + 8 * i + 4 * h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dpacc[4 * i + j] = sacc[4 * i + j] * fmaf(dpacc[4 * i + j], p.scale, -dv4[j]);
-    }
+    for (int e = 0; e < 16; ++e) dpacc[e] = sacc[e] * dpacc[e];
     // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries.
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -267,8 +272,8 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dd = j * 32 + 8 * i + 4 * h;
-        f32x4 vk = (f32x4){dk[j][4 * i], dk[j][4 * i + 1], dk[j][4 * i + 2], dk[j][4 * i + 3]};
-        f32x4 vv = (f32x4){dv[j][4 * i], dv[j][4 * i + 1], dv[j][4 * i + 2], dv[j][4 * i + 3]};
+        f32x4 vk = (f32x4){dk[j][4 * i], dk[j][4 * i + 1], dk[j][4 * i + 2], dk[j][4 * i + 3]} * p.dk_mul;
+        f32x4 vv = (f32x4){dv[j][4 * i], dv[j][4 * i + 1], dv[j][4 * i + 2], dv[j][4 * i + 3]} * p.dv_mul;
         f32x4* pk = reinterpret_cast<f32x4*>(p.dk_acc + kw * D + dd);
         f32x4* pv = reinterpret_cast<f32x4*>(p.dv_acc + kw * D + dd);
         if (p.accumulate) {
@@ -326,7 +331,7 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
   }
   // past the end of the sequence LSE = +inf makes P = 0
   const float lse2 = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : INFINITY;
-  const float dlt = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] * p.scale : 0.f;
+  const float dlt = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] : 0.f;
   f32x16 dq[ND];
 #pragma unroll
   for (int j = 0; j < ND; ++j) dq[j] = zero16();
@@ -395,11 +400,12 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
           mma(sacc[kt], ld_frag(Ks + L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[s]);
           mma(dpacc[kt], ld_frag(Vs + L::idx(kt * 32 + r, s * 16 + 8 * h)), df[s]);
         }
-      // P = exp2(S * scale*log2(e) - LSE*log2(e)); dS = P (dP scale - Delta scale)
+      // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d) (log2 units and the
+      // 1/sqrt(d) come with the pre-scaled q and dout)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kt][e] = fast_exp2(fmaf(sacc[kt][e], p.scale_log2, -lse2));
+        for (int e = 0; e < 16; ++e) sacc[kt][e] = fast_exp2(sacc[kt][e] - lse2);
       if (k0 + BC - 1 > q0w) {  // wave-uniform: the tile crosses this wave's diagonal
         // element e of key tile kt is key kt*32 + 8(e/4) + 4h + e%4 of the tile
         const int qrel = (int)(q - k0) - 4 * h;
@@ -411,7 +417,7 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dpacc[kt][e] = sacc[kt][e] * fmaf(dpacc[kt][e], p.scale, -dlt);
+        for (int e = 0; e < 16; ++e) dpacc[kt][e] = sacc[kt][e] * (dpacc[kt][e] - dlt);
       // dQ^T += K^T dS^T (contraction over the tile's keys = accumulator rows)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)

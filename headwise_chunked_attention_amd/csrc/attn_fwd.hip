@@ -192,7 +192,7 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
 #pragma unroll
       for (int t = 0; t < NQT; ++t) {
         if constexpr (sizeof(T) == 2) {
-          // P = exp2(S scale log2(e) - base), packed; returns the lane's row sum (mode 0)
+          // P = exp2(S - base) (S is in log2 units), packed; returns the lane's row sum (mode 0)
           auto make_p = [&](float base) {
             const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
             float ps[2] = {0.f, 0.f};
@@ -202,8 +202,8 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
               for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                  const float x0 = fast_exp2(fmaf(sacc[kt][t][8 * s2 + e], p.scale_log2, -base));
-                  const float x1 = fast_exp2(fmaf(sacc[kt][t][8 * s2 + e + 1], p.scale_log2, -base));
+                  const float x0 = fast_exp2(sacc[kt][t][8 * s2 + e] - base);
+                  const float x1 = fast_exp2(sacc[kt][t][8 * s2 + e + 1] - base);
                   const bf16x2 pr = {(bf16)x0, (bf16)x1};
                   pf[kt][s2][t].v[e] = pr[0];
                   pf[kt][s2][t].v[e + 1] = pr[1];
@@ -220,7 +220,7 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
 #pragma unroll
                 for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][t][e]);
               // key 0 is visible to every query, so after the first tile m_new is finite
-              const float m_new = fmaxf(m_run[t], wave_max_pair(mx) * p.scale_log2);
+              const float m_new = fmaxf(m_run[t], wave_max_pair(mx));
               const float alpha = fast_exp2(m_run[t] - m_new);
               m_run[t] = m_new;
               l_run[t] *= alpha;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
               for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][t][e]);
-            mx = wave_max_pair(mx) * p.scale_log2;
+            mx = wave_max_pair(mx);
             const bool need = mx > m_run[t] + 8.0f;
             if (__builtin_amdgcn_ballot_w64(need)) {
               const float m_new = need ? mx : m_run[t];
@@ -257,7 +257,7 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-              const float pe = fast_exp2(fmaf(sacc[kt][t][e], p.scale_log2, -base_row[t]));
+              const float pe = fast_exp2(sacc[kt][t][e] - base_row[t]);
               sacc[kt][t][e] = pe;
               psum += pe;
             }

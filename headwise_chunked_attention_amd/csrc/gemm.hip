@@ -236,7 +236,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
         const int row = c / (BN / VEC), cv = c % (BN / VEC);
         float v[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e] * ho.scale;
         st16_f<T>(dst + row * BN + cv * VEC, v);
       }
     }

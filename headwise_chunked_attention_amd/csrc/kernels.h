@@ -19,6 +19,7 @@ struct HeadOut {
   T* pre;          // [heads][Np][d] values before norm/RoPE, or null
   const T* gamma;  // [d] RMSNorm weight (norm applied iff non-null)
   int rope;        // rotate (i, i + d/2) pairs by pos * theta^(-2i/d)
+  float scale;     // multiplies the values stored to rm (after norm and RoPE)
 };
 
 // C[m][n] = sum_k A(m,k) B(n,k), both operands contiguous along k.
@@ -69,6 +70,10 @@ struct GemmTN {
 // mode 0: online softmax, writes o (normalised) and lse.
 // mode 1: reads lse, writes o and delta[h][i] = sum_d dO[h][i][d] * O[h][i][d].
 template <typename T>
+// The attention kernels take q pre-multiplied by log2(e)/sqrt(D) (so Q K^T
+// is the softmax exponent in log2 units) and, in the backward, dout
+// pre-multiplied by 1/sqrt(D) (so dO V^T is dP/sqrt(D)); the projection
+// epilogue stores them that way. delta is then rowsum(dout o O) of that dout.
 struct AttnFwd {
   const T* q;
   const T* k;
@@ -80,7 +85,6 @@ struct AttnFwd {
   float* delta;   // mode 1, [nh][Np]
   int64_t N, Np;
   int nh;
-  float scale_log2;  // log2(e) / sqrt(D)
 };
 
 // Causal GQA attention backward over one kv head and `nh` q heads.
@@ -103,8 +107,8 @@ struct AttnBwd {
   int64_t N, Np;
   int nh;
   int accumulate;
-  float scale_log2;  // log2(e) / sqrt(D)
-  float scale;       // 1 / sqrt(D)
+  float dk_mul;  // sqrt(D) ln 2: dK from the pre-scaled q (see below)
+  float dv_mul;  // sqrt(D): dV from the pre-scaled dout
 };
 
 // Per-row gradient finish for heads stored [nh][Np][D]:

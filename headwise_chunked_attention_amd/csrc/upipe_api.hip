@@ -252,6 +252,7 @@ int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   const double l2t = log2(theta);
   const int64_t head = s.Np * s.d;
   const int nh = s.C < s.G ? s.C : s.G;  // q heads of the chunk per kv head
+  const float q_scale = (float)(1.4426950408889634 / sqrt((double)s.d));
   for (int c0 = 0; c0 < s.Hq; c0 += s.C) {
     const int g0 = c0 / s.G;
     const bool new_kv = (c0 % s.G) == 0;
@@ -262,10 +263,13 @@ int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
     ho[0].rm = Q;
     ho[0].gamma = qn;
     ho[0].rope = 1;
+    ho[0].scale = q_scale;  // Q K^T is then the softmax exponent in log2 units
     ho[1].rm = K;
     ho[1].gamma = kn;
     ho[1].rope = 1;
+    ho[1].scale = 1.f;
     ho[2].rm = V;
+    ho[2].scale = 1.f;
     int rc = run_projection<T>(s, x, new_kv ? 3 : 1, w, nheads, ho, eps, l2t, st);
     if (rc) return rc;
     for (int j = 0; j < s.kvC; ++j) {
@@ -280,7 +284,6 @@ int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       a.N = s.N;
       a.Np = s.Np;
       a.nh = nh;
-      a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.d));
       HIP_TRY(timed(UPIPE_KERNEL_ATTN_FWD, 4.0 * s.d * nh * causal_pairs(s.N), st,
                     [&] { return launch_attn_fwd<T>(a, s.d, 0, st); }));
     }
@@ -314,8 +317,12 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   const int64_t head = s.Np * s.d;
   const int64_t Cd = (int64_t)s.C * s.d, kvd = (int64_t)s.kvC * s.d;
   const int nh = s.C < s.G ? s.C : s.G;
-  const float scale = (float)(1.0 / sqrt((double)s.d));
-  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)s.d));
+  // q is stored times log2(e)/sqrt(d) and dO times 1/sqrt(d) (see kernels.h);
+  // the dK/dV kernel undoes those factors on its results
+  const float q_scale = (float)(1.4426950408889634 / sqrt((double)s.d));
+  const float do_scale = (float)(1.0 / sqrt((double)s.d));
+  const float dk_mul = (float)(sqrt((double)s.d) * 0.6931471805599453);
+  const float dv_mul = (float)sqrt((double)s.d);
 
   HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dwq, (int64_t)s.Hq * s.d * s.D, 0.f, st); }));
   HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dwk, (int64_t)s.Hkv * s.d * s.D, 0.f, st); }));
@@ -347,11 +354,14 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       ho[0].pre = Uq;
       ho[0].gamma = qn;
       ho[0].rope = 1;
+      ho[0].scale = q_scale;
       ho[1].rm = K;
       ho[1].pre = Uk;
       ho[1].gamma = kn;
       ho[1].rope = 1;
+      ho[1].scale = 1.f;
       ho[2].rm = V;
+      ho[2].scale = 1.f;
       int rc = run_projection<T>(s, x, new_kv ? 3 : 1, w, nheads, ho, eps, l2t, st);
       if (rc) return rc;
     }
@@ -362,6 +372,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       HeadOut<T> ho[1];
       memset(ho, 0, sizeof(ho));
       ho[0].rm = dO;
+      ho[0].scale = do_scale;
       int rc = run_projection<T>(s, dy, 1, w, nheads, ho, eps, l2t, st);
       if (rc) return rc;
     }
@@ -380,7 +391,6 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       a.N = s.N;
       a.Np = s.Np;
       a.nh = nh;
-      a.scale_log2 = scale_log2;
       HIP_TRY(timed(UPIPE_KERNEL_ATTN_RECOMPUTE, 4.0 * s.d * nh * causal_pairs(s.N), st,
                     [&] { return launch_attn_fwd<T>(a, s.d, 1, st); }));
     }
@@ -405,8 +415,8 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       b.Np = s.Np;
       b.nh = nh;
       b.accumulate = new_kv ? 0 : 1;
-      b.scale_log2 = scale_log2;
-      b.scale = scale;
+      b.dk_mul = dk_mul;
+      b.dv_mul = dv_mul;
       HIP_TRY(timed(UPIPE_KERNEL_ATTN_BWD_DKDV, 8.0 * s.d * nh * causal_pairs(s.N), st,
                     [&] { return launch_attn_bwd_dkdv<T>(b, s.d, st); }));
       HIP_TRY(timed(UPIPE_KERNEL_ATTN_BWD_DQ, 6.0 * s.d * nh * causal_pairs(s.N), st,
