@@ -332,6 +332,12 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
   // past the end of the sequence LSE = +inf makes P = 0
   const float lse2 = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : INFINITY;
   const float dlt = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] : 0.f;
+  f32x16 init_s, init_dp;  // accumulator starts: -LSE and -Delta of this lane's query
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    init_s[e] = -lse2;
+    init_dp[e] = -dlt;
+  }
   f32x16 dq[ND];
 #pragma unroll
   for (int j = 0; j < ND; ++j) dq[j] = zero16();
@@ -387,43 +393,34 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
     const T* Ks = smem + buf * G::STAGE;
     const T* Vs = Ks + L::ELEMS(BC);
     if (k0 <= q0w + 31) {  // some key of the tile is visible to this wave
-      f32x16 sacc[2], dpacc[2];
+      // The two 32-key halves one after the other. S^T - LSE and dP^T - Delta:
+      // every accumulator chain starts from the loop-invariant splat of -LSE
+      // (or -Delta) of this lane's query, so the MFMAs do the subtraction.
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = zero16();
-        dpacc[kt] = zero16();
-      }
+        f32x16 sacc = mma_first(ld_frag(Ks + L::idx(kt * 32 + r, 8 * h)), qf[0], init_s);
+        f32x16 dpacc = mma_first(ld_frag(Vs + L::idx(kt * 32 + r, 8 * h)), df[0], init_dp);
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          mma(sacc[kt], ld_frag(Ks + L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[s]);
-          mma(dpacc[kt], ld_frag(Vs + L::idx(kt * 32 + r, s * 16 + 8 * h)), df[s]);
+        for (int s = 1; s < NS; ++s) {
+          mma(sacc, ld_frag(Ks + L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[s]);
+          mma(dpacc, ld_frag(Vs + L::idx(kt * 32 + r, s * 16 + 8 * h)), df[s]);
         }
-      // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d) (log2 units and the
-      // 1/sqrt(d) come with the pre-scaled q and dout)
+        // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d) (log2 units and the
+        // 1/sqrt(d) come with the pre-scaled q and dout)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int e = 0; e < 16; ++e) sacc[e] = fast_exp2(sacc[e]);
+        if (k0 + kt * 32 + 31 > q0w) {  // wave-uniform: the half crosses this wave's diagonal
+          // element e is key kt*32 + 8(e/4) + 4h + e%4 of the tile
+          const int qrel = (int)(q - k0) - 4 * h - kt * 32;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kt][e] = fast_exp2(sacc[kt][e] - lse2);
-      if (k0 + BC - 1 > q0w) {  // wave-uniform: the tile crosses this wave's diagonal
-        // element e of key tile kt is key kt*32 + 8(e/4) + 4h + e%4 of the tile
-        const int qrel = (int)(q - k0) - 4 * h;
+          for (int e = 0; e < 16; ++e) sacc[e] = (8 * (e >> 2) + (e & 3) <= qrel) ? sacc[e] : 0.f;
+        }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) sacc[kt][e] = (kt * 32 + 8 * (e >> 2) + (e & 3) <= qrel) ? sacc[kt][e] : 0.f;
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) dpacc[kt][e] = sacc[kt][e] * (dpacc[kt][e] - dlt);
-      // dQ^T += K^T dS^T (contraction over the tile's keys = accumulator rows)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int e = 0; e < 16; ++e) dpacc[e] = sacc[e] * dpacc[e];
+        // dQ^T += K^T dS^T (contraction over the half's keys = accumulator rows)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const Frag<T> sb = frag_from_acc<T>(dpacc[kt], s2, 1.0f);
+          const Frag<T> sb = frag_from_acc<T>(dpacc, s2, 1.0f);
           const int row0 = kt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
           for (int j = 0; j < ND; ++j) {
@@ -431,6 +428,7 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
             mma(dq[j], a, sb);
           }
         }
+      }
     }
     if (kt_i + 1 < ntiles) {
       if constexpr (DMA)

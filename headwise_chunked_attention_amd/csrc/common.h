@@ -86,6 +86,20 @@ template <> DEV Frag<float> frag_from_acc<float>(const f32x16& c, int s, float m
   return f;
 }
 
+// A * B + c0 over one 16-wide k step, into a new accumulator (c0 is kept).
+template <typename T> DEV f32x16 mma_first(const Frag<T>& a, const Frag<T>& b, const f32x16& c0);
+template <> DEV f32x16 mma_first<bf16>(const Frag<bf16>& a, const Frag<bf16>& b, const f32x16& c0) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c0, 0, 0, 0);
+}
+template <> DEV f32x16 mma_first<float>(const Frag<float>& a, const Frag<float>& b, const f32x16& c0) {
+  f32x16 c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[0], b.lo[0], c0, 0, 0, 0);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[i], b.lo[i], c, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[i], b.hi[i], c, 0, 0, 0);
+  return c;
+}
+
 // c += A * B over one 16-wide k step.
 template <typename T> DEV void mma(f32x16& c, const Frag<T>& a, const Frag<T>& b);
 template <> DEV void mma<bf16>(f32x16& c, const Frag<bf16>& a, const Frag<bf16>& b) {
