@@ -150,6 +150,14 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
   // max of the tile becomes the base and O, l are rescaled. Every P stays
   // <= 2^16, and O / l and LSE = base + log2(l) do not depend on the base.
   constexpr float P_LIMIT = 65536.f;
+  // bf16: every S^T chain starts from init = splat(-base), base = the LSE in
+  // the recompute, the running softmax base in the forward
+  float base = 0.f;
+  bool have_base = MODE == 1;
+  f32x16 init;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) init[e] = (MODE == 1) ? -base_row[0] : 0.f;
+  if constexpr (MODE == 1) base = base_row[0];
   auto step = [&](auto bc, int64_t kt_i) {
     constexpr int buf = decltype(bc)::value;  // LDS stage (immediate offsets)
     const int64_t k0 = kt_i * BC;
@@ -162,77 +170,123 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
     const T* Ks = smem + buf * G::STAGE;
     const T* Vs = Ks + G::K_ELEMS;
 
-    if (k0 <= q0w + G::ROWS_W - 1) {  // some key of the tile is visible to this wave
-      f32x16 sacc[2][NQT];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int t = 0; t < NQT; ++t) sacc[kt][t] = zero16();
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
+    if constexpr (sizeof(T) == 2) {
+      if (k0 <= q0w + G::ROWS_W - 1) {  // some key of the tile is visible to this wave
+        // The two 32-key halves in turn. Each S^T chain starts from the splat
+        // of -base, so the accumulator holds S - base (log2 units).
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const Frag<T> a = ld_frag(Ks + G::L::idx(kt * 32 + r, s * 16 + 8 * h));
+          f32x16 sacc = mma_first(ld_frag(Ks + G::L::idx(kt * 32 + r, 8 * h)), qf[0][0], init);
 #pragma unroll
-          for (int t = 0; t < NQT; ++t) mma(sacc[kt][t], a, qf[t][s]);
-        }
-      }
-      if (k0 + BC - 1 > q0w) {  // the tile crosses this wave's diagonal
-#pragma unroll
-        for (int t = 0; t < NQT; ++t) {
-          const int qrel = (int)(q0w - k0) + t * 32 + r;  // query minus tile start
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+          for (int s = 1; s < NS; ++s) mma(sacc, ld_frag(Ks + G::L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[0][s]);
+          if (k0 + kt * 32 + 31 > q0w) {  // the half crosses this wave's diagonal
+            const int qrel = (int)(q0w - k0) + r - kt * 32;  // query minus the half's first key
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-              if (kt * 32 + 8 * (e >> 2) + 4 * h + (e & 3) > qrel) sacc[kt][t][e] = -INFINITY;
-        }
-      }
-      Frag<T> pf[2][2][NQT];  // P^T as B operands [key half][16-key step][query tile]
-#pragma unroll
-      for (int t = 0; t < NQT; ++t) {
-        if constexpr (sizeof(T) == 2) {
-          // P = exp2(S - base) (S is in log2 units), packed; returns the lane's row sum (mode 0)
-          auto make_p = [&](float base) {
+              if (8 * (e >> 2) + 4 * h + (e & 3) > qrel) sacc[e] = -INFINITY;
+          }
+          // P = exp2(S - base) packed as MFMA operands; returns the lane's row sum
+          Frag<T> pf[2];
+          auto make_p = [&](float shift) {
             const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
             float ps[2] = {0.f, 0.f};
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-              for (int s2 = 0; s2 < 2; ++s2)
+              for (int e = 0; e < 8; e += 2) {
+                const float x0 = fast_exp2(sacc[8 * s2 + e] - shift);
+                const float x1 = fast_exp2(sacc[8 * s2 + e + 1] - shift);
+                const bf16x2 pr = {(bf16)x0, (bf16)x1};
+                pf[s2].v[e] = pr[0];
+                pf[s2].v[e + 1] = pr[1];
+                if constexpr (MODE == 0) ps[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[(e >> 1) & 1], false);
+              }
+            return ps[0] + ps[1];
+          };
+          auto make_p0 = [&]() {  // shift 0: no subtraction
+            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+            float ps[2] = {0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                  const float x0 = fast_exp2(sacc[kt][t][8 * s2 + e] - base);
-                  const float x1 = fast_exp2(sacc[kt][t][8 * s2 + e + 1] - base);
-                  const bf16x2 pr = {(bf16)x0, (bf16)x1};
-                  pf[kt][s2][t].v[e] = pr[0];
-                  pf[kt][s2][t].v[e + 1] = pr[1];
-                  if constexpr (MODE == 0) ps[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[(e >> 1) & 1], false);
-                }
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+              for (int e = 0; e < 8; e += 2) {
+                const bf16x2 pr = {(bf16)fast_exp2(sacc[8 * s2 + e]), (bf16)fast_exp2(sacc[8 * s2 + e + 1])};
+                pf[s2].v[e] = pr[0];
+                pf[s2].v[e + 1] = pr[1];
+                if constexpr (MODE == 0) ps[(e >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[(e >> 1) & 1], false);
+              }
             return ps[0] + ps[1];
           };
           if constexpr (MODE == 0) {
-            float psum = make_p(m_run[t]);
-            if (__builtin_amdgcn_ballot_w64(!(psum <= P_LIMIT))) {
+            // The base moves only when a lane's row sum leaves [0, 2^16] (or is not
+            // finite), and on the first half: then the row max becomes the base and
+            // O and l are rescaled. Every P stays <= 2^16; O / l and
+            // LSE = base + log2(l) do not depend on the base.
+            float psum = have_base ? make_p0() : 0.f;
+            if (!have_base || __builtin_amdgcn_ballot_w64(!(psum <= P_LIMIT))) {
               float mx = -INFINITY;
 #pragma unroll
-              for (int kt = 0; kt < 2; ++kt)
+              for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+              // the first half holds key 0, visible to every query: m_new is finite
+              const float m_new = fmaxf(m_run[0], wave_max_pair(mx) + base);
+              const float alpha = fast_exp2(m_run[0] - m_new);
+              l_run[0] *= alpha;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][t][e]);
-              // key 0 is visible to every query, so after the first tile m_new is finite
-              const float m_new = fmaxf(m_run[t], wave_max_pair(mx));
-              const float alpha = fast_exp2(m_run[t] - m_new);
-              m_run[t] = m_new;
-              l_run[t] *= alpha;
+              for (int j = 0; j < ND; ++j) oacc[0][j] *= alpha;
+              psum = make_p(m_new - base);
+              m_run[0] = m_new;
+              base = m_new;
 #pragma unroll
-              for (int j = 0; j < ND; ++j) oacc[t][j] *= alpha;
-              psum = make_p(m_run[t]);
+              for (int e = 0; e < 16; ++e) init[e] = -base;
+              have_base = true;
             }
-            l_run[t] += psum;
+            l_run[0] += psum;
           } else {
-            make_p(base_row[t]);
+            make_p0();
           }
-        } else {
+          // O^T += V^T P^T over the half's keys
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int row0 = kt * 32 + 16 * s2 + 4 * h;
+#pragma unroll
+            for (int j = 0; j < ND; ++j) {
+              const Frag<T> a = frag_from_col4<T>(ld_col4<typename G::L>(Vs, row0, j * 32),
+                                                  ld_col4<typename G::L>(Vs, row0 + 8, j * 32));
+              mma(oacc[0][j], a, pf[s2]);
+            }
+          }
+        }
+      }
+    } else {
+      if (k0 <= q0w + G::ROWS_W - 1) {  // some key of the tile is visible to this wave
+        f32x16 sacc[2][NQT];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) sacc[kt][t] = zero16();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const Frag<T> a = ld_frag(Ks + G::L::idx(kt * 32 + r, s * 16 + 8 * h));
+#pragma unroll
+            for (int t = 0; t < NQT; ++t) mma(sacc[kt][t], a, qf[t][s]);
+          }
+        }
+        if (k0 + BC - 1 > q0w) {  // the tile crosses this wave's diagonal
+#pragma unroll
+          for (int t = 0; t < NQT; ++t) {
+            const int qrel = (int)(q0w - k0) + t * 32 + r;  // query minus tile start
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                if (kt * 32 + 8 * (e >> 2) + 4 * h + (e & 3) > qrel) sacc[kt][t][e] = -INFINITY;
+          }
+        }
+        Frag<T> pf[2][2][NQT];  // P^T as B operands [key half][16-key step][query tile]
+#pragma unroll
+        for (int t = 0; t < NQT; ++t) {
           if constexpr (MODE == 0) {
             // fp32: lazily moved base, raised when a score exceeds it by more than 2^8
             float mx = -INFINITY;
@@ -267,21 +321,21 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) pf[kt][s2][t] = frag_from_acc<T>(sacc[kt][t], s2, 1.0f);
         }
-      }
-      // O^T += V^T P^T
+        // O^T += V^T P^T
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int row0 = kt * 32 + 16 * s2 + 4 * h;
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int row0 = kt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
-          for (int j = 0; j < ND; ++j) {
-            const Frag<T> a = frag_from_col4<T>(ld_col4<typename G::L>(Vs, row0, j * 32),
-                                                ld_col4<typename G::L>(Vs, row0 + 8, j * 32));
+            for (int j = 0; j < ND; ++j) {
+              const Frag<T> a = frag_from_col4<T>(ld_col4<typename G::L>(Vs, row0, j * 32),
+                                                  ld_col4<typename G::L>(Vs, row0 + 8, j * 32));
 #pragma unroll
-            for (int t = 0; t < NQT; ++t) mma(oacc[t][j], a, pf[kt][s2][t]);
+              for (int t = 0; t < NQT; ++t) mma(oacc[t][j], a, pf[kt][s2][t]);
+            }
           }
-        }
+      }
     }
     if (kt_i + 1 < ntiles) {
       if constexpr (DMA)
