@@ -38,7 +38,7 @@ struct Shape {
 // Workspace regions (byte offsets). Forward uses q, k|v, o.
 // Backward aliases: the dq of a chunk overwrites q, dk|dv overwrite k|v.
 struct Plan {
-  size_t q, uq, k, v, uk, dout, o, delta, dq_acc, dk_acc, dv_acc, wo_t, wq_t, wkv_t;
+  size_t q, uq, k, v, uk, dout, o, delta, dq_acc, dk_acc, dv_acc, wo_t, wqkv_t;
   size_t total;
 };
 
@@ -56,8 +56,10 @@ Plan make_plan(const Shape& s, bool backward) {
   memset(&p, 0, sizeof(p));
   const size_t head = (size_t)s.Np * s.d;  // elements of one [Np][d] head buffer
   Carver c;
+  // Q, then K, then V: contiguous heads of stride Np*d (the backward's dx
+  // product reads dq|dk|dv, which alias them, as one operand)
   p.q = c.take(head * s.C * s.es);
-  p.k = c.take(head * 2 * s.kvC * s.es);  // K then V, contiguous (backward: dk|dv alias them)
+  p.k = c.take(head * 2 * s.kvC * s.es);  // K then V (backward: dk|dv alias them)
   p.v = p.k + head * s.kvC * s.es;
   if (!backward) {
     p.o = c.take(head * s.C * s.es);
@@ -73,8 +75,8 @@ Plan make_plan(const Shape& s, bool backward) {
   p.dk_acc = c.take(head * s.kvC * 4);
   p.dv_acc = c.take(head * s.kvC * 4);
   p.wo_t = c.take((size_t)s.C * s.d * s.D * s.es);
-  p.wq_t = c.take((size_t)s.C * s.d * s.D * s.es);
-  p.wkv_t = c.take((size_t)2 * s.kvC * s.d * s.D * s.es);
+  // [D][C*d + 2*kvC*d]: Wq_c^T columns, then Wk_g^T, then Wv_g^T
+  p.wqkv_t = c.take((size_t)(s.C + 2 * s.kvC) * s.d * s.D * s.es);
   p.total = c.off;
   return p;
 }
@@ -311,11 +313,13 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   float* dKa = reinterpret_cast<float*>(ws + pl.dk_acc);
   float* dVa = reinterpret_cast<float*>(ws + pl.dv_acc);
   T* WoT = reinterpret_cast<T*>(ws + pl.wo_t);
-  T* WqT = reinterpret_cast<T*>(ws + pl.wq_t);
-  T* WkvT = reinterpret_cast<T*>(ws + pl.wkv_t);
+  // one row of WqkvT is [Wq_c^T | Wk_g^T | Wv_g^T]; Q, K, V heads are contiguous
+  // in the workspace in the same order, so dx takes all three in one product
+  T* WqkvT = reinterpret_cast<T*>(ws + pl.wqkv_t);
   const double l2t = log2(theta);
   const int64_t head = s.Np * s.d;
   const int64_t Cd = (int64_t)s.C * s.d, kvd = (int64_t)s.kvC * s.d;
+  const int64_t ldw = Cd + 2 * kvd;  // row stride of WqkvT
   const int nh = s.C < s.G ? s.C : s.G;
   // q is stored times log2(e)/sqrt(d) and dO times 1/sqrt(d) (see kernels.h);
   // the dK/dV kernel undoes those factors on its results
@@ -339,10 +343,10 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
     const bool last_kv = ((c0 + s.C) % s.G) == 0;
     // weight slices transposed for the products that contract over their rows
     HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wo + (int64_t)c0 * s.d, s.D, Cd, (int64_t)s.Hq * s.d, WoT, s.D, st); }));
-    HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wq + (int64_t)c0 * s.d * s.D, Cd, s.D, s.D, WqT, Cd, st); }));
+    HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wq + (int64_t)c0 * s.d * s.D, Cd, s.D, s.D, WqkvT, ldw, st); }));
     if (new_kv) {
-      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wk + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WkvT, 2 * kvd, st); }));
-      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wv + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WkvT + kvd, 2 * kvd, st); }));
+      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wk + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WqkvT + Cd, ldw, st); }));
+      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_transpose<T>(wv + (int64_t)g0 * s.d * s.D, kvd, s.D, s.D, WqkvT + Cd + kvd, ldw, st); }));
     }
     // recompute the chunk's projections
     {
@@ -441,9 +445,11 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
     }
     rc = run_weight_grad<T>(s, x, Q, s.C, dwq + (int64_t)c0 * s.d * s.D, 1, s.D, st);
     if (rc) return rc;
-    rc = run_heads_times_wt<T>(s, Q, s.C, WqT, Cd, dx, c0 > 0, st);
-    if (rc) return rc;
-    if (last_kv || s.C >= s.G) {
+    const bool group_done = last_kv || s.C >= s.G;  // dk/dv of the kv group are complete
+    if (!group_done) {
+      rc = run_heads_times_wt<T>(s, Q, s.C, WqkvT, ldw, dx, c0 > 0, st);
+      if (rc) return rc;
+    } else {
       GradFinish<T> f;
       memset(&f, 0, sizeof(f));
       f.gacc = dKa;
@@ -470,7 +476,8 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       if (rc) return rc;
       rc = run_weight_grad<T>(s, x, V, s.kvC, dwv + (int64_t)g0 * s.d * s.D, 1, s.D, st);
       if (rc) return rc;
-      rc = run_heads_times_wt<T>(s, K, 2 * s.kvC, WkvT, 2 * kvd, dx, 1, st);
+      // dx (+)= [dq_c | dk_g | dv_g] [Wq_c; Wk_g; Wv_g] in one pass over dx
+      rc = run_heads_times_wt<T>(s, Q, s.C + 2 * s.kvC, WqkvT, ldw, dx, c0 > 0, st);
       if (rc) return rc;
     }
   }
