@@ -172,13 +172,20 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
 
     if constexpr (sizeof(T) == 2) {
       if (k0 <= q0w + G::ROWS_W - 1) {  // some key of the tile is visible to this wave
-        // The two 32-key halves in turn. Each S^T chain starts from the splat
-        // of -base, so the accumulator holds S - base (log2 units).
+        // S^T of both 32-key halves (two independent chains), each chain
+        // started from the splat of -base, so it holds S - base (log2 units);
+        // then softmax and P V half by half.
+        f32x16 sacc2[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc2[kt] = mma_first(ld_frag(Ks + G::L::idx(kt * 32 + r, 8 * h)), qf[0][0], init);
+#pragma unroll
+        for (int s = 1; s < NS; ++s)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            mma(sacc2[kt], ld_frag(Ks + G::L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[0][s]);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          f32x16 sacc = mma_first(ld_frag(Ks + G::L::idx(kt * 32 + r, 8 * h)), qf[0][0], init);
-#pragma unroll
-          for (int s = 1; s < NS; ++s) mma(sacc, ld_frag(Ks + G::L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[0][s]);
+          f32x16& sacc = sacc2[kt];
           if (k0 + kt * 32 + 31 > q0w) {  // the half crosses this wave's diagonal
             const int qrel = (int)(q0w - k0) + r - kt * 32;  // query minus the half's first key
 #pragma unroll
@@ -234,6 +241,11 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
 #pragma unroll
               for (int j = 0; j < ND; ++j) oacc[0][j] *= alpha;
               psum = make_p(m_new - base);
+              // the other half's chain already ran against the old base
+              if (kt == 0) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc2[1][e] -= m_new - base;
+              }
               m_run[0] = m_new;
               base = m_new;
 #pragma unroll
