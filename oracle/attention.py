@@ -301,13 +301,15 @@ def _kv_all(x_rows_fn, n_tokens, wk, wv, kh, d, k_norm, eps, theta, block, use_r
 
 def layer_fwd_rows(x_rows_fn, x_at_fn, n_tokens, rows, wq, wk, wv, wo, n_q_heads,
                    n_kv_heads, head_dim, rope_theta, q_norm=None, k_norm=None,
-                   eps=1e-6, block=65536, row_group=16):
+                   eps=1e-6, block=65536, row_group=16, progress=None):
     """y and lse at selected query rows only (same definition as ``layer_fwd``).
 
     ``x_rows_fn(r0, r1)`` returns rows ``[r0, r1)`` of x and ``x_at_fn(idx)``
     returns the rows ``idx``; K and V are needed for all tokens, Q, S, P and O
     only for the selected rows (taken ``row_group`` rows at a time: rows are
     independent, so this bounds memory without reordering any sum).
+    ``progress(msg)``, if given, is called after each kv head's K/V and each
+    q head (long runs report as they go; it does not touch the arithmetic).
     Returns ``(y_rows [R][D], lse_rows [Hq][R])``.
     """
     rows = np.asarray(rows, dtype=np.int64)
@@ -319,6 +321,8 @@ def layer_fwd_rows(x_rows_fn, x_at_fn, n_tokens, rows, wq, wk, wv, wo, n_q_heads
     kpos = np.arange(n_tokens)
     for kh in range(n_kv_heads):
         k, v = _kv_all(x_rows_fn, n_tokens, wk, wv, kh, d, k_norm, eps, rope_theta, block)
+        if progress:
+            progress(f"oracle: k, v of kv head {kh}")
         for h in range(kh * g, (kh + 1) * g):
             q, _ = _qk_heads(x_sel, wq, h, d, q_norm, eps, rope_theta, rows)
             wo_h = np.asarray(wo[:, h * d:(h + 1) * d], dtype=F64)
@@ -327,12 +331,14 @@ def layer_fwd_rows(x_rows_fn, x_at_fn, n_tokens, rows, wq, wk, wv, wo, n_q_heads
                 o, l_h, _ = causal_attention(q[r0:r1], k, v, q_pos=rows[r0:r1], k_pos=kpos)
                 lse[h, r0:r1] = l_h
                 y[r0:r1] += o @ wo_h.T
+            if progress:
+                progress(f"oracle: rows of q head {h}")
     return y, lse
 
 
 def layer_bwd_tail_dx(x_rows_fn, dy_rows_fn, n_tokens, tail, rows, wq, wk, wv, wo,
                       n_q_heads, n_kv_heads, head_dim, rope_theta, q_norm=None,
-                      k_norm=None, eps=1e-6, block=65536, row_group=32):
+                      k_norm=None, eps=1e-6, block=65536, row_group=32, progress=None):
     """dx at selected rows inside the last ``tail`` positions.
 
     For a row i near the end, dq_i needs only query row i, and dk_i, dv_i need
@@ -340,6 +346,7 @@ def layer_bwd_tail_dx(x_rows_fn, dy_rows_fn, n_tokens, tail, rows, wq, wk, wv, w
     dx rows follow from K/V of all tokens plus Q, dO, LSE and Delta of the
     window. The window's queries are taken ``row_group`` at a time (each
     query's P row is independent; dk/dv sum their contributions).
+    ``progress(msg)`` as in ``layer_fwd_rows``.
     Returns ``dx_rows [R][D]``.
     """
     rows = np.asarray(rows, dtype=np.int64)
@@ -356,6 +363,8 @@ def layer_bwd_tail_dx(x_rows_fn, dy_rows_fn, n_tokens, tail, rows, wq, wk, wv, w
     dx = np.zeros((rows.size, xw.shape[1]), dtype=F64)
     for kh in range(n_kv_heads):
         k, v = _kv_all(x_rows_fn, n_tokens, wk, wv, kh, d, k_norm, eps, rope_theta, block)
+        if progress:
+            progress(f"oracle: k, v of kv head {kh}")
         _, uk = _qk_heads(xw, wk, kh, d, k_norm, eps, rope_theta, wpos)
         dk_w = np.zeros((tail, d))
         dv_w = np.zeros((tail, d))
@@ -376,6 +385,8 @@ def layer_bwd_tail_dx(x_rows_fn, dy_rows_fn, n_tokens, tail, rows, wq, wk, wv, w
             if q_norm is not None:
                 dq, _ = rmsnorm_bwd(uq, q_norm, eps, dq)
             dx += dq[sel] @ np.asarray(wq[h * d:(h + 1) * d], dtype=F64)
+            if progress:
+                progress(f"oracle: tail of q head {h}")
         dk_w = rope_transpose(dk_w, wpos, rope_theta)
         if k_norm is not None:
             dk_w, _ = rmsnorm_bwd(uk, k_norm, eps, dk_w)

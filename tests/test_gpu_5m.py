@@ -1,0 +1,130 @@
+"""GPU parity at the 5M-token Llama3-8B share (opt-in: about ten minutes).
+
+Workload: N = 5242880 tokens, d_model 4096, 4 q / 1 kv heads, head_dim 128,
+bf16, RoPE theta 5e5, causal, chunk_heads = 1, through the same C ABI and
+launch configuration as the bench.
+
+So that the fp64 oracle stays affordable on the host, x and dY are periodic
+in the token dimension: an 8192-row seeded block tiled over the sequence.
+RoPE still makes every position distinct (a key's rotation depends on its
+absolute position), every kernel runs at full size, and x offsets pass
+2^32 elements, so 64-bit indexing is exercised. Checked:
+  * y and LSE at 256 sampled query rows (corners, rows past 2^31/d_model,
+    seeded uniform draws) against ``oracle.layer_fwd_rows``;
+  * dx at 64 rows of the last 512 positions against ``oracle.layer_bwd_tail_dx``;
+  * the weight-gradient identities <dWo, Wo> = <dWv, Wv> = <dY, y> and
+    <dWq, Wq> = <dWk, Wk>, which hold exactly at any size;
+  * the forward and backward workspace bytes.
+Enable with UPIPE_TEST_5M=1.
+"""
+import os
+import time
+
+import numpy as np
+import pytest
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(os.environ.get("UPIPE_TEST_5M") != "1", reason="opt-in (UPIPE_TEST_5M=1): ~10 min"),
+]
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from headwise_chunked_attention_amd import api  # noqa: E402
+from headwise_chunked_attention_amd.synth import LayerInputs  # noqa: E402
+
+N, D, HQ, HKV, HD, THETA, C = 5242880, 4096, 4, 1, 128, 5e5, 1
+PERIOD = 8192
+TOL = 2e-2
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _relerr(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def _dot(a, b, rows=65536):
+    # fp64 sum, in row blocks (a whole [N][D] tensor in fp64 does not fit)
+    a2, b2 = a.reshape(a.shape[0], -1), b.reshape(b.shape[0], -1)
+    tot = 0.0
+    for r0 in range(0, a2.shape[0], rows):
+        tot += float((a2[r0:r0 + rows].double() * b2[r0:r0 + rows].double()).sum().item())
+    return tot
+
+
+def _rows(a, b, base):
+    return base[np.arange(a, b) % PERIOD]
+
+
+@pytest.mark.timeout(1150)
+def test_llama_share_5m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    inp = LayerInputs(PERIOD, D, HQ, HKV, HD, "bf16", seed=5)
+    dev = "cuda"
+    bf = torch.bfloat16
+    reps = N // PERIOD
+    x = torch.from_numpy(inp.x).to(dev).to(bf).repeat(reps, 1)
+    dy = torch.from_numpy(inp.dy).to(dev).to(bf).repeat(reps, 1)
+    w = {k: torch.from_numpy(getattr(inp, k)).to(dev).to(bf) for k in ("wq", "wk", "wv", "wo")}
+    kw = dict(n_q_heads=HQ, n_kv_heads=HKV, head_dim=HD, rope_theta=THETA, chunk_heads=C)
+    ws_f = api.workspace_bytes(N, D, HQ, HKV, HD, C, False, "bf16", False)
+    ws_b = api.workspace_bytes(N, D, HQ, HKV, HD, C, False, "bf16", True)
+    _log(f"N={N}: workspace fwd {ws_f / 1e9:.2f} GB, bwd {ws_b / 1e9:.2f} GB")
+
+    _log("GPU forward")
+    t0 = time.perf_counter()
+    y, lse = api.attn_fwd(x, w["wq"], w["wk"], w["wv"], w["wo"], **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _log(f"GPU forward {t1 - t0:.1f} s (first call); backward")
+    g = api.attn_bwd(x, w["wq"], w["wk"], w["wv"], w["wo"], dy, lse, **kw)
+    torch.cuda.synchronize()
+    dx, dwq, dwk, dwv, dwo = g[:5]
+    _log(f"GPU backward {time.perf_counter() - t1:.1f} s (first call)")
+
+    # weight-gradient identities (every row of the sequence contributes)
+    ref = _dot(dy, y)
+    a_o, a_v, a_q, a_k = _dot(dwo, w["wo"]), _dot(dwv, w["wv"]), _dot(dwq, w["wq"]), _dot(dwk, w["wk"])
+    _log(f"<dY,y>={ref:.6e} <dWo,Wo>={a_o:.6e} <dWv,Wv>={a_v:.6e} <dWq,Wq>={a_q:.6e} <dWk,Wk>={a_k:.6e}")
+    assert abs(a_o - ref) <= TOL * abs(ref)
+    assert abs(a_v - ref) <= TOL * abs(ref)
+    assert abs(a_q - a_k) <= TOL * max(abs(a_q), abs(a_k))
+
+    # sampled query rows of the forward
+    fixed = {0, 1, 63, 64, 255, 256, PERIOD - 1, PERIOD, (1 << 31) // D, (1 << 31) // D + 1,
+             (1 << 32) // D, N // 2, N - 2, N - 1}
+    rng = np.random.default_rng(7)
+    rows = set(fixed)
+    while len(rows) < 256:
+        rows.add(int(rng.integers(0, N)))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    idx = torch.from_numpy(rows).to(dev)
+    y_rows = y.index_select(0, idx).float().cpu().numpy()
+    lse_rows = lse.index_select(1, idx).float().cpu().numpy()
+    y_ref, lse_ref = oracle.layer_fwd_rows(lambda a, b: _rows(a, b, inp.x), lambda i: inp.x[np.asarray(i) % PERIOD], N,
+                                           rows, inp.wq, inp.wk, inp.wv, inp.wo, HQ, HKV, HD, THETA, row_group=64,
+                                           progress=_log)
+    ey, el = _relerr(y_rows, y_ref), _relerr(lse_rows, lse_ref)
+    ml = float(np.max(np.abs(lse_rows - lse_ref)))
+    _log(f"sampled rows: y rel {ey:.3e}  lse rel {el:.3e} max {ml:.3e}")
+    assert ey <= TOL and el <= TOL and ml <= TOL
+
+    # dx at rows of the last 512 positions
+    tail = 512
+    trows = np.sort(rng.choice(np.arange(N - tail, N), size=64, replace=False))
+    trows[-1] = N - 1
+    got = dx.index_select(0, torch.from_numpy(trows).to(dev)).float().cpu().numpy()
+    del x, dy, y, g, dx
+    torch.cuda.empty_cache()
+    ref_dx = oracle.layer_bwd_tail_dx(lambda a, b: _rows(a, b, inp.x), lambda a, b: _rows(a, b, inp.dy), N, tail,
+                                      trows, inp.wq, inp.wk, inp.wv, inp.wo, HQ, HKV, HD, THETA, progress=_log)
+    e = _relerr(got, ref_dx)
+    _log(f"tail dx rel {e:.3e}")
+    assert e <= TOL
