@@ -377,16 +377,20 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   float* Cs = reinterpret_cast<float*>(smem);
   acc_to_lds<BN>(Cs, wm, wn, acc);
   lds_barrier();
+  int seg = 0;
+  while (seg + 1 < p.nseg && n0 >= p.seg_end[seg]) ++seg;
+  float* out = p.out[seg];
+  const int64_t nc0 = n0 - (seg ? p.seg_end[seg - 1] : 0);
   const int tid = threadIdx.x;
   if (p.ldn == 1) {
     for (int c = tid; c < BM * BN; c += NTHREADS) {
       const int row = c / BN, col = c % BN;
-      atomicAdd(p.out + (m0 + row) * p.ldm + (n0 + col), Cs[row * SC + col]);
+      atomicAdd(out + (m0 + row) * p.ldm + (nc0 + col), Cs[row * SC + col]);
     }
   } else {
     for (int c = tid; c < BM * BN; c += NTHREADS) {
       const int col = c / BM, row = c % BM;
-      atomicAdd(p.out + (m0 + row) * p.ldm + (n0 + col) * p.ldn, Cs[row * SC + col]);
+      atomicAdd(out + (m0 + row) * p.ldm + (nc0 + col) * p.ldn, Cs[row * SC + col]);
     }
   }
 }

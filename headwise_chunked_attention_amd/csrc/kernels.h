@@ -60,7 +60,11 @@ struct GemmTN {
   int64_t ldb;
   int64_t M, N, K;
   int64_t ksplit;
-  float* out;
+  // output column n of segment s (n < seg_end[s]) goes to
+  // out[s] + m * ldm + (n - seg_begin(s)) * ldn; segments hold whole n tiles
+  float* out[3];
+  int64_t seg_end[3];
+  int nseg;
   int64_t ldm, ldn;
 };
 

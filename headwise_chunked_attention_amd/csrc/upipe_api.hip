@@ -215,10 +215,12 @@ int run_heads_times_wt(const Shape& s, const T* a_heads, int nheads, const T* b,
   return UPIPE_OK;
 }
 
-// Weight gradient out[m*ldm + n*ldn] += sum_tok rows[tok][m] * heads[n/d][tok][n%d]
+// Weight gradient out[m*ldm + n*ldn] += sum_tok rows[tok][m] * heads[n/d][tok][n%d],
+// with the heads split into up to 3 segments of seg_heads[i] heads, each with
+// its own output.
 template <typename T>
-int run_weight_grad(const Shape& s, const T* rows, const T* heads, int nheads, float* out, int64_t ldm,
-                    int64_t ldn, hipStream_t st) {
+int run_weight_grad_segs(const Shape& s, const T* rows, const T* heads, int nseg, const int* seg_heads,
+                         float* const* outs, int64_t ldm, int64_t ldn, hipStream_t st) {
   GemmTN<T> g;
   memset(&g, 0, sizeof(g));
   g.a = rows;
@@ -228,18 +230,32 @@ int run_weight_grad(const Shape& s, const T* rows, const T* heads, int nheads, f
   g.b_nblk_stride = s.Np * s.d;
   g.ldb = s.d;
   g.M = s.D;
-  g.N = (int64_t)nheads * s.d;
+  int64_t n = 0;
+  bool all128 = true;
+  for (int i = 0; i < nseg; ++i) {
+    n += (int64_t)seg_heads[i] * s.d;
+    g.seg_end[i] = n;
+    g.out[i] = outs[i];
+    all128 = all128 && ((int64_t)seg_heads[i] * s.d) % 128 == 0;
+  }
+  g.nseg = nseg;
+  g.N = n;
   g.K = s.N;
-  const int bn = (g.N % 128 == 0) ? 128 : 64;
+  const int bn = all128 ? 128 : 64;  // n tiles never straddle two segments
   const int64_t tiles = (g.M / 128) * (g.N / bn);
   int64_t splits = 1024 / (tiles > 0 ? tiles : 1);
   if (splits < 1) splits = 1;
   g.ksplit = round_up((s.N + splits - 1) / splits, 64);
-  g.out = out;
   g.ldm = ldm;
   g.ldn = ldn;
   HIP_TRY(timed(UPIPE_KERNEL_WGRAD, 2.0 * g.M * g.N * g.K, st, [&] { return launch_gemm_tn<T>(g, bn, st); }));
   return UPIPE_OK;
+}
+
+template <typename T>
+int run_weight_grad(const Shape& s, const T* rows, const T* heads, int nheads, float* out, int64_t ldm,
+                    int64_t ldn, hipStream_t st) {
+  return run_weight_grad_segs<T>(s, rows, heads, 1, &nheads, &out, ldm, ldn, st);
 }
 
 template <typename T>
@@ -443,10 +459,10 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       f.log2_theta = l2t;
       HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_grad_finish<T>(f, s.d, st); }));
     }
-    rc = run_weight_grad<T>(s, x, Q, s.C, dwq + (int64_t)c0 * s.d * s.D, 1, s.D, st);
-    if (rc) return rc;
     const bool group_done = last_kv || s.C >= s.G;  // dk/dv of the kv group are complete
     if (!group_done) {
+      rc = run_weight_grad<T>(s, x, Q, s.C, dwq + (int64_t)c0 * s.d * s.D, 1, s.D, st);
+      if (rc) return rc;
       rc = run_heads_times_wt<T>(s, Q, s.C, WqkvT, ldw, dx, c0 > 0, st);
       if (rc) return rc;
     } else {
@@ -472,10 +488,14 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       fv.N = s.N;
       fv.Np = s.Np;
       HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_grad_finish<T>(fv, s.d, st); }));
-      rc = run_weight_grad<T>(s, x, K, s.kvC, dwk + (int64_t)g0 * s.d * s.D, 1, s.D, st);
-      if (rc) return rc;
-      rc = run_weight_grad<T>(s, x, V, s.kvC, dwv + (int64_t)g0 * s.d * s.D, 1, s.D, st);
-      if (rc) return rc;
+      // dWq_c, dWk_g, dWv_g from one pass over x: [dq_c | dk_g | dv_g] are contiguous heads
+      {
+        const int seg_heads[3] = {s.C, s.kvC, s.kvC};
+        float* const outs[3] = {dwq + (int64_t)c0 * s.d * s.D, dwk + (int64_t)g0 * s.d * s.D,
+                                dwv + (int64_t)g0 * s.d * s.D};
+        rc = run_weight_grad_segs<T>(s, x, Q, 3, seg_heads, outs, 1, s.D, st);
+        if (rc) return rc;
+      }
       // dx (+)= [dq_c | dk_g | dv_g] [Wq_c; Wk_g; Wv_g] in one pass over dx
       rc = run_heads_times_wt<T>(s, Q, s.C + 2 * s.kvC, WqkvT, ldw, dx, c0 > 0, st);
       if (rc) return rc;
