@@ -9,6 +9,10 @@
 //
 // With P = exp(S/sqrt(d) - LSE) and dS = P (dP - Delta) / sqrt(d):
 //   dV = P^T dO,  dK = dS^T Q,  dQ = dS K.
+// q arrives multiplied by log2(e)/sqrt(d) and dO by 1/sqrt(d), so Q K^T is
+// the exponent in log2 units and dO V^T is dP/sqrt(d); the dK/dV kernel
+// scales its two results back once at the end. Both kernels form the same
+// dS values.
 // Two kernels, no atomics:
 //  * dK/dV kernel, key-stationary: a workgroup owns a block of keys and walks
 //    the query tiles at or after it for every q head of the chunk reading this

@@ -9,15 +9,19 @@
 // one query column and 16 keys of each 32x32 tile. Row statistics of the
 // softmax are then an in-lane reduction plus one exchange between the two
 // half-waves, and P^T feeds O^T = V^T P^T straight from the accumulators
-// (see common.h). K and V tiles are row-major copies [key][d] in LDS, double
-// buffered and prefetched through registers one tile ahead; V^T operands are
-// column reads (LDS transpose reads).
+// (see common.h). q arrives multiplied by log2(e)/sqrt(d), so S is already
+// the exponent in log2 units. K and V tiles are row-major copies [key][d] in
+// LDS, double buffered: bf16 tiles arrive one tile ahead by direct
+// global -> LDS loads, fp32 tiles through registers; V^T operands are column
+// reads (LDS transpose reads).
 //
-// Workgroup: 8 waves x (32*NQT) query rows (two waves per SIMD). `hp` heads of the same kv head
-// are packed per workgroup (GQA): the K/V tile in LDS then serves hp heads.
+// Workgroup: 8 waves x (32*NQT) query rows (two waves per SIMD). `hp` heads
+// of the same kv head are packed per workgroup (GQA): the K/V tile in LDS then
+// serves hp heads.
 // Mode 0 (training forward): online softmax; writes O and LSE.
 // Mode 1 (backward recompute): LSE is given; writes O and
-//   Delta_i = dO_i . O_i, the row term of the softmax backward.
+//   Delta_i = dO_i . O_i (with the backward's pre-scaled dO), the row term of
+//   the softmax backward.
 #include <math.h>
 
 #include <type_traits>
