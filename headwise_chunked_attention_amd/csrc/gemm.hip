@@ -23,16 +23,25 @@ namespace {
 constexpr int BM = 128;
 constexpr int NTHREADS = 256;
 
-template <typename T> struct GemmGeo {
-  static constexpr int BK = 128 / (int)sizeof(T);  // 128 bytes of k per row
+// KB bytes of k per tile row; LDS rows padded by 16 bytes (16 rows of one
+// 16-byte column then hit 16 distinct bank groups).
+template <typename T, int KB = 128> struct GemmGeo {
+  static constexpr int BK = KB / (int)sizeof(T);
   static constexpr int SK = lds_stride<T>(BK);
   static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int CPR = BK / VEC;  // 16-byte chunks per tile row
 };
+// The accumulating products (y/dx, K = a few heads) are bound by the
+// read-modify-write of their output: 64-byte k rows and a two-pass epilogue
+// keep their LDS at 40 KB, so three workgroups share a CU. The projections
+// (K = d_model) keep 128-byte rows (fewer k steps and barriers).
+template <int EPI> constexpr int nt_kb() { return EPI == EPI_ACCUM ? 64 : 128; }
+constexpr int EPI_ROWS = BM / 2;  // rows per epilogue pass
 
-template <typename T, int BN>
+template <typename T, int BN, int EPI>
 constexpr int gemm_smem_bytes() {
-  constexpr int main_bytes = 2 * (BM + BN) * GemmGeo<T>::SK * (int)sizeof(T);
-  constexpr int epi_bytes = BM * (BN + 4) * 4;
+  constexpr int main_bytes = 2 * (BM + BN) * GemmGeo<T, nt_kb<EPI>()>::SK * (int)sizeof(T);
+  constexpr int epi_bytes = EPI_ROWS * (BN + 4) * 4;
   return main_bytes > epi_bytes ? main_bytes : epi_bytes;
 }
 
@@ -55,10 +64,12 @@ DEV void mma_tile_step(const T* As, const T* Bs, int SK, int ks, int wm, int wn,
     for (int nt = 0; nt < NTW; ++nt) mma(acc[mt][nt], a[mt], b[nt]);
 }
 
-// Accumulators -> fp32 LDS tile Cs[BM][BN + 4].
+// Accumulators -> fp32 LDS tile Cs[rows][BN + 4]; row0 is the tile row of
+// Cs row 0 (the waves of other rows skip).
 template <int BN>
-DEV void acc_to_lds(float* Cs, int wm, int wn, const f32x16 (&acc)[2][BN / 64]) {
+DEV void acc_to_lds(float* Cs, int row0, int nrows, int wm, int wn, const f32x16 (&acc)[2][BN / 64]) {
   constexpr int NTW = BN / 64, SC = BN + 4;
+  if (wm * 64 + 64 <= row0 || wm * 64 >= row0 + nrows) return;
   const int l = lane_id();
   const int col0 = wn * (BN / 2) + (l & 31), h = l >> 5;
 #pragma unroll
@@ -69,52 +80,52 @@ DEV void acc_to_lds(float* Cs, int wm, int wn, const f32x16 (&acc)[2][BN / 64]) 
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          Cs[(wm * 64 + mt * 32 + 8 * i + 4 * h + j) * SC + col0 + nt * 32] = acc[mt][nt][4 * i + j];
+          Cs[(wm * 64 + mt * 32 + 8 * i + 4 * h + j - row0) * SC + col0 + nt * 32] = acc[mt][nt][4 * i + j];
 }
 
-template <typename T, int BN>
+template <typename T, int BN, class G>
 DEV void nt_load_tile(const GemmNT<T>& p, const T* bptr, int64_t ldb, int64_t m0, int64_t nrow0,
-                      int64_t k0, u32x4 (&ra)[BM * 8 / NTHREADS], u32x4 (&rb)[BN * 8 / NTHREADS]) {
-  constexpr int VEC = GemmGeo<T>::VEC;
+                      int64_t k0, u32x4 (&ra)[BM * G::CPR / NTHREADS], u32x4 (&rb)[BN * G::CPR / NTHREADS]) {
+  constexpr int VEC = G::VEC, CPR = G::CPR;
   const int tid = threadIdx.x;
   const T* abase = p.a + (k0 / p.a_kblk) * p.a_kblk_stride + (k0 % p.a_kblk);
 #pragma unroll
-  for (int i = 0; i < BM * 8 / NTHREADS; ++i) {
+  for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
     const int c = tid + i * NTHREADS;
-    const int row = c >> 3, cc = c & 7;
+    const int row = c / CPR, cc = c % CPR;
     const int64_t m = m0 + row;
     ra[i] = (m < p.M) ? ld_raw16(abase + m * p.lda + cc * VEC) : zero_raw16();
   }
 #pragma unroll
-  for (int i = 0; i < BN * 8 / NTHREADS; ++i) {
+  for (int i = 0; i < BN * CPR / NTHREADS; ++i) {
     const int c = tid + i * NTHREADS;
-    const int row = c >> 3, cc = c & 7;
+    const int row = c / CPR, cc = c % CPR;
     rb[i] = ld_raw16(bptr + (nrow0 + row) * ldb + k0 + cc * VEC);
   }
 }
 
-template <typename T, int BN>
-DEV void nt_store_tile(T* As, T* Bs, const u32x4 (&ra)[BM * 8 / NTHREADS],
-                       const u32x4 (&rb)[BN * 8 / NTHREADS]) {
-  constexpr int VEC = GemmGeo<T>::VEC, SK = GemmGeo<T>::SK;
+template <typename T, int BN, class G>
+DEV void nt_store_tile(T* As, T* Bs, const u32x4 (&ra)[BM * G::CPR / NTHREADS], const u32x4 (&rb)[BN * G::CPR / NTHREADS]) {
+  constexpr int VEC = G::VEC, SK = G::SK, CPR = G::CPR;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < BM * 8 / NTHREADS; ++i) {
+  for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
     const int c = tid + i * NTHREADS;
-    st_raw16(As + (c >> 3) * SK + (c & 7) * VEC, ra[i]);
+    st_raw16(As + (c / CPR) * SK + (c % CPR) * VEC, ra[i]);
   }
 #pragma unroll
-  for (int i = 0; i < BN * 8 / NTHREADS; ++i) {
+  for (int i = 0; i < BN * CPR / NTHREADS; ++i) {
     const int c = tid + i * NTHREADS;
-    st_raw16(Bs + (c >> 3) * SK + (c & 7) * VEC, rb[i]);
+    st_raw16(Bs + (c / CPR) * SK + (c % CPR) * VEC, rb[i]);
   }
 }
 
 template <typename T, int BN, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
-  constexpr int BK = GemmGeo<T>::BK, SK = GemmGeo<T>::SK, VEC = GemmGeo<T>::VEC;
+  using G = GemmGeo<T, nt_kb<EPI>()>;
+  constexpr int BK = G::BK, SK = G::SK, VEC = G::VEC;
   constexpr int NTW = BN / 64, SC = BN + 4;
-  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<T, BN>()];
+  __shared__ __attribute__((aligned(16))) char smem[gemm_smem_bytes<T, BN, EPI>()];
   T* As = reinterpret_cast<T*>(smem);
   T* Bs = As + 2 * BM * SK;
 
@@ -138,116 +149,119 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
     for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = zero16();
 
   const int tid = threadIdx.x;
-  // EPI_ACCUM: the old values of the output tile are fetched before the
-  // k loop (K is short here, so their latency would otherwise be exposed)
-  constexpr int CH = EPI == EPI_ACCUM ? BM * BN / VEC / NTHREADS : 1;
+  constexpr int CPR = G::CPR;
+  // EPI_ACCUM: the old values of the first epilogue pass's rows are fetched
+  // before the k loop (K is short here, so their latency would otherwise be
+  // exposed), those of the second pass when the epilogue starts
+  constexpr int CH = EPI == EPI_ACCUM ? EPI_ROWS * BN / VEC / NTHREADS : 1;
   u32x4 old[CH];
-  if constexpr (EPI == EPI_ACCUM) {
+  auto load_old = [&](int pass) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + i * NTHREADS;
-      const int row = c / (BN / VEC), cv = c % (BN / VEC);
+      const int row = pass * EPI_ROWS + c / (BN / VEC), cv = c % (BN / VEC);
       const int64_t m = m0 + row;
       old[i] = (p.accumulate && m < p.M) ? ld_raw16(p.c + m * p.ldc + n0 + cv * VEC) : zero_raw16();
     }
-  }
+  };
+  if constexpr (EPI == EPI_ACCUM) load_old(0);
 
-  u32x4 ra[BM * 8 / NTHREADS], rb[BN * 8 / NTHREADS];
+  u32x4 ra[BM * CPR / NTHREADS], rb[BN * CPR / NTHREADS];
   const int64_t nk = p.K / BK;
-  nt_load_tile<T, BN>(p, bptr, ldb, m0, nrow0, 0, ra, rb);
-  nt_store_tile<T, BN>(As, Bs, ra, rb);
+  nt_load_tile<T, BN, G>(p, bptr, ldb, m0, nrow0, 0, ra, rb);
+  nt_store_tile<T, BN, G>(As, Bs, ra, rb);
   lds_barrier();
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int buf = (int)(kt & 1);
-    if (kt + 1 < nk) nt_load_tile<T, BN>(p, bptr, ldb, m0, nrow0, (kt + 1) * BK, ra, rb);
+    if (kt + 1 < nk) nt_load_tile<T, BN, G>(p, bptr, ldb, m0, nrow0, (kt + 1) * BK, ra, rb);
     // LDS holds [A0][A1][B0][B1]
     const T* Ab = As + buf * BM * SK;
     const T* Bb = Bs + buf * BN * SK;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) mma_tile_step<T, BN>(Ab, Bb, SK, ks, wm, wn, acc);
-    if (kt + 1 < nk) nt_store_tile<T, BN>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra, rb);
+    if (kt + 1 < nk) nt_store_tile<T, BN, G>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra, rb);
     lds_barrier();
   }
 
+  // Epilogue in two passes of EPI_ROWS tile rows through Cs[EPI_ROWS][BN + 4].
   float* Cs = reinterpret_cast<float*>(smem);
-  acc_to_lds<BN>(Cs, wm, wn, acc);
-  lds_barrier();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int r0 = pass * EPI_ROWS;
+    if (pass) lds_barrier();  // the previous pass is done with Cs
+    acc_to_lds<BN>(Cs, r0, EPI_ROWS, wm, wn, acc);
+    lds_barrier();
 
-  if constexpr (EPI == EPI_ACCUM) {
+    if constexpr (EPI == EPI_ACCUM) {
+      if (pass) load_old(1);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + i * NTHREADS;
-      const int row = c / (BN / VEC), cv = c % (BN / VEC);
-      const int64_t m = m0 + row;
-      if (m >= p.M) continue;
-      float v[VEC], o[VEC];
-      raw16_to_f<T>(old[i], o);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e] + o[e];
-      st16_f<T>(p.c + m * p.ldc + n0 + cv * VEC, v);
-    }
-  } else {
-    const HeadOut<T> ho = p.ho[seg];
-    const int64_t head = nrow0 / BN;
-    if (ho.pre) {
-      T* dst = ho.pre + head * p.Np * BN + m0 * BN;
-      for (int c = tid; c < BM * BN / VEC; c += NTHREADS) {
+      for (int i = 0; i < CH; ++i) {
+        const int c = tid + i * NTHREADS;
         const int row = c / (BN / VEC), cv = c % (BN / VEC);
-        float v[VEC];
+        const int64_t m = m0 + r0 + row;
+        if (m >= p.M) continue;
+        float v[VEC], o[VEC];
+        raw16_to_f<T>(old[i], o);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
-        st16_f<T>(dst + row * BN + cv * VEC, v);
+        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e] + o[e];
+        st16_f<T>(p.c + m * p.ldc + n0 + cv * VEC, v);
       }
-      lds_barrier();
-    }
-    if (ho.gamma || ho.rope) {
-      // two threads per row; thread half covers pairs [half*BN/4, half*BN/4 + BN/4)
-      const int row = tid >> 1, half = tid & 1;
-      float* cr = Cs + row * SC;
-      constexpr int PP = BN / 4;
-      if (ho.gamma) {
-        float ss = 0.f;
+    } else {
+      const HeadOut<T> ho = p.ho[seg];
+      const int64_t head = nrow0 / BN;
+      const int64_t mr = m0 + r0;  // first token row of the pass
+      if (ho.pre) {
+        T* dst = ho.pre + head * p.Np * BN + mr * BN;
+        for (int c = tid; c < EPI_ROWS * BN / VEC; c += NTHREADS) {
+          const int row = c / (BN / VEC), cv = c % (BN / VEC);
+          float v[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+          st16_f<T>(dst + row * BN + cv * VEC, v);
+        }
+        lds_barrier();
+      }
+      if (ho.gamma || ho.rope) {
+        // four threads per row; quarter q covers pairs [q*BN/8, q*BN/8 + BN/8)
+        static_assert(EPI_ROWS * 4 == NTHREADS, "four threads per row");
+        const int row = tid >> 2, qq = tid & 3;
+        float* cr = Cs + row * SC;
+        constexpr int PP = BN / 8;
+        if (ho.gamma) {
+          float ss = 0.f;
 #pragma unroll 4
-        for (int i = half * PP; i < half * PP + PP; ++i) ss += cr[i] * cr[i] + cr[i + BN / 2] * cr[i + BN / 2];
-        ss += __shfl_xor(ss, 1);
-        const float r = 1.0f / sqrtf(ss / (float)BN + p.eps);
-        for (int i = half * PP; i < half * PP + PP; ++i) {
-          cr[i] = to_f<T>(ho.gamma[i]) * (cr[i] * r);
-          cr[i + BN / 2] = to_f<T>(ho.gamma[i + BN / 2]) * (cr[i + BN / 2] * r);
+          for (int i = qq * PP; i < qq * PP + PP; ++i) ss += cr[i] * cr[i] + cr[i + BN / 2] * cr[i + BN / 2];
+          ss += __shfl_xor(ss, 1);
+          ss += __shfl_xor(ss, 2);
+          const float rs = 1.0f / sqrtf(ss / (float)BN + p.eps);
+          for (int i = qq * PP; i < qq * PP + PP; ++i) {
+            cr[i] = to_f<T>(ho.gamma[i]) * (cr[i] * rs);
+            cr[i + BN / 2] = to_f<T>(ho.gamma[i + BN / 2]) * (cr[i + BN / 2] * rs);
+          }
         }
-      }
-      if (ho.rope) {
-        const double pos = (double)(m0 + row);
-        for (int i = half * PP; i < half * PP + PP; ++i) {
-          const double omega = exp2(-(2.0 * i / BN) * p.log2_theta);
-          double sd, cd;
-          sincos(pos * omega, &sd, &cd);
-          const float c = (float)cd, s = (float)sd;
-          const float u = cr[i], wv = cr[i + BN / 2];
-          cr[i] = u * c - wv * s;
-          cr[i + BN / 2] = wv * c + u * s;
+        if (ho.rope) {
+          const double pos = (double)(mr + row);
+          for (int i = qq * PP; i < qq * PP + PP; ++i) {
+            const double omega = exp2(-(2.0 * i / BN) * p.log2_theta);
+            double sd, cd;
+            sincos(pos * omega, &sd, &cd);
+            const float c = (float)cd, sn = (float)sd;
+            const float u = cr[i], wv = cr[i + BN / 2];
+            cr[i] = u * c - wv * sn;
+            cr[i + BN / 2] = wv * c + u * sn;
+          }
         }
+        lds_barrier();
       }
-      lds_barrier();
-    }
-    if (ho.rm) {
-      T* dst = ho.rm + head * p.Np * BN + m0 * BN;
-      for (int c = tid; c < BM * BN / VEC; c += NTHREADS) {
-        const int row = c / (BN / VEC), cv = c % (BN / VEC);
-        float v[VEC];
+      if (ho.rm) {
+        T* dst = ho.rm + head * p.Np * BN + mr * BN;
+        for (int c = tid; c < EPI_ROWS * BN / VEC; c += NTHREADS) {
+          const int row = c / (BN / VEC), cv = c % (BN / VEC);
+          float v[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e] * ho.scale;
-        st16_f<T>(dst + row * BN + cv * VEC, v);
-      }
-    }
-    if (ho.tr) {
-      T* dst = ho.tr + head * BN * p.Np + m0;
-      for (int c = tid; c < BN * (BM / VEC); c += NTHREADS) {
-        const int col = c / (BM / VEC), rv = c % (BM / VEC);
-        float v[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) v[e] = Cs[(rv * VEC + e) * SC + col];
-        st16_f<T>(dst + col * p.Np + rv * VEC, v);
+          for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e] * ho.scale;
+          st16_f<T>(dst + row * BN + cv * VEC, v);
+        }
       }
     }
   }
@@ -263,7 +277,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
 template <typename T, int COLS>
 struct TnTile {
   using L = Tile<T, COLS>;
-  static constexpr int VEC = 16 / (int)sizeof(T), BK = GemmGeo<T>::BK;
+  static constexpr int VEC = 16 / (int)sizeof(T), BK = GemmGeo<T, 128>::BK;
   static constexpr int RCH = COLS / VEC;        // 16-byte chunks per row
   static constexpr int PER = BK * RCH / NTHREADS;  // chunks per thread
   static_assert((BK * RCH) % NTHREADS == 0, "tile chunks");
@@ -292,7 +306,7 @@ DEV void tn_store(T* S, const u32x4 (&r)[TnTile<T, COLS>::PER]) {
 
 template <typename T, int BN>
 constexpr int tn_smem_bytes() {
-  constexpr int BK = GemmGeo<T>::BK;
+  constexpr int BK = GemmGeo<T, 128>::BK;
   constexpr int main_bytes = 2 * (Tile<T, BM>::ELEMS(BK) + Tile<T, BN>::ELEMS(BK)) * (int)sizeof(T);
   constexpr int epi_bytes = BM * (BN + 4) * 4;
   return main_bytes > epi_bytes ? main_bytes : epi_bytes;
@@ -300,7 +314,7 @@ constexpr int tn_smem_bytes() {
 
 template <typename T, int BN>
 __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
-  constexpr int BK = GemmGeo<T>::BK;
+  constexpr int BK = GemmGeo<T, 128>::BK;
   constexpr int NTW = BN / 64, SC = BN + 4;
   using LA = Tile<T, BM>;
   using LB = Tile<T, BN>;
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   }
 
   float* Cs = reinterpret_cast<float*>(smem);
-  acc_to_lds<BN>(Cs, wm, wn, acc);
+  acc_to_lds<BN>(Cs, 0, BM, wm, wn, acc);
   lds_barrier();
   int seg = 0;
   while (seg + 1 < p.nseg && n0 >= p.seg_end[seg]) ++seg;

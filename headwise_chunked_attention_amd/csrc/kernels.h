@@ -15,7 +15,6 @@ enum { EPI_ACCUM = 0, EPI_HEADS = 1 };
 template <typename T>
 struct HeadOut {
   T* rm;           // [heads][Np][d] row-major, or null
-  T* tr;           // [heads][d][Np] transposed, or null
   T* pre;          // [heads][Np][d] values before norm/RoPE, or null
   const T* gamma;  // [d] RMSNorm weight (norm applied iff non-null)
   int rope;        // rotate (i, i + d/2) pairs by pos * theta^(-2i/d)
