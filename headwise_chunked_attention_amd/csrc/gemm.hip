@@ -13,6 +13,8 @@
 //   atomics.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -93,8 +95,10 @@ DEV void nt_load_tile(const GemmNT<T>& p, const T* bptr, int64_t ldb, int64_t m0
   for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
     const int c = tid + i * NTHREADS;
     const int row = c / CPR, cc = c % CPR;
-    const int64_t m = m0 + row;
-    ra[i] = (m < p.M) ? ld_raw16(abase + m * p.lda + cc * VEC) : zero_raw16();
+    // rows past M load row M-1 (no branch around the load, so the waits
+    // for a register slot can count it); the tile store zeroes them
+    const int64_t m = min(m0 + row, p.M - 1);
+    ra[i] = ld_raw16(abase + m * p.lda + cc * VEC);
   }
 #pragma unroll
   for (int i = 0; i < BN * CPR / NTHREADS; ++i) {
@@ -105,13 +109,22 @@ DEV void nt_load_tile(const GemmNT<T>& p, const T* bptr, int64_t ldb, int64_t m0
 }
 
 template <typename T, int BN, class G>
-DEV void nt_store_tile(T* As, T* Bs, const u32x4 (&ra)[BM * G::CPR / NTHREADS], const u32x4 (&rb)[BN * G::CPR / NTHREADS]) {
+DEV void nt_store_tile(T* As, T* Bs, const u32x4 (&ra)[BM * G::CPR / NTHREADS], const u32x4 (&rb)[BN * G::CPR / NTHREADS],
+                       int64_t rows_left) {
   constexpr int VEC = G::VEC, SK = G::SK, CPR = G::CPR;
   const int tid = threadIdx.x;
+  if (rows_left >= BM) {
 #pragma unroll
-  for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
-    const int c = tid + i * NTHREADS;
-    st_raw16(As + (c / CPR) * SK + (c % CPR) * VEC, ra[i]);
+    for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
+      const int c = tid + i * NTHREADS;
+      st_raw16(As + (c / CPR) * SK + (c % CPR) * VEC, ra[i]);
+    }
+  } else {  // last row tile: rows past M are zero
+#pragma unroll
+    for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
+      const int c = tid + i * NTHREADS;
+      st_raw16(As + (c / CPR) * SK + (c % CPR) * VEC, c / CPR < rows_left ? ra[i] : zero_raw16());
+    }
   }
 #pragma unroll
   for (int i = 0; i < BN * CPR / NTHREADS; ++i) {
@@ -166,22 +179,45 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   };
   if constexpr (EPI == EPI_ACCUM) load_old(0);
 
-  u32x4 ra[BM * CPR / NTHREADS], rb[BN * CPR / NTHREADS];
+  // Register-staged k tiles, NPF of them in flight: at step kt the tiles
+  // kt+1 .. kt+NPF are loading into register slots while tile kt is in LDS.
+  // Two slots for the long-k (d_model) projection of bf16 rows, which waits
+  // on HBM; one elsewhere (the accumulating GEMM has only a few k tiles).
+  constexpr int NPF = (sizeof(T) == 2 && EPI == EPI_HEADS) ? 2 : 1;
+  constexpr int RA = BM * CPR / NTHREADS, RB = BN * CPR / NTHREADS;
+  u32x4 ra[NPF][RA], rb[NPF][RB];
   const int64_t nk = p.K / BK;
-  nt_load_tile<T, BN, G>(p, bptr, ldb, m0, nrow0, 0, ra, rb);
-  nt_store_tile<T, BN, G>(As, Bs, ra, rb);
+#pragma unroll
+  for (int i = 0; i < NPF; ++i)
+    nt_load_tile<T, BN, G>(p, bptr, ldb, m0, nrow0, min((int64_t)i, nk - 1) * BK, ra[i], rb[i]);
+  nt_store_tile<T, BN, G>(As, Bs, ra[0], rb[0], p.M - m0);
   lds_barrier();
-  for (int64_t kt = 0; kt < nk; ++kt) {
+  auto step = [&](auto slot_c, int64_t kt) {
+    constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % NPF;
     const int buf = (int)(kt & 1);
-    if (kt + 1 < nk) nt_load_tile<T, BN, G>(p, bptr, ldb, m0, nrow0, (kt + 1) * BK, ra, rb);
-    // LDS holds [A0][A1][B0][B1]
+    // With several slots, past the end the last tile is loaded again: every
+    // step issues the same loads, so the wait before a slot's store counts
+    // exactly the younger slots.
+    if (NPF > 1 || kt + 1 < nk)
+      nt_load_tile<T, BN, G>(p, bptr, ldb, m0, nrow0, min(kt + NPF, nk - 1) * BK, ra[SLOT], rb[SLOT]);
     const T* Ab = As + buf * BM * SK;
     const T* Bb = Bs + buf * BN * SK;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) mma_tile_step<T, BN>(Ab, Bb, SK, ks, wm, wn, acc);
-    if (kt + 1 < nk) nt_store_tile<T, BN, G>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra, rb);
+    if (NPF > 1 || kt + 1 < nk)
+      nt_store_tile<T, BN, G>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra[NEXT], rb[NEXT], p.M - m0);
     lds_barrier();
+  };
+  int64_t kt = 0;
+  for (; kt + NPF <= nk; kt += NPF) {
+    step(std::integral_constant<int, 0>(), kt);
+    if constexpr (NPF > 1) step(std::integral_constant<int, 1>(), kt + 1);
+    if constexpr (NPF > 2) step(std::integral_constant<int, 2>(), kt + 2);
   }
+  if constexpr (NPF > 1)
+    if (kt < nk) step(std::integral_constant<int, 0>(), kt);
+  if constexpr (NPF > 2)
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>(), kt + 1);
 
   // Epilogue in two passes of EPI_ROWS tile rows through Cs[EPI_ROWS][BN + 4].
   float* Cs = reinterpret_cast<float*>(smem);
@@ -416,6 +452,9 @@ hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
   const int64_t mt = (epi == EPI_HEADS ? p.Np : p.M + BM - 1) / BM;
   const int64_t grid = mt * (p.N / bn);
   if (grid <= 0) return hipSuccess;
+  // the k loop reads whole k tiles and clamps rows to M-1
+  const int bk = (epi == EPI_ACCUM ? nt_kb<EPI_ACCUM>() : nt_kb<EPI_HEADS>()) / (int)sizeof(T);
+  if (p.M <= 0 || p.K <= 0 || p.K % bk) return hipErrorInvalidValue;
   if (epi == EPI_ACCUM && bn == 128)
     hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_ACCUM>), dim3(grid), dim3(NTHREADS), 0, s, p);
   else if (epi == EPI_ACCUM && bn == 64)
