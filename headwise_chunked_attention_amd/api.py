@@ -47,6 +47,9 @@ def load():
                                    vp, vp, vp, vp, vp, vp, vp, flt, vp, vp, vp,
                                    vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.upipe_attn_bwd.restype = i32
+    lib.upipe_choose_chunk_heads.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32, sz,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.upipe_choose_chunk_heads.restype = i32
     lib.upipe_strerror.argtypes = [i32]
     lib.upipe_strerror.restype = ctypes.c_char_p
     lib.upipe_version.argtypes = []
@@ -85,6 +88,21 @@ def workspace_bytes(n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, chunk_he
     return int(load().upipe_attn_workspace_bytes(int(n_tokens), int(d_model), int(n_q_heads),
                                                   int(n_kv_heads), int(head_dim), int(chunk_heads),
                                                   int(bool(qk_norm)), dtype_code(dtype), int(bool(backward))))
+
+
+def choose_chunk_heads(n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, qk_norm, dtype, backward,
+                       budget_bytes) -> tuple[int, int]:
+    """Largest accepted chunk_heads whose workspace fits budget_bytes, and that workspace.
+
+    Raises UpipeError (code UPIPE_ERR_WORKSPACE) when not even one head per chunk fits.
+    """
+    ws = ctypes.c_size_t(0)
+    c = int(load().upipe_choose_chunk_heads(int(n_tokens), int(d_model), int(n_q_heads), int(n_kv_heads),
+                                            int(head_dim), int(bool(qk_norm)), dtype_code(dtype),
+                                            int(bool(backward)), int(budget_bytes), ctypes.byref(ws)))
+    if c < 0:
+        raise UpipeError(c, "upipe_choose_chunk_heads")
+    return c, int(ws.value)
 
 
 def _ptr(t):

@@ -543,6 +543,26 @@ size_t upipe_attn_workspace_bytes(int64_t n_tokens, int64_t d_model, int n_q_hea
   return make_plan(s, backward != 0).total;
 }
 
+int upipe_choose_chunk_heads(int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads, int head_dim,
+                             int qk_norm, upipe_dtype_t dtype, int backward, size_t budget_bytes,
+                             size_t* ws_bytes) {
+  Shape s;
+  // chunk_heads = 1 is a valid chunking for every accepted shape, so this
+  // reports exactly the shape errors the entry points would
+  const int rc = check_shape(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, 1, &s);
+  if (rc) return rc;
+  for (int c = n_q_heads; c >= 1; --c) {
+    if (check_shape(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, c, &s)) continue;
+    s.norm = qk_norm != 0;
+    const size_t need = make_plan(s, backward != 0).total;
+    if (need <= budget_bytes) {
+      if (ws_bytes) *ws_bytes = need;
+      return c;
+    }
+  }
+  return UPIPE_ERR_WORKSPACE;
+}
+
 int upipe_attn_fwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
                    int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
                    const void* wk, const void* wv, const void* wo, const void* q_norm_w,

@@ -88,6 +88,27 @@ size_t upipe_attn_workspace_bytes(int64_t n_tokens, int64_t d_model, int n_q_hea
                                   int qk_norm, upipe_dtype_t dtype, int backward);
 
 /*
+ * Chunk-size chooser: the largest chunk_heads whose workspace fits in
+ * budget_bytes. A larger chunk holds more heads at once, so it needs more
+ * memory and runs a little faster (the trade-off reported in the talk's
+ * results: memeeeeeex.com article, section "結果と教訓"; liquidgold.cc notes,
+ * results part); the largest chunk that fits is therefore the pick.
+ * Candidates are exactly the chunk sizes the entry points accept for these
+ * sizes (divisors of n_q_heads that divide or are multiples of
+ * G = n_q_heads/n_kv_heads). The size compared with the budget is the
+ * backward's workspace when backward != 0 (it is the larger of the two),
+ * else the forward's. Pure host arithmetic, no HIP call.
+ *   ws_bytes: if non-NULL, receives upipe_attn_workspace_bytes of the choice
+ * Returns the chosen chunk_heads (>= 1); UPIPE_ERR_WORKSPACE when not even
+ * chunk_heads = 1 fits; or the error code the entry points give for these
+ * sizes (UPIPE_ERR_INVALID_ARG, UPIPE_ERR_UNSUPPORTED). *ws_bytes is left
+ * untouched on error.
+ */
+int upipe_choose_chunk_heads(int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
+                             int head_dim, int qk_norm, upipe_dtype_t dtype, int backward,
+                             size_t budget_bytes, size_t* ws_bytes);
+
+/*
  * Forward pass: y = attention layer(x) over the share, and lse for backward.
  * Chunks of chunk_heads query heads run in order; each projects its Q (the
  * first chunk of a kv group also projects that group's K and V), runs causal

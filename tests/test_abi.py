@@ -17,8 +17,9 @@ def lib():
 
 def test_exports_every_header_symbol(lib):
     names = api.header_symbols()
-    assert set(names) == {"upipe_attn_workspace_bytes", "upipe_attn_fwd", "upipe_attn_bwd",
-                          "upipe_strerror", "upipe_version", "upipe_profile_start", "upipe_profile_stop"}
+    assert set(names) == {"upipe_attn_workspace_bytes", "upipe_choose_chunk_heads", "upipe_attn_fwd",
+                          "upipe_attn_bwd", "upipe_strerror", "upipe_version", "upipe_profile_start",
+                          "upipe_profile_stop"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.upipe_version() == 100
@@ -81,6 +82,61 @@ def _fwd(lib, **kw):
     return lib.upipe_attn_fwd(a["dtype"], a["N"], a["D"], a["hq"], a["hkv"], a["d"], a["theta"], a["C"],
                               a["x"], a["wq"], a["wk"], a["wv"], a["wo"], a["qn"], a["kn"], a["eps"],
                               a["y"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def _valid_chunks(hq, hkv):
+    G = hq // hkv
+    return [c for c in range(1, hq + 1) if hq % c == 0 and (c % G == 0 or G % c == 0)]
+
+
+@pytest.mark.parametrize("N,D,hq,hkv,d,norm", [(2048, 512, 8, 2, 64, False), (131072, 4096, 4, 1, 128, False),
+                                               (524288, 5120, 8, 1, 128, True), (1000, 128, 12, 3, 128, False),
+                                               (4096, 256, 6, 6, 64, True)])
+def test_chunk_chooser_picks_largest_fitting_chunk(N, D, hq, hkv, d, norm):
+    # brute force over every accepted chunk size, each priced by the documented layout
+    for dt, es in (("fp32", 4), ("bf16", 2)):
+        for bwd in (False, True):
+            sizes = {c: _expected_ws(N, D, hq, hkv, d, c, norm, es, bwd) for c in _valid_chunks(hq, hkv)}
+            budgets = {0, min(sizes.values()) - 1, max(sizes.values()) * 10}
+            for v in sizes.values():
+                budgets |= {v - 1, v, v + 1}
+            for b in sorted(x for x in budgets if x >= 0):
+                fits = [c for c, v in sizes.items() if v <= b]
+                if not fits:
+                    with pytest.raises(api.UpipeError) as e:
+                        api.choose_chunk_heads(N, D, hq, hkv, d, norm, dt, bwd, b)
+                    assert e.value.code == WORKSPACE
+                    continue
+                c, ws = api.choose_chunk_heads(N, D, hq, hkv, d, norm, dt, bwd, b)
+                assert (c, ws) == (max(fits), sizes[max(fits)]), (dt, bwd, b)
+
+
+def test_chunk_chooser_at_the_llama_and_qwen_shares():
+    gb = 10 ** 9
+    # Llama3-8B share at 131072 tokens, backward 0.37 / 0.54 / 0.88 GB for C = 1 / 2 / 4
+    assert api.choose_chunk_heads(131072, 4096, 4, 1, 128, False, "bf16", True, 0.5 * gb)[0] == 1
+    assert api.choose_chunk_heads(131072, 4096, 4, 1, 128, False, "bf16", True, 0.6 * gb)[0] == 2
+    assert api.choose_chunk_heads(131072, 4096, 4, 1, 128, False, "bf16", True, 288 * gb)[0] == 4
+    # 5242880 tokens: the forward at C = 1 takes 5.37 GB, so a 5 GB budget fits nothing
+    with pytest.raises(api.UpipeError):
+        api.choose_chunk_heads(5242880, 4096, 4, 1, 128, False, "bf16", False, 5 * gb)
+    # Qwen3-32B share at 524288 tokens with q/k norm: forward 0.54 / 0.81 / 1.34 / 2.42 GB
+    assert api.choose_chunk_heads(524288, 5120, 8, 1, 128, True, "bf16", False, 2 * gb)[0] == 4
+
+
+def test_chunk_chooser_reports_shape_errors(lib):
+    ws = ctypes.c_size_t(12345)
+    big = 1 << 62
+    # (dtype, N, D, hq, hkv, d) -> the entry points' code
+    for args, code in [((1, 0, 512, 8, 2, 64), INVALID), ((1, 2048, 512, 8, 3, 64), INVALID),
+                       ((1, 2048, 512, 8, 2, 96), UNSUPPORTED), ((1, 2048, 500, 8, 2, 64), UNSUPPORTED),
+                       ((7, 2048, 512, 8, 2, 64), INVALID)]:
+        dt, N, D, hq, hkv, d = args
+        rc = lib.upipe_choose_chunk_heads(N, D, hq, hkv, d, 0, dt, 1, big, ctypes.byref(ws))
+        assert rc == code, args
+        assert ws.value == 12345  # untouched on error
+    # a NULL ws_bytes is allowed
+    assert lib.upipe_choose_chunk_heads(2048, 512, 8, 2, 64, 0, 1, 1, big, None) == 8
 
 
 def test_fwd_validation_errors(lib):
