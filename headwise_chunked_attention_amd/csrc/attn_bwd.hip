@@ -128,6 +128,7 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   constexpr bool DMA = L::SWZ;  // bf16: Q/dO tiles by direct global -> LDS loads
   u32x4 rq[DMA ? 1 : G::PER], rdo[DMA ? 1 : G::PER];
   float rl = 0.f, rd = 0.f;
+  bool rvalid = false;
   // (head, query tile) of a step, without 64-bit division in the loop
   auto prefetch = [&](int hh, int64_t q0, int dst) {
     if constexpr (DMA) {
@@ -143,10 +144,12 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       load_rows<T, D, G>(p.dout + (int64_t)hh * p.Np * D, q0, rdo);
     }
     if (tid < BQ) {
+      // raw values now, used at the commit: nothing here waits for the loads
       const int64_t q = q0 + tid;
-      // negated: they start the S and dP accumulators
-      rl = (q < p.N) ? -p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : -INFINITY;
-      rd = (q < p.N) ? -p.delta[(int64_t)hh * p.Np + q] : 0.f;
+      const int64_t qc = q < p.N ? q : p.N - 1;
+      rl = p.lse[(int64_t)hh * p.lse_stride + qc];
+      rd = p.delta[(int64_t)hh * p.Np + qc];
+      rvalid = q < p.N;
     }
   };
   auto commit = [&](int b) {
@@ -157,8 +160,9 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       store_rows<T, D, G>(sm + G::BUF_OFF + b * G::BUF_ELEMS + L::ELEMS(BQ), rdo);
     }
     if (tid < BQ) {
-      stat[b * 2 * BQ + tid] = rl;
-      stat[b * 2 * BQ + BQ + tid] = rd;
+      // negated: they start the S and dP accumulators; rows past the end get P = 0
+      stat[b * 2 * BQ + tid] = rvalid ? -rl * 1.4426950408889634f : -INFINITY;
+      stat[b * 2 * BQ + BQ + tid] = rvalid ? -rd : 0.f;
     }
   };
 
