@@ -9,9 +9,11 @@ seeded, generated on the host and resident in HBM before timing starts.
 
 Printed (one JSON line): model TFLOP/s of the step at the headline chunk size
 (chunk_heads=1 unless --chunk is given) and its fraction of the bf16 dense
-MFMA peak; the workspace bytes per chunk size; a chunk-size sweep; per-kernel
-event timings; the roofline entry of the dominant kernel (attention
-backward); and the CPU fp64 oracle timed on a bounded sample.
+MFMA peak; median and minimum step, forward and backward times; the
+attention-core and hardware (recompute included) rates; the workspace bytes
+per chunk size; a chunk-size sweep; per-kernel event timings (from a second,
+profiled run of the same steps); the roofline entry of the dominant kernel
+(attention backward); and the CPU fp64 oracle timed on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--chunk 1] [--no-sweep] [--no-cpu]
 """
@@ -39,7 +41,7 @@ KERNEL_NAMES = {"attn_fwd": "attn_fwd_kernel<bf16,128,0>", "attn_recompute": "at
 # HBM bytes per launch of a kernel from rocprofv3 counters (FETCH_SIZE +
 # WRITE_SIZE, scaled by a plain copy of known size), measured on the kernel as
 # it now stands; absent (null) until measured again after a kernel change.
-TRAFFIC_BYTES = {"attn_bwd_dkdv": 3.821e9}  # fetch 3.687 GB + write 0.134 GB
+TRAFFIC_BYTES = {"attn_bwd_dkdv": 3.788e9}  # fetch 3.654 GB + write 0.134 GB
 
 
 def model_flops(N, D, hq, hkv, d):
@@ -48,6 +50,19 @@ def model_flops(N, D, hq, hkv, d):
     (fwd 2*N*D*d per head for q, k, v, o; bwd twice that)."""
     pairs = N * (N + 1) / 2
     return 14.0 * d * hq * pairs + 12.0 * N * D * d * (hq + hkv)
+
+
+def attn_core_flops(N, hq, d):
+    """The attention-core part of model_flops: 14*d per visible (query, key) pair per q head."""
+    return 14.0 * d * hq * N * (N + 1) / 2
+
+
+def hardware_flops(N, D, hq, hkv, d):
+    """Flops the step actually executes: model flops plus the backward's recompute
+    of O from the saved LSE (4*d per pair per q head) and of the projections
+    (2*N*D*d per q head and per k/v head)."""
+    pairs = N * (N + 1) / 2
+    return model_flops(N, D, hq, hkv, d) + 4.0 * d * hq * pairs + 2.0 * N * D * d * (hq + 2 * hkv)
 
 
 def cpu_baseline(w, sample_n=8192):
@@ -138,36 +153,51 @@ def main():
                torch.empty(t["wv"].shape, dtype=f32, device=dev), torch.empty(t["wo"].shape, dtype=f32, device=dev),
                None, None)
 
-        def step():
+        def fwd():
             api.attn_fwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], y=y, lse=lse, workspace=ws, **kw)
+
+        def bwd():
             api.attn_bwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], t["dy"], lse, out=out, workspace=ws, **kw)
 
         for _ in range(warmup):
-            step()
+            fwd()
+            bwd()
         torch.cuda.synchronize()
         mem0 = torch.cuda.memory_allocated(dev)
         free0, _ = torch.cuda.mem_get_info(dev)
         if profile:
             api.profile_start()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
+        # events before each step, between its fwd and bwd, and after the last step
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        ev_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(steps):
-            step()
-        ev1.record(stream)
+        for i in range(steps):
+            evs[i][0].record(stream)
+            fwd()
+            evs[i][1].record(stream)
+            bwd()
+        ev_end.record(stream)
         torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / steps
+        ms = evs[0][0].elapsed_time(ev_end) / steps
+        t_f = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
+        t_b = [evs[i][1].elapsed_time(evs[i + 1][0] if i + 1 < steps else ev_end) for i in range(steps)]
+        t_s = [a + b for a, b in zip(t_f, t_b)]
         prof = api.profile_stop() if profile else None
         free1, _ = torch.cuda.mem_get_info(dev)
         assert torch.cuda.memory_allocated(dev) == mem0, "the library must not allocate"
         res = {"chunk_heads": C, "ms_per_step": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+               "step_ms": {"median": float(np.median(t_s)), "min": float(np.min(t_s))},
+               "fwd_ms": {"median": float(np.median(t_f)), "min": float(np.min(t_f))},
+               "bwd_ms": {"median": float(np.median(t_b)), "min": float(np.min(t_b))},
                "ws_fwd_gb": ws_f / 1e9, "ws_bwd_gb": ws_b / 1e9, "hidden_alloc_bytes": int(free0 - free1)}
         del ws, y, lse, out
         torch.cuda.empty_cache()
         return res, prof
 
-    head, prof = run_chunk(args.chunk, args.steps, args.warmup, profile=True)
+    # the headline run carries no per-kernel events; a second run of the same
+    # steps, with the library's per-kernel timing on, gives the kernel table
+    head, _ = run_chunk(args.chunk, args.steps, args.warmup, profile=False)
+    _, prof = run_chunk(args.chunk, args.steps, 1, profile=True)
     sweep = []
     if not args.no_sweep:
         for C in w["chunks"]:
@@ -185,6 +215,11 @@ def main():
             kernels[k] = {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["launches"] / args.steps,
                           "avg_launch_ms": v["ms"] / v["launches"],
                           "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None}
+    # attention-core rate: the core's model flops over the time of the kernels
+    # that do them (forward attention, dK/dV and dQ; the recompute is extra work)
+    core_ms = sum(prof[k]["ms"] for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq")) / args.steps
+    core_tflops = attn_core_flops(N, hq, d) / (core_ms * 1e-3) / 1e12
+    hw_tflops = hardware_flops(N, D, hq, hkv, d) / (head["ms_per_step"] * 1e-3) / 1e12
     # dominant kernel of the step: the attention kernel kind with the most time
     dom = max(("attn_fwd", "attn_recompute", "attn_bwd_dkdv", "attn_bwd_dq"), key=lambda k: prof[k]["ms"])
     ab = prof[dom]
@@ -220,6 +255,11 @@ def main():
                    "parallelism": "one GPU's Ulysses head share (no collectives)"},
         "frac_of_peak": head["tflops"] / PEAK_BF16_TFLOPS,
         "model_flops_per_step": fl,
+        "step_ms": head["step_ms"],
+        "fwd_ms": head["fwd_ms"],
+        "bwd_ms": head["bwd_ms"],
+        "attention_core_tflops": core_tflops,
+        "hardware_tflops": hw_tflops,
         "workspace_gb": {"fwd": head["ws_fwd_gb"], "bwd": head["ws_bwd_gb"]},
         "chunk_sweep": sweep,
         "kernels": kernels,
