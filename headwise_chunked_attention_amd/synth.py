@@ -7,7 +7,7 @@ input streams.
 
 Recipe (stated once, used everywhere):
   * every tensor has an integer "tensor id": x 0, Wq 1, Wk 2, Wv 3, Wo 4,
-    dY 5, q-norm gamma 6, k-norm gamma 7;
+    dY 5, q-norm gamma 6, k-norm gamma 7, MLP gate/up/down weights 8/9/10;
   * a 2-D tensor is drawn in blocks of ``ROW_BLOCK`` rows; block ``b`` of
     tensor ``t`` under run seed ``s`` uses
     ``numpy.random.default_rng(SeedSequence([s, t, b]))`` and draws
@@ -28,7 +28,8 @@ import numpy as np
 ROW_BLOCK = 8192
 GEN_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
-TENSOR_IDS = {"x": 0, "wq": 1, "wk": 2, "wv": 3, "wo": 4, "dy": 5, "q_norm": 6, "k_norm": 7}
+TENSOR_IDS = {"x": 0, "wq": 1, "wk": 2, "wv": 3, "wo": 4, "dy": 5, "q_norm": 6, "k_norm": 7,
+              "wg": 8, "wu": 9, "wd": 10}
 
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
@@ -146,3 +147,20 @@ class LayerInputs:
         else:
             self.q_norm = gen_gamma("q_norm", d, qk_norm, dtype, seed)
             self.k_norm = gen_gamma("k_norm", d, qk_norm, dtype, seed)
+
+
+class MlpInputs:
+    """All inputs of one gated-SiLU MLP problem, as float32 host arrays.
+
+    x, dy ``[N][D]`` (std 1); wg, wu ``[F][D]``, wd ``[D][F]`` (std ``w_std``).
+    """
+
+    def __init__(self, n_tokens: int, d_model: int, d_ff: int, dtype: str, seed: int = 0,
+                 w_std: float = 0.02, with_x: bool = True, with_dy: bool = True):
+        self.n_tokens, self.d_model, self.d_ff, self.dtype, self.seed = n_tokens, d_model, d_ff, dtype, seed
+        N, D, F = n_tokens, d_model, d_ff
+        self.x = gen_rows("x", N, D, 1.0, dtype, seed) if with_x else None
+        self.dy = gen_rows("dy", N, D, 1.0, dtype, seed) if with_dy else None
+        self.wg = gen_rows("wg", F, D, w_std, dtype, seed)
+        self.wu = gen_rows("wu", F, D, w_std, dtype, seed)
+        self.wd = gen_rows("wd", D, F, w_std, dtype, seed)

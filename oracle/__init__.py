@@ -1,4 +1,5 @@
-"""CPU fp64 oracle for headwise-chunked causal RoPE/GQA attention.
+"""CPU fp64 oracle for headwise-chunked causal RoPE/GQA attention and the
+sequence-tiled gated-SiLU MLP.
 
 TEST INFRASTRUCTURE ONLY. Nothing in the product package imports this; only
 ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -17,4 +18,13 @@ from .attention import (  # noqa: F401
     layer_fwd_rows,
     layer_bwd_tail_dx,
     chunk_plan,
+)
+from .mlp import (  # noqa: F401
+    sigmoid,
+    silu,
+    silu_grad,
+    mlp_fwd,
+    mlp_bwd,
+    mlp_rows,
+    mlp_dx_rows,
 )
