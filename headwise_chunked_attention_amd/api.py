@@ -50,6 +50,12 @@ def load():
     lib.upipe_choose_chunk_heads.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32, sz,
                                              ctypes.POINTER(ctypes.c_size_t)]
     lib.upipe_choose_chunk_heads.restype = i32
+    lib.upipe_mlp_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.upipe_mlp_workspace_bytes.restype = sz
+    lib.upipe_mlp_fwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.upipe_mlp_fwd.restype = i32
+    lib.upipe_mlp_bwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.upipe_mlp_bwd.restype = i32
     lib.upipe_strerror.argtypes = [i32]
     lib.upipe_strerror.restype = ctypes.c_char_p
     lib.upipe_version.argtypes = []
@@ -219,7 +225,64 @@ def attn_bwd(x, wq, wk, wv, wo, dy, lse, *, n_q_heads, n_kv_heads, head_dim, rop
 
 
 KERNEL_KINDS = ("projection", "out_gemm", "attn_fwd", "attn_recompute", "attn_bwd_dkdv", "attn_bwd_dq", "wgrad",
-                "other")
+                "other", "mlp_gemm", "mlp_wgrad")
+
+
+def mlp_workspace_bytes(n_tokens, d_model, d_ff, tile_tokens, dtype, backward) -> int:
+    return int(load().upipe_mlp_workspace_bytes(int(n_tokens), int(d_model), int(d_ff), int(tile_tokens),
+                                                 dtype_code(dtype), int(bool(backward))))
+
+
+def mlp_fwd(x, w_gate, w_up, w_down, *, tile_tokens, y=None, workspace=None, stream=None):
+    """y = (silu(x Wg^T) * (x Wu^T)) Wd^T, tile_tokens rows at a time (upipe_mlp_fwd)."""
+    lib = load()
+    dev, dt = x.device, x.dtype
+    N, D = x.shape
+    F = w_gate.shape[0]
+    _check(x, "x", dt, (N, D), dev)
+    _check(w_gate, "w_gate", dt, (F, D), dev)
+    _check(w_up, "w_up", dt, (F, D), dev)
+    _check(w_down, "w_down", dt, (D, F), dev)
+    if y is None:
+        y = torch.empty((N, D), dtype=dt, device=dev)
+    _check(y, "y", dt, (N, D), dev)
+    if workspace is None:
+        workspace = alloc_workspace(mlp_workspace_bytes(N, D, F, tile_tokens, dt, False), dev)
+    rc = lib.upipe_mlp_fwd(dtype_code(dt), N, D, F, int(tile_tokens), _ptr(x), _ptr(w_gate), _ptr(w_up),
+                           _ptr(w_down), _ptr(y), _ptr(workspace), workspace.numel(), _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_mlp_fwd")
+    return y
+
+
+def mlp_bwd(x, w_gate, w_up, w_down, dy, *, tile_tokens, out=None, workspace=None, stream=None):
+    """(dx, dw_gate, dw_up, dw_down) of ``mlp_fwd`` for upstream gradient dy (upipe_mlp_bwd)."""
+    lib = load()
+    dev, dt = x.device, x.dtype
+    N, D = x.shape
+    F = w_gate.shape[0]
+    _check(x, "x", dt, (N, D), dev)
+    _check(w_gate, "w_gate", dt, (F, D), dev)
+    _check(w_up, "w_up", dt, (F, D), dev)
+    _check(w_down, "w_down", dt, (D, F), dev)
+    _check(dy, "dy", dt, (N, D), dev)
+    f32 = torch.float32
+    if out is None:
+        out = (torch.empty((N, D), dtype=dt, device=dev), torch.empty((F, D), dtype=f32, device=dev),
+               torch.empty((F, D), dtype=f32, device=dev), torch.empty((D, F), dtype=f32, device=dev))
+    dx, dwg, dwu, dwd = out
+    _check(dx, "dx", dt, (N, D), dev)
+    _check(dwg, "dw_gate", f32, (F, D), dev)
+    _check(dwu, "dw_up", f32, (F, D), dev)
+    _check(dwd, "dw_down", f32, (D, F), dev)
+    if workspace is None:
+        workspace = alloc_workspace(mlp_workspace_bytes(N, D, F, tile_tokens, dt, True), dev)
+    rc = lib.upipe_mlp_bwd(dtype_code(dt), N, D, F, int(tile_tokens), _ptr(x), _ptr(w_gate), _ptr(w_up),
+                           _ptr(w_down), _ptr(dy), _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd), _ptr(workspace),
+                           workspace.numel(), _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_mlp_bwd")
+    return dx, dwg, dwu, dwd
 
 
 def profile_start():

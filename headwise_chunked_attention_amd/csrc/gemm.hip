@@ -38,6 +38,8 @@ template <typename T, int KB = 128> struct GemmGeo {
 // keep their LDS at 40 KB, so three workgroups share a CU. The projections
 // (K = d_model) keep 128-byte rows (fewer k steps and barriers).
 template <int EPI> constexpr int nt_kb() { return EPI == EPI_ACCUM ? 64 : 128; }
+// gate/up halves of a gated B tile
+template <int EPI> constexpr bool nt_gated() { return EPI == EPI_GLU; }
 constexpr int EPI_ROWS = BM / 2;  // rows per epilogue pass
 
 template <typename T, int BN, int EPI>
@@ -85,8 +87,10 @@ DEV void acc_to_lds(float* Cs, int row0, int nrows, int wm, int wn, const f32x16
           Cs[(wm * 64 + mt * 32 + 8 * i + 4 * h + j - row0) * SC + col0 + nt * 32] = acc[mt][nt][4 * i + j];
 }
 
+// B rows 0 .. BN/2-1 come from blo, rows BN/2 .. BN-1 from bhi (the same
+// pointer plus BN/2 rows, except for a gated tile).
 template <typename T, int BN, class G>
-DEV void nt_load_tile(const GemmNT<T>& p, const T* bptr, int64_t ldb, int64_t m0, int64_t nrow0,
+DEV void nt_load_tile(const GemmNT<T>& p, const T* blo, const T* bhi, int64_t ldb, int64_t m0,
                       int64_t k0, u32x4 (&ra)[BM * G::CPR / NTHREADS], u32x4 (&rb)[BN * G::CPR / NTHREADS]) {
   constexpr int VEC = G::VEC, CPR = G::CPR;
   const int tid = threadIdx.x;
@@ -104,7 +108,8 @@ DEV void nt_load_tile(const GemmNT<T>& p, const T* bptr, int64_t ldb, int64_t m0
   for (int i = 0; i < BN * CPR / NTHREADS; ++i) {
     const int c = tid + i * NTHREADS;
     const int row = c / CPR, cc = c % CPR;
-    rb[i] = ld_raw16(bptr + (nrow0 + row) * ldb + k0 + cc * VEC);
+    const T* base = row < BN / 2 ? blo + row * ldb : bhi + (row - BN / 2) * ldb;
+    rb[i] = ld_raw16(base + k0 + cc * VEC);
   }
 }
 
@@ -149,9 +154,18 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   int seg = 0;
   while (seg + 1 < p.nseg && n0 >= p.seg_end[seg]) ++seg;
   const int64_t seg_begin = seg ? p.seg_end[seg - 1] : 0;
-  const T* bptr = p.b[seg];
   const int64_t ldb = p.ldb[seg];
   const int64_t nrow0 = n0 - seg_begin;
+  const T* blo;
+  const T* bhi;
+  if constexpr (nt_gated<EPI>()) {
+    static_assert(BN == 128, "gated tiles hold 64 gate and 64 up rows");
+    blo = p.b[0] + (n0 / 2) * ldb;
+    bhi = p.b[1] + (n0 / 2) * ldb;
+  } else {
+    blo = p.b[seg] + nrow0 * ldb;
+    bhi = blo + (BN / 2) * ldb;
+  }
 
   const int w = wave_id();
   const int wm = w >> 1, wn = w & 1;
@@ -183,13 +197,13 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   // kt+1 .. kt+NPF are loading into register slots while tile kt is in LDS.
   // Two slots for the long-k (d_model) projection of bf16 rows, which waits
   // on HBM; one elsewhere (the accumulating GEMM has only a few k tiles).
-  constexpr int NPF = (sizeof(T) == 2 && EPI == EPI_HEADS) ? 2 : 1;
+  constexpr int NPF = (sizeof(T) == 2 && EPI != EPI_ACCUM) ? 2 : 1;
   constexpr int RA = BM * CPR / NTHREADS, RB = BN * CPR / NTHREADS;
   u32x4 ra[NPF][RA], rb[NPF][RB];
   const int64_t nk = p.K / BK;
 #pragma unroll
   for (int i = 0; i < NPF; ++i)
-    nt_load_tile<T, BN, G>(p, bptr, ldb, m0, nrow0, min((int64_t)i, nk - 1) * BK, ra[i], rb[i]);
+    nt_load_tile<T, BN, G>(p, blo, bhi, ldb, m0, min((int64_t)i, nk - 1) * BK, ra[i], rb[i]);
   nt_store_tile<T, BN, G>(As, Bs, ra[0], rb[0], p.M - m0);
   lds_barrier();
   auto step = [&](auto slot_c, int64_t kt) {
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
     // step issues the same loads, so the wait before a slot's store counts
     // exactly the younger slots.
     if (NPF > 1 || kt + 1 < nk)
-      nt_load_tile<T, BN, G>(p, bptr, ldb, m0, nrow0, min(kt + NPF, nk - 1) * BK, ra[SLOT], rb[SLOT]);
+      nt_load_tile<T, BN, G>(p, blo, bhi, ldb, m0, min(kt + NPF, nk - 1) * BK, ra[SLOT], rb[SLOT]);
     const T* Ab = As + buf * BM * SK;
     const T* Bb = Bs + buf * BN * SK;
 #pragma unroll
@@ -228,7 +242,72 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
     acc_to_lds<BN>(Cs, r0, EPI_ROWS, wm, wn, acc);
     lds_barrier();
 
-    if constexpr (EPI == EPI_ACCUM) {
+    if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+      for (int i = 0; i < EPI_ROWS * BN / VEC / NTHREADS; ++i) {
+        const int c = tid + i * NTHREADS;
+        const int row = c / (BN / VEC), cv = c % (BN / VEC);
+        const int64_t m = m0 + r0 + row;
+        if (m >= p.M) continue;
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+        st16_f<T>(p.c + m * p.ldc + n0 + cv * VEC, v);
+      }
+    } else if constexpr (EPI == EPI_GLU) {
+      const GluOut<T>& g = p.glu;
+      if (g.a) {  // a = silu(h) * u for the tile's 64 features
+        for (int c = tid; c < EPI_ROWS * (BN / 2) / VEC; c += NTHREADS) {
+          const int row = c / (BN / 2 / VEC), cv = c % (BN / 2 / VEC);
+          const int64_t m = m0 + r0 + row;
+          if (m >= p.M) continue;
+          float v[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float hh = Cs[row * SC + cv * VEC + e], uu = Cs[row * SC + BN / 2 + cv * VEC + e];
+            v[e] = hh / (1.0f + expf(-hh)) * uu;
+          }
+          st16_f<T>(g.a + m * g.ldf + n0 / 2 + cv * VEC, v);
+        }
+      }
+      if (g.hu) {  // h and u as computed, in the tile's own column order
+        for (int c = tid; c < EPI_ROWS * BN / VEC; c += NTHREADS) {
+          const int row = c / (BN / VEC), cv = c % (BN / VEC);
+          const int64_t m = m0 + r0 + row;
+          if (m >= p.M) continue;
+          float v[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+          st16_f<T>(g.hu + m * 2 * g.ldf + n0 + cv * VEC, v);
+        }
+      }
+    } else if constexpr (EPI == EPI_GLU_BWD) {
+      // C = da over features n0 .. n0+BN-1; h, u of feature f sit at columns
+      // 128 (f / 64) + f % 64 and that + 64 of hu
+      const GluOut<T>& g = p.glu;
+      for (int c = tid; c < EPI_ROWS * BN / VEC; c += NTHREADS) {
+        const int row = c / (BN / VEC), cv = c % (BN / VEC);
+        const int64_t m = m0 + r0 + row;
+        if (m >= p.M) continue;
+        const int64_t f0 = n0 + cv * VEC;
+        const T* hp = g.hu + m * 2 * g.ldf + (f0 / 64) * 128 + f0 % 64;
+        float hh[VEC], uu[VEC], dh[VEC], du[VEC], av[VEC];
+        ld16_f<T>(hp, hh);
+        ld16_f<T>(hp + 64, uu);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float da = Cs[row * SC + cv * VEC + e];
+          const float sg = 1.0f / (1.0f + expf(-hh[e]));
+          const float sh = hh[e] * sg;
+          dh[e] = da * uu[e] * (sg * (1.0f + hh[e] * (1.0f - sg)));
+          du[e] = da * sh;
+          av[e] = sh * uu[e];
+        }
+        st16_f<T>(g.dh + m * g.ldf + f0, dh);
+        st16_f<T>(g.du + m * g.ldf + f0, du);
+        st16_f<T>(g.a + m * g.ldf + f0, av);
+      }
+    } else if constexpr (EPI == EPI_ACCUM) {
       if (pass) load_old(1);
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
@@ -455,7 +534,15 @@ hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
   // the k loop reads whole k tiles and clamps rows to M-1
   const int bk = (epi == EPI_ACCUM ? nt_kb<EPI_ACCUM>() : nt_kb<EPI_HEADS>()) / (int)sizeof(T);
   if (p.M <= 0 || p.K <= 0 || p.K % bk) return hipErrorInvalidValue;
-  if (epi == EPI_ACCUM && bn == 128)
+  if ((epi == EPI_GLU || epi == EPI_GLU_BWD) && (bn != 128 || p.N % 128 || p.glu.ldf % 64))
+    return hipErrorInvalidValue;
+  if (epi == EPI_STORE && bn == 128)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_STORE>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else if (epi == EPI_GLU)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_GLU>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else if (epi == EPI_GLU_BWD)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_GLU_BWD>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else if (epi == EPI_ACCUM && bn == 128)
     hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_ACCUM>), dim3(grid), dim3(NTHREADS), 0, s, p);
   else if (epi == EPI_ACCUM && bn == 64)
     hipLaunchKernelGGL((gemm_nt_kernel<T, 64, EPI_ACCUM>), dim3(grid), dim3(NTHREADS), 0, s, p);

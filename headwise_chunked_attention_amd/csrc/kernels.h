@@ -8,7 +8,7 @@ typedef __bf16 bf16;
 
 namespace upipe {
 
-enum { EPI_ACCUM = 0, EPI_HEADS = 1 };
+enum { EPI_ACCUM = 0, EPI_HEADS = 1, EPI_STORE = 2, EPI_GLU = 3, EPI_GLU_BWD = 4 };
 
 // Where one group of heads produced by a projection GEMM goes. A head is one
 // N-tile of the GEMM (BN == head_dim).
@@ -21,11 +21,31 @@ struct HeadOut {
   float scale;     // multiplies the values stored to rm (after norm and RoPE)
 };
 
+// Gated-SiLU MLP epilogues (BN = 128; F = ldf features).
+// EPI_GLU: the B operand is gated: tile t (128 columns of C) takes rows
+//   64t .. 64t+63 of b[0] (the gate weight) and then the same rows of b[1]
+//   (the up weight), so it holds h and u of the same 64 features. It writes
+//     a[m][64t + j] = silu(h) * u          if a is set (forward), and/or
+//     hu[m][128t + c] = C[m][c]             if hu is set (h block, u block).
+// EPI_GLU_BWD: C = da over features n (ordinary B); reads h, u from hu and
+//   writes dh = da * u * silu'(h), du = da * silu(h), a = silu(h) * u.
+// All rows m < M; a, dh, du have row stride ldf, hu 2 * ldf.
+template <typename T>
+struct GluOut {
+  T* a;
+  T* hu;
+  T* dh;
+  T* du;
+  int64_t ldf;
+};
+
 // C[m][n] = sum_k A(m,k) B(n,k), both operands contiguous along k.
 //   A(m,k) = a + (k / a_kblk) * a_kblk_stride + m * lda + (k % a_kblk)
 //   B(n,k) = b[s] + (n - seg_begin(s)) * ldb[s] + k for the segment s holding n
 // EPI_ACCUM:  c[m * ldc + n] = (accumulate ? c : 0) + C   (rows m < M)
+// EPI_STORE:  c[m * ldc + n] = C (rows m < M); long k (128-byte k rows)
 // EPI_HEADS:  head-wise epilogue per segment (see HeadOut), rows m < Np.
+// EPI_GLU, EPI_GLU_BWD: see GluOut.
 template <typename T>
 struct GemmNT {
   const T* a;
@@ -44,6 +64,7 @@ struct GemmNT {
   int64_t Np;
   float eps;
   double log2_theta;
+  GluOut<T> glu;
 };
 
 // out[m*ldm + n*ldn] += sum_{k in split} A(k,m) B(k,n)   (fp32 atomics)

@@ -17,16 +17,21 @@
 #include <vector>
 
 #include "upipe.h"
+#include "host.h"
 #include "kernels.h"
 
 using namespace upipe;
+using namespace upipe::host;
+
+namespace upipe {
+namespace host {
+Profiler g_prof;
+}  // namespace host
+}  // namespace upipe
 
 namespace {
 
-int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
-
 constexpr int64_t ROW_PAD = 256;   // token rows of per-head buffers are padded to this
-constexpr size_t REGION_ALIGN = 256;
 
 struct Shape {
   int64_t N, D, Np;
@@ -40,15 +45,6 @@ struct Shape {
 struct Plan {
   size_t q, uq, k, v, uk, dout, o, delta, dq_acc, dk_acc, dv_acc, wo_t, wqkv_t;
   size_t total;
-};
-
-struct Carver {
-  size_t off = 0;
-  size_t take(size_t bytes) {
-    const size_t at = off;
-    off += (bytes + REGION_ALIGN - 1) / REGION_ALIGN * REGION_ALIGN;
-    return at;
-  }
 };
 
 Plan make_plan(const Shape& s, bool backward) {
@@ -107,53 +103,8 @@ int check_shape(int dtype, int64_t N, int64_t D, int Hq, int Hkv, int d, int C, 
   return UPIPE_OK;
 }
 
-bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-
-// ---- opt-in per-kernel timing ------------------------------------------
-struct ProfRec {
-  int kind;
-  double flops;
-  hipEvent_t a, b;
-};
-struct Profiler {
-  bool on = false;
-  std::vector<ProfRec> recs;
-  std::vector<hipEvent_t> pool;
-  hipEvent_t get() {
-    if (!pool.empty()) {
-      hipEvent_t e = pool.back();
-      pool.pop_back();
-      return e;
-    }
-    hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    return e;
-  }
-};
-Profiler g_prof;
-
-// Enqueue one kernel through `launch`, bracketed by events when timing is on.
-template <class F>
-hipError_t timed(int kind, double flops, hipStream_t st, F&& launch) {
-  if (!g_prof.on) return launch();
-  hipEvent_t a = g_prof.get(), b = g_prof.get();
-  if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, st);
-  if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(b, st);
-  g_prof.recs.push_back({kind, flops, a, b});
-  return e;
-}
-
 // Visible (query, key) pairs of causal attention over N tokens.
 double causal_pairs(int64_t N) { return 0.5 * (double)N * (double)(N + 1); }
-
-#define HIP_TRY(x)                                 \
-  do {                                             \
-    if ((x) != hipSuccess) return UPIPE_ERR_HIP;   \
-  } while (0)
 
 template <typename T>
 GemmNT<T> gemm_base() {

@@ -147,6 +147,42 @@ int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n
                    void* stream);
 
 /*
+ * Sequence-tiled gated-SiLU MLP, the component next to the attention op in
+ * the talk's memory stack: the element-wise parts of the model (the MLP and
+ * the loss) are tiled along the sequence, so that no intermediate is as long
+ * as the whole sequence ("Road to 5 Million Tokens", talk transcript, the
+ * part after CPU offloading, on Arctic sequence length training;
+ * liquidgold.cc notes, "Progression of Techniques", item 6). The models the
+ * talk trains (Llama 3, Qwen3) use the bias-free gated SiLU MLP:
+ *
+ *   y = (silu(x Wg^T) * (x Wu^T)) Wd^T,   silu(z) = z / (1 + e^-z)
+ *
+ * computed tile_tokens rows at a time through one reused workspace whose
+ * size grows with tile_tokens, not with N. The backward recomputes each
+ * tile's activations from x (activation checkpointing) and adds the tile's
+ * share of every weight gradient.
+ *   x, y, dy, dx  [N][D] io dtype
+ *   w_gate, w_up  [F][D] io dtype (nn.Linear [out][in]); w_down [D][F]
+ *   dw_gate, dw_up [F][D], dw_down [D][F] fp32 (out, overwritten)
+ * Supported: N >= 1; D and F positive multiples of 128; tile_tokens a
+ * positive multiple of 128 (a tile larger than N is one tile). Pointers,
+ * streams, validation and error codes follow the conventions above; the
+ * workspace must hold upipe_mlp_workspace_bytes(..., backward) bytes.
+ */
+size_t upipe_mlp_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                 int64_t tile_tokens, upipe_dtype_t dtype, int backward);
+
+int upipe_mlp_fwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                  int64_t tile_tokens, const void* x, const void* w_gate, const void* w_up,
+                  const void* w_down, void* y, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+int upipe_mlp_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                  int64_t tile_tokens, const void* x, const void* w_gate, const void* w_up,
+                  const void* w_down, const void* dy, void* dx, float* dw_gate, float* dw_up,
+                  float* dw_down, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Optional per-kernel timing (for benchmarks and profilers; off by default).
  * While enabled, every kernel the library enqueues is bracketed by two
  * hipEvents on the caller's stream, and its algorithmic work (flops of the
@@ -167,7 +203,9 @@ enum {
   UPIPE_KERNEL_ATTN_BWD_DQ = 5,     /* attention backward, query-stationary: dQ (6*d per pair) */
   UPIPE_KERNEL_WGRAD = 6,           /* split-K weight-gradient GEMMs */
   UPIPE_KERNEL_OTHER = 7,           /* RoPE/RMSNorm backward, transposes, fills */
-  UPIPE_KERNEL_KINDS = 8
+  UPIPE_KERNEL_MLP_GEMM = 8,        /* MLP products of x, a and dy (gated-SiLU epilogues) and dx */
+  UPIPE_KERNEL_MLP_WGRAD = 9,       /* MLP weight-gradient GEMMs */
+  UPIPE_KERNEL_KINDS = 10
 };
 int upipe_profile_start(void);
 int upipe_profile_stop(double* total_ms, int64_t* launches, double* flops, int n_kinds);

@@ -19,7 +19,7 @@ def test_exports_every_header_symbol(lib):
     names = api.header_symbols()
     assert set(names) == {"upipe_attn_workspace_bytes", "upipe_choose_chunk_heads", "upipe_attn_fwd",
                           "upipe_attn_bwd", "upipe_strerror", "upipe_version", "upipe_profile_start",
-                          "upipe_profile_stop"}
+                          "upipe_profile_stop", "upipe_mlp_workspace_bytes", "upipe_mlp_fwd", "upipe_mlp_bwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.upipe_version() == 100
@@ -180,3 +180,82 @@ def test_profile_stop_without_launches_is_empty(lib):
     res = api.profile_stop()
     assert set(res) == set(api.KERNEL_KINDS)
     assert all(v["launches"] == 0 and v["ms"] == 0.0 for v in res.values())
+
+
+# ---------------------------------------------------------------------------
+# sequence-tiled MLP
+# ---------------------------------------------------------------------------
+def _expected_mlp_ws(N, D, F, T, es, bwd):
+    """The documented layout: tile buffers of min(T, N rounded up to 128) rows."""
+    rows = min(T, (N + 127) // 128 * 128)
+    tile = rows * F * es
+
+    def r(b):
+        return (b + 255) // 256 * 256
+    total = r(tile)  # a
+    if bwd:
+        total += r(2 * tile) + r(tile) + r(tile)  # h|u, dh, du
+        total += r(F * D * es) + r(2 * F * D * es)  # Wd^T, [Wg^T | Wu^T]
+    return total
+
+
+@pytest.mark.parametrize("N,D,F,T", [(300, 256, 384, 128), (1, 128, 128, 128), (16384, 4096, 14336, 4096),
+                                     (100, 512, 1024, 4096), (5242880 // 8, 5120, 25600, 8192)])
+def test_mlp_workspace_formula(N, D, F, T):
+    for dt, es in (("fp32", 4), ("bf16", 2)):
+        for bwd in (False, True):
+            assert api.mlp_workspace_bytes(N, D, F, T, dt, bwd) == _expected_mlp_ws(N, D, F, T, es, bwd)
+
+
+def test_mlp_workspace_scales_with_tile_not_tokens():
+    # the tile buffers grow with tile_tokens; past one tile, N does not change them
+    a = api.mlp_workspace_bytes(1 << 20, 4096, 14336, 4096, "bf16", True)
+    b = api.mlp_workspace_bytes(1 << 22, 4096, 14336, 4096, "bf16", True)
+    c = api.mlp_workspace_bytes(1 << 20, 4096, 14336, 8192, "bf16", True)
+    assert a == b
+    assert c - a == 5 * 4096 * 14336 * 2
+
+
+def test_mlp_workspace_rejects_bad_shapes():
+    assert api.mlp_workspace_bytes(0, 256, 384, 128, "bf16", False) == 0
+    assert api.mlp_workspace_bytes(300, 250, 384, 128, "bf16", False) == 0
+    assert api.mlp_workspace_bytes(300, 256, 320, 128, "bf16", False) == 0
+    assert api.mlp_workspace_bytes(300, 256, 384, 100, "bf16", False) == 0
+    assert api.mlp_workspace_bytes(300, 256, 384, 0, "bf16", False) == 0
+
+
+def _mlp_fwd(lib, **kw):
+    a = dict(dtype=1, N=300, D=256, F=384, T=128, x=P, wg=P, wu=P, wd=P, y=P, ws=P, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.upipe_mlp_fwd(a["dtype"], a["N"], a["D"], a["F"], a["T"], a["x"], a["wg"], a["wu"], a["wd"],
+                             a["y"], a["ws"], a["wsb"], a["stream"])
+
+
+def _mlp_bwd(lib, **kw):
+    a = dict(dtype=0, N=300, D=256, F=384, T=128, x=P, wg=P, wu=P, wd=P, dy=P, dx=P, dwg=P, dwu=P, dwd=P, ws=P,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.upipe_mlp_bwd(a["dtype"], a["N"], a["D"], a["F"], a["T"], a["x"], a["wg"], a["wu"], a["wd"],
+                             a["dy"], a["dx"], a["dwg"], a["dwu"], a["dwd"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_mlp_fwd_validation_errors(lib):
+    assert _mlp_fwd(lib, dtype=5) == INVALID
+    assert _mlp_fwd(lib, N=0) == INVALID
+    assert _mlp_fwd(lib, D=200) == UNSUPPORTED
+    assert _mlp_fwd(lib, F=200) == UNSUPPORTED
+    assert _mlp_fwd(lib, T=64) == UNSUPPORTED
+    assert _mlp_fwd(lib, wu=None) == INVALID
+    assert _mlp_fwd(lib, y=P + 2) == ALIGN
+    need = api.mlp_workspace_bytes(300, 256, 384, 128, "bf16", False)
+    assert _mlp_fwd(lib, wsb=need - 1) == WORKSPACE
+    assert _mlp_fwd(lib, ws=None) == WORKSPACE
+    assert _mlp_fwd(lib, ws=P + 16) == ALIGN
+
+
+def test_mlp_bwd_validation_errors(lib):
+    assert _mlp_bwd(lib, dwd=None) == INVALID
+    assert _mlp_bwd(lib, dy=P + 4) == ALIGN
+    assert _mlp_bwd(lib, F=0) == INVALID
+    need = api.mlp_workspace_bytes(300, 256, 384, 128, "fp32", True)
+    assert _mlp_bwd(lib, wsb=need - 256) == WORKSPACE
