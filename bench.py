@@ -89,6 +89,77 @@ def cpu_baseline(w, sample_n=8192):
                       f"rate = model flops of that sample / time"}
 
 
+MLP_WORKLOAD = dict(name="llama3-8b-mlp-seq-shard-16k", n_tokens=16384, d_model=4096, d_ff=14336,
+                    tile_tokens=4096, dtype="bf16")
+
+
+def mlp_bench(dev, steps, warmup):
+    """The sequence-tiled gated-SiLU MLP on one GPU's sequence shard of the same
+    131072-token Llama3-8B run (131072 / 8 tokens, d_model 4096, d_ff 14336),
+    tile_tokens 4096, bf16: forward and backward times, model TFLOP/s
+    (18 N D F: three GEMMs forward, six backward), the per-kind kernel table
+    and the tiled vs untiled workspace."""
+    import numpy as np
+    import torch
+
+    from headwise_chunked_attention_amd import api
+    from headwise_chunked_attention_amd.synth import MlpInputs
+
+    w = MLP_WORKLOAD
+    N, D, F, T = w["n_tokens"], w["d_model"], w["d_ff"], w["tile_tokens"]
+    inp = MlpInputs(N, D, F, "bf16", seed=0)
+    t = {k: torch.from_numpy(getattr(inp, k)).to(dev).to(torch.bfloat16) for k in ("x", "dy", "wg", "wu", "wd")}
+    del inp
+    ws = api.alloc_workspace(api.mlp_workspace_bytes(N, D, F, T, "bf16", True), dev)
+    y = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    f32 = torch.float32
+    out = (torch.empty((N, D), dtype=torch.bfloat16, device=dev), torch.empty((F, D), dtype=f32, device=dev),
+           torch.empty((F, D), dtype=f32, device=dev), torch.empty((D, F), dtype=f32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        api.mlp_fwd(t["x"], t["wg"], t["wu"], t["wd"], tile_tokens=T, y=y, workspace=ws)
+
+    def bwd():
+        api.mlp_bwd(t["x"], t["wg"], t["wu"], t["wd"], t["dy"], tile_tokens=T, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t_f = [e[0].elapsed_time(e[1]) for e in evs]
+    t_b = [e[1].elapsed_time(e[2]) for e in evs]
+    api.profile_start()
+    fwd()
+    bwd()
+    prof = api.profile_stop()
+    model = 18.0 * N * D * F
+    step_ms = float(np.median([a + b for a, b in zip(t_f, t_b)]))
+    kinds = {k: {"ms": v["ms"], "launches": v["launches"],
+                 "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None}
+             for k, v in prof.items() if v["launches"]}
+    g = prof["mlp_gemm"]
+    achieved = g["flops"] / (g["ms"] * 1e-3) / 1e12
+    es = 2
+    return {"workload": w["name"], "n_tokens": N, "d_model": D, "d_ff": F, "tile_tokens": T, "dtype": "bf16",
+            "fwd_ms": float(np.median(t_f)), "bwd_ms": float(np.median(t_b)), "step_ms": step_ms,
+            "model_tflops": model / (step_ms * 1e-3) / 1e12, "model_flops": model,
+            "kernels": kinds,
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                         "kernel": "gemm_nt_kernel (gated-SiLU, store epilogues)"},
+            "workspace_gb": {"tiled_bwd": api.mlp_workspace_bytes(N, D, F, T, "bf16", True) / 1e9,
+                             "untiled_intermediates": 5 * N * F * es / 1e9}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +168,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=1)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP measurement")
     ap.add_argument("--n-tokens", type=int, default=None, help="override N (not the headline workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) so that "
@@ -230,6 +302,12 @@ def main():
                 "algorithmic_flops_per_launch": ab["flops"] / ab["launches"],
                 "avg_launch_ms": ab["ms"] / ab["launches"]}
 
+    mlp = None
+    if not args.no_mlp:
+        mlp = mlp_bench(dev, max(2, args.steps // 2), 1)
+        print(f"# mlp: fwd {mlp['fwd_ms']:.2f} ms, bwd {mlp['bwd_ms']:.2f} ms, {mlp['model_tflops']:.0f} TFLOP/s",
+              file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         try:
@@ -265,6 +343,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "mlp": mlp,
     }
     print(json.dumps(line), flush=True)
 
