@@ -7,7 +7,8 @@ input streams.
 
 Recipe (stated once, used everywhere):
   * every tensor has an integer "tensor id": x 0, Wq 1, Wk 2, Wv 3, Wo 4,
-    dY 5, q-norm gamma 6, k-norm gamma 7, MLP gate/up/down weights 8/9/10;
+    dY 5, q-norm gamma 6, k-norm gamma 7, MLP gate/up/down weights 8/9/10,
+    LM-head weight 11, loss targets 12, per-token loss gradients 13;
   * a 2-D tensor is drawn in blocks of ``ROW_BLOCK`` rows; block ``b`` of
     tensor ``t`` under run seed ``s`` uses
     ``numpy.random.default_rng(SeedSequence([s, t, b]))`` and draws
@@ -29,7 +30,7 @@ ROW_BLOCK = 8192
 GEN_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 TENSOR_IDS = {"x": 0, "wq": 1, "wk": 2, "wv": 3, "wo": 4, "dy": 5, "q_norm": 6, "k_norm": 7,
-              "wg": 8, "wu": 9, "wd": 10}
+              "wg": 8, "wu": 9, "wd": 10, "w_lm": 11, "targets": 12, "g_loss": 13}
 
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
@@ -164,3 +165,22 @@ class MlpInputs:
         self.wg = gen_rows("wg", F, D, w_std, dtype, seed)
         self.wu = gen_rows("wu", F, D, w_std, dtype, seed)
         self.wd = gen_rows("wd", D, F, w_std, dtype, seed)
+
+
+class LossInputs:
+    """Inputs of one tiled cross-entropy problem, as host arrays.
+
+    h ``[N][D]`` float32 (std 1), w ``[V][D]`` float32 (std ``w_std``),
+    targets ``[N]`` int32 uniform in ``[0, V)``, g ``[N]`` float32 per-token
+    upstream gradients uniform in ``[0.5, 1.5) / N`` (a mean loss, jittered).
+    """
+
+    def __init__(self, n_tokens: int, d_model: int, vocab: int, dtype: str, seed: int = 0, w_std: float = 0.02):
+        self.n_tokens, self.d_model, self.vocab, self.dtype, self.seed = n_tokens, d_model, vocab, dtype, seed
+        N = n_tokens
+        self.h = gen_rows("x", N, d_model, 1.0, dtype, seed)
+        self.w = gen_rows("w_lm", vocab, d_model, w_std, dtype, seed)
+        rng = _block_rng(seed, TENSOR_IDS["targets"], 0)
+        self.targets = rng.integers(0, vocab, N).astype(np.int32)
+        rng = _block_rng(seed, TENSOR_IDS["g_loss"], 0)
+        self.g = (rng.uniform(0.5, 1.5, N) / N).astype(np.float32)

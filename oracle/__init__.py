@@ -1,5 +1,5 @@
-"""CPU fp64 oracle for headwise-chunked causal RoPE/GQA attention and the
-sequence-tiled gated-SiLU MLP.
+"""CPU fp64 oracle for headwise-chunked causal RoPE/GQA attention, the
+sequence-tiled gated-SiLU MLP and the sequence-tiled cross-entropy loss.
 
 TEST INFRASTRUCTURE ONLY. Nothing in the product package imports this; only
 ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -27,4 +27,10 @@ from .mlp import (  # noqa: F401
     mlp_bwd,
     mlp_rows,
     mlp_dx_rows,
+)
+from .loss import (  # noqa: F401
+    ce_fwd,
+    ce_bwd,
+    ce_rows,
+    ce_dh_rows,
 )
