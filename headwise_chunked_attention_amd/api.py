@@ -56,6 +56,12 @@ def load():
     lib.upipe_mlp_fwd.restype = i32
     lib.upipe_mlp_bwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.upipe_mlp_bwd.restype = i32
+    lib.upipe_loss_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.upipe_loss_workspace_bytes.restype = sz
+    lib.upipe_loss_fwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.upipe_loss_fwd.restype = i32
+    lib.upipe_loss_bwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.upipe_loss_bwd.restype = i32
     lib.upipe_strerror.argtypes = [i32]
     lib.upipe_strerror.restype = ctypes.c_char_p
     lib.upipe_version.argtypes = []
@@ -225,7 +231,62 @@ def attn_bwd(x, wq, wk, wv, wo, dy, lse, *, n_q_heads, n_kv_heads, head_dim, rop
 
 
 KERNEL_KINDS = ("projection", "out_gemm", "attn_fwd", "attn_recompute", "attn_bwd_dkdv", "attn_bwd_dq", "wgrad",
-                "other", "mlp_gemm", "mlp_wgrad")
+                "other", "mlp_gemm", "mlp_wgrad", "loss_gemm", "loss_wgrad")
+
+
+def loss_workspace_bytes(n_tokens, d_model, vocab, tile_tokens, dtype, backward) -> int:
+    return int(load().upipe_loss_workspace_bytes(int(n_tokens), int(d_model), int(vocab), int(tile_tokens),
+                                                  dtype_code(dtype), int(bool(backward))))
+
+
+def loss_fwd(h, w, targets, *, tile_tokens, loss=None, lse=None, workspace=None, stream=None):
+    """Per-token cross-entropy of the LM head h W^T, tile_tokens rows at a time
+    (upipe_loss_fwd). Returns (loss [N], lse [N]), both fp32."""
+    lib = load()
+    dev, dt = h.device, h.dtype
+    N, D = h.shape
+    V = w.shape[0]
+    _check(h, "h", dt, (N, D), dev)
+    _check(w, "w", dt, (V, D), dev)
+    _check(targets, "targets", torch.int32, (N,), dev)
+    f32 = torch.float32
+    loss = torch.empty((N,), dtype=f32, device=dev) if loss is None else loss
+    lse = torch.empty((N,), dtype=f32, device=dev) if lse is None else lse
+    _check(loss, "loss", f32, (N,), dev)
+    _check(lse, "lse", f32, (N,), dev)
+    if workspace is None:
+        workspace = alloc_workspace(loss_workspace_bytes(N, D, V, tile_tokens, dt, False), dev)
+    rc = lib.upipe_loss_fwd(dtype_code(dt), N, D, V, int(tile_tokens), _ptr(h), _ptr(w), _ptr(targets), _ptr(loss),
+                            _ptr(lse), _ptr(workspace), workspace.numel(), _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_loss_fwd")
+    return loss, lse
+
+
+def loss_bwd(h, w, targets, lse, g, *, tile_tokens, dh=None, dw=None, workspace=None, stream=None):
+    """(dh, dW) of the per-token losses for upstream gradients g [N] (upipe_loss_bwd)."""
+    lib = load()
+    dev, dt = h.device, h.dtype
+    N, D = h.shape
+    V = w.shape[0]
+    f32 = torch.float32
+    _check(h, "h", dt, (N, D), dev)
+    _check(w, "w", dt, (V, D), dev)
+    _check(targets, "targets", torch.int32, (N,), dev)
+    _check(lse, "lse", f32, (N,), dev)
+    _check(g, "g", f32, (N,), dev)
+    dh = torch.empty((N, D), dtype=dt, device=dev) if dh is None else dh
+    dw = torch.empty((V, D), dtype=f32, device=dev) if dw is None else dw
+    _check(dh, "dh", dt, (N, D), dev)
+    _check(dw, "dw", f32, (V, D), dev)
+    if workspace is None:
+        workspace = alloc_workspace(loss_workspace_bytes(N, D, V, tile_tokens, dt, True), dev)
+    rc = lib.upipe_loss_bwd(dtype_code(dt), N, D, V, int(tile_tokens), _ptr(h), _ptr(w), _ptr(targets), _ptr(lse),
+                            _ptr(g), _ptr(dh), _ptr(dw), _ptr(workspace), workspace.numel(),
+                            _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_loss_bwd")
+    return dh, dw
 
 
 def mlp_workspace_bytes(n_tokens, d_model, d_ff, tile_tokens, dtype, backward) -> int:

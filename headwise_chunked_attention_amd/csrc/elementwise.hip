@@ -98,7 +98,37 @@ __global__ __launch_bounds__(256) void fill_f32_kernel(float* p, int64_t n, floa
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
+// One wave per row: combine the row's per-tile (max, sum exp) partials.
+__global__ __launch_bounds__(256) void ce_reduce_kernel(const float* part, const float* tgt, int64_t rows,
+                                                        int64_t ntiles, float* lse, float* loss) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float* pr = part + row * ntiles * 2;
+  float mx = -INFINITY;
+  for (int64_t t = l; t < ntiles; t += 64) mx = fmaxf(mx, pr[t * 2]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  float se = 0.f;
+  for (int64_t t = l; t < ntiles; t += 64) se += pr[t * 2 + 1] * expf(pr[t * 2] - mx);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) se += __shfl_xor(se, o);
+  if (l == 0) {
+    const float v = mx + logf(se);
+    lse[row] = v;
+    loss[row] = v - tgt[row];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_ce_reduce(const float* part, const float* tgt, int64_t rows, int64_t ntiles, float* lse,
+                            float* loss, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, part, tgt, rows, ntiles,
+                     lse, loss);
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_grad_finish(const GradFinish<T>& p, int head_dim, hipStream_t s) {

@@ -307,6 +307,49 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
         st16_f<T>(g.du + m * g.ldf + f0, du);
         st16_f<T>(g.a + m * g.ldf + f0, av);
       }
+    } else if constexpr (EPI == EPI_CE) {
+      // four threads per row, 32 logits each: the tile's row max and sum of
+      // exp(logit - max), and the target's logit where the tile holds it
+      static_assert(EPI_ROWS * 4 == NTHREADS && BN == 128, "four threads per row");
+      const CeOut<T>& ce = p.ce;
+      const int row = tid >> 2, qq = tid & 3;
+      const int64_t m = m0 + r0 + row;
+      const float* cr = Cs + row * SC + qq * 32;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) mx = fmaxf(mx, cr[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      float se = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) se += expf(cr[j] - mx);
+      se += __shfl_xor(se, 1);
+      se += __shfl_xor(se, 2);
+      if (m < p.M) {
+        if (qq == 0) {
+          float* pp = ce.part + (m * (p.N / BN) + n0 / BN) * 2;
+          pp[0] = mx;
+          pp[1] = se;
+        }
+        const int64_t t = (int64_t)ce.targets[m] - n0 - qq * 32;
+        if (t >= 0 && t < 32) ce.tgt[m] = cr[t];
+      }
+    } else if constexpr (EPI == EPI_CE_BWD) {
+      const CeOut<T>& ce = p.ce;
+      for (int c = tid; c < EPI_ROWS * BN / VEC; c += NTHREADS) {
+        const int row = c / (BN / VEC), cv = c % (BN / VEC);
+        const int64_t m = m0 + r0 + row;
+        if (m >= p.M) continue;
+        const float l = ce.lse[m], gg = ce.g[m];
+        const int64_t tcol = (int64_t)ce.targets[m] - n0 - cv * VEC;
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float pr = expf(Cs[row * SC + cv * VEC + e] - l) - (tcol == e ? 1.0f : 0.0f);
+          v[e] = pr * gg;
+        }
+        st16_f<T>(ce.dz + m * ce.ldz + n0 + cv * VEC, v);
+      }
     } else if constexpr (EPI == EPI_ACCUM) {
       if (pass) load_old(1);
 #pragma unroll
@@ -536,6 +579,12 @@ hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
   if (p.M <= 0 || p.K <= 0 || p.K % bk) return hipErrorInvalidValue;
   if ((epi == EPI_GLU || epi == EPI_GLU_BWD) && (bn != 128 || p.N % 128 || p.glu.ldf % 64))
     return hipErrorInvalidValue;
+  if ((epi == EPI_CE || epi == EPI_CE_BWD) && (bn != 128 || p.N % 128)) return hipErrorInvalidValue;
+  if (epi == EPI_CE)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_CE>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else if (epi == EPI_CE_BWD)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_CE_BWD>), dim3(grid), dim3(NTHREADS), 0, s, p);
+  else
   if (epi == EPI_STORE && bn == 128)
     hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_STORE>), dim3(grid), dim3(NTHREADS), 0, s, p);
   else if (epi == EPI_GLU)

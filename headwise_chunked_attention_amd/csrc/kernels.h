@@ -8,7 +8,7 @@ typedef __bf16 bf16;
 
 namespace upipe {
 
-enum { EPI_ACCUM = 0, EPI_HEADS = 1, EPI_STORE = 2, EPI_GLU = 3, EPI_GLU_BWD = 4 };
+enum { EPI_ACCUM = 0, EPI_HEADS = 1, EPI_STORE = 2, EPI_GLU = 3, EPI_GLU_BWD = 4, EPI_CE = 5, EPI_CE_BWD = 6 };
 
 // Where one group of heads produced by a projection GEMM goes. A head is one
 // N-tile of the GEMM (BN == head_dim).
@@ -39,13 +39,29 @@ struct GluOut {
   int64_t ldf;
 };
 
+// Cross-entropy epilogues over logits C = h W^T (BN = 128; rows m < M).
+// EPI_CE: per row and 128-column tile t, part[(m * N/128 + t) * 2 + {0, 1}] =
+//   (max of the tile's logits, sum of exp(logit - that max)); and
+//   tgt[m] = C[m][targets[m]] from the tile that holds the target.
+// EPI_CE_BWD: dz[m * ldz + n] = (exp(C[m][n] - lse[m]) - [n == targets[m]]) * g[m].
+template <typename T>
+struct CeOut {
+  const int32_t* targets;
+  float* part;
+  float* tgt;
+  const float* lse;
+  const float* g;
+  T* dz;
+  int64_t ldz;
+};
+
 // C[m][n] = sum_k A(m,k) B(n,k), both operands contiguous along k.
 //   A(m,k) = a + (k / a_kblk) * a_kblk_stride + m * lda + (k % a_kblk)
 //   B(n,k) = b[s] + (n - seg_begin(s)) * ldb[s] + k for the segment s holding n
 // EPI_ACCUM:  c[m * ldc + n] = (accumulate ? c : 0) + C   (rows m < M)
 // EPI_STORE:  c[m * ldc + n] = C (rows m < M); long k (128-byte k rows)
 // EPI_HEADS:  head-wise epilogue per segment (see HeadOut), rows m < Np.
-// EPI_GLU, EPI_GLU_BWD: see GluOut.
+// EPI_GLU, EPI_GLU_BWD: see GluOut. EPI_CE, EPI_CE_BWD: see CeOut.
 template <typename T>
 struct GemmNT {
   const T* a;
@@ -65,6 +81,7 @@ struct GemmNT {
   float eps;
   double log2_theta;
   GluOut<T> glu;
+  CeOut<T> ce;
 };
 
 // out[m*ldm + n*ldn] += sum_{k in split} A(k,m) B(k,n)   (fp32 atomics)
@@ -162,5 +179,9 @@ template <typename T>
 hipError_t launch_transpose(const T* src, int64_t rows, int64_t cols, int64_t ld_src, T* dst,
                             int64_t ld_dst, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// Per row m < rows: lse[m] = log sum over the ntiles tiles of the row's
+// (max, sum exp) partials; loss[m] = lse[m] - tgt[m].
+hipError_t launch_ce_reduce(const float* part, const float* tgt, int64_t rows, int64_t ntiles, float* lse,
+                            float* loss, hipStream_t s);
 
 }  // namespace upipe

@@ -183,6 +183,37 @@ int upipe_mlp_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int64_
                   float* dw_down, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Sequence-tiled cross-entropy loss of the LM head, the other element-wise
+ * part that the talk's memory stack tiles along the sequence (same passages
+ * as the MLP above): the [N][V] logits never exist; tile_tokens rows of them
+ * at a time are consumed by the GEMM's epilogue.
+ *
+ *   z = h W^T,  lse_i = log sum_v exp z[i, v],  loss_i = lse_i - z[i, t_i]
+ *   backward, for per-token upstream gradients g_i:
+ *   dz = (softmax(z) - onehot(t)) g,  dh = dz W,  dW = dz^T h
+ *
+ *   h, dh [N][D] io dtype; W [V][D] io dtype (nn.Linear [out][in]);
+ *   targets [N] int32, each in [0, V) (a target outside that range makes its
+ *   loss NaN in the forward and contributes no onehot in the backward);
+ *   loss, lse, g [N] fp32 (lse is written by the forward and read by the
+ *   backward); dW [V][D] fp32 (out, overwritten).
+ * Supported: N >= 1; D and V positive multiples of 128; tile_tokens a
+ * positive multiple of 128. Pointers, streams, validation and error codes as
+ * above; the workspace must hold upipe_loss_workspace_bytes(...) bytes.
+ */
+size_t upipe_loss_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t vocab,
+                                  int64_t tile_tokens, upipe_dtype_t dtype, int backward);
+
+int upipe_loss_fwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int64_t vocab,
+                   int64_t tile_tokens, const void* h, const void* w, const int32_t* targets,
+                   float* loss, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+int upipe_loss_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int64_t vocab,
+                   int64_t tile_tokens, const void* h, const void* w, const int32_t* targets,
+                   const float* lse, const float* g, void* dh, float* dw, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
  * Optional per-kernel timing (for benchmarks and profilers; off by default).
  * While enabled, every kernel the library enqueues is bracketed by two
  * hipEvents on the caller's stream, and its algorithmic work (flops of the
@@ -205,7 +236,9 @@ enum {
   UPIPE_KERNEL_OTHER = 7,           /* RoPE/RMSNorm backward, transposes, fills */
   UPIPE_KERNEL_MLP_GEMM = 8,        /* MLP products of x, a and dy (gated-SiLU epilogues) and dx */
   UPIPE_KERNEL_MLP_WGRAD = 9,       /* MLP weight-gradient GEMMs */
-  UPIPE_KERNEL_KINDS = 10
+  UPIPE_KERNEL_LOSS_GEMM = 10,      /* LM-head logits (loss epilogues), their reduction, dh */
+  UPIPE_KERNEL_LOSS_WGRAD = 11,     /* LM-head weight-gradient GEMMs */
+  UPIPE_KERNEL_KINDS = 12
 };
 int upipe_profile_start(void);
 int upipe_profile_stop(double* total_ms, int64_t* launches, double* flops, int n_kinds);

@@ -19,7 +19,8 @@ def test_exports_every_header_symbol(lib):
     names = api.header_symbols()
     assert set(names) == {"upipe_attn_workspace_bytes", "upipe_choose_chunk_heads", "upipe_attn_fwd",
                           "upipe_attn_bwd", "upipe_strerror", "upipe_version", "upipe_profile_start",
-                          "upipe_profile_stop", "upipe_mlp_workspace_bytes", "upipe_mlp_fwd", "upipe_mlp_bwd"}
+                          "upipe_profile_stop", "upipe_mlp_workspace_bytes", "upipe_mlp_fwd", "upipe_mlp_bwd",
+                          "upipe_loss_workspace_bytes", "upipe_loss_fwd", "upipe_loss_bwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.upipe_version() == 100
@@ -259,3 +260,53 @@ def test_mlp_bwd_validation_errors(lib):
     assert _mlp_bwd(lib, F=0) == INVALID
     need = api.mlp_workspace_bytes(300, 256, 384, 128, "fp32", True)
     assert _mlp_bwd(lib, wsb=need - 256) == WORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# sequence-tiled cross-entropy loss
+# ---------------------------------------------------------------------------
+def _expected_loss_ws(N, D, V, T, es, bwd):
+    rows = min(T, (N + 127) // 128 * 128)
+
+    def r(b):
+        return (b + 255) // 256 * 256
+    if not bwd:
+        return r(rows * (V // 128) * 2 * 4) + r(rows * 4)
+    return r(rows * V * es) + r(V * D * es)
+
+
+@pytest.mark.parametrize("N,D,V,T", [(300, 256, 1024, 128), (1, 128, 128, 128), (16384, 4096, 128256, 1024),
+                                     (100, 512, 151936, 4096)])
+def test_loss_workspace_formula(N, D, V, T):
+    for dt, es in (("fp32", 4), ("bf16", 2)):
+        for bwd in (False, True):
+            assert api.loss_workspace_bytes(N, D, V, T, dt, bwd) == _expected_loss_ws(N, D, V, T, es, bwd)
+    # past one tile, N does not change the workspace
+    assert api.loss_workspace_bytes(1 << 22, D, V, T, "bf16", True) == api.loss_workspace_bytes(1 << 20, D, V, T,
+                                                                                                "bf16", True)
+
+
+def test_loss_validation_errors(lib):
+    def fwd(**kw):
+        a = dict(dtype=1, N=300, D=256, V=1024, T=128, h=P, w=P, t=P, loss=P, lse=P, ws=P, wsb=1 << 40)
+        a.update(kw)
+        return lib.upipe_loss_fwd(a["dtype"], a["N"], a["D"], a["V"], a["T"], a["h"], a["w"], a["t"], a["loss"],
+                                  a["lse"], a["ws"], a["wsb"], None)
+
+    def bwd(**kw):
+        a = dict(dtype=0, N=300, D=256, V=1024, T=128, h=P, w=P, t=P, lse=P, g=P, dh=P, dw=P, ws=P, wsb=1 << 40)
+        a.update(kw)
+        return lib.upipe_loss_bwd(a["dtype"], a["N"], a["D"], a["V"], a["T"], a["h"], a["w"], a["t"], a["lse"],
+                                  a["g"], a["dh"], a["dw"], a["ws"], a["wsb"], None)
+
+    assert fwd(dtype=3) == INVALID
+    assert fwd(N=0) == INVALID
+    assert fwd(V=1000) == UNSUPPORTED
+    assert fwd(D=100) == UNSUPPORTED
+    assert fwd(T=200) == UNSUPPORTED
+    assert fwd(t=None) == INVALID
+    assert fwd(lse=P + 4) == ALIGN
+    assert fwd(wsb=api.loss_workspace_bytes(300, 256, 1024, 128, "bf16", False) - 1) == WORKSPACE
+    assert bwd(g=None) == INVALID
+    assert bwd(dw=P + 8) == ALIGN
+    assert bwd(wsb=api.loss_workspace_bytes(300, 256, 1024, 128, "fp32", True) - 256) == WORKSPACE
