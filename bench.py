@@ -13,7 +13,8 @@ MFMA peak; median and minimum step, forward and backward times; the
 attention-core and hardware (recompute included) rates; the workspace bytes
 per chunk size; a chunk-size sweep; per-kernel event timings (from a second,
 profiled run of the same steps); the roofline entry of the dominant kernel
-(attention backward); and the CPU fp64 oracle timed on a bounded sample.
+(attention backward); the CPU fp64 oracle timed on a bounded sample; and the
+sequence-tiled MLP and LM-head loss next to the op (``mlp``, ``loss``).
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--chunk 1] [--no-sweep] [--no-cpu]
 """
@@ -160,6 +161,78 @@ def mlp_bench(dev, steps, warmup):
                              "untiled_intermediates": 5 * N * F * es / 1e9}}
 
 
+LOSS_WORKLOAD = dict(name="llama3-lm-head-loss-seq-shard-16k", n_tokens=16384, d_model=4096, vocab=128256,
+                     tile_tokens=1024, dtype="bf16")
+
+
+def loss_bench(dev, steps, warmup):
+    """The sequence-tiled cross-entropy of the Llama3 LM head (vocab 128256) on
+    the same 16384-token sequence shard, tile_tokens 1024, bf16: forward and
+    backward times, model TFLOP/s (2 N D V forward, 4 N D V backward: dh and
+    dW), kernel table and the tiled vs untiled logits buffer."""
+    import numpy as np
+    import torch
+
+    from headwise_chunked_attention_amd import api
+    from headwise_chunked_attention_amd.synth import LossInputs
+
+    w = LOSS_WORKLOAD
+    N, D, V, T = w["n_tokens"], w["d_model"], w["vocab"], w["tile_tokens"]
+    inp = LossInputs(N, D, V, "bf16", seed=0)
+    h = torch.from_numpy(inp.h).to(dev).to(torch.bfloat16)
+    wt = torch.from_numpy(inp.w).to(dev).to(torch.bfloat16)
+    tg = torch.from_numpy(inp.targets).to(dev)
+    g = torch.from_numpy(inp.g).to(dev)
+    del inp
+    ws = api.alloc_workspace(max(api.loss_workspace_bytes(N, D, V, T, "bf16", True),
+                                 api.loss_workspace_bytes(N, D, V, T, "bf16", False)), dev)
+    loss = torch.empty((N,), dtype=torch.float32, device=dev)
+    lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    dh = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((V, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        api.loss_fwd(h, wt, tg, tile_tokens=T, loss=loss, lse=lse, workspace=ws)
+
+    def bwd():
+        api.loss_bwd(h, wt, tg, lse, g, tile_tokens=T, dh=dh, dw=dw, workspace=ws)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t_f = [e[0].elapsed_time(e[1]) for e in evs]
+    t_b = [e[1].elapsed_time(e[2]) for e in evs]
+    api.profile_start()
+    fwd()
+    bwd()
+    prof = api.profile_stop()
+    model = 6.0 * N * D * V
+    step_ms = float(np.median([a + b for a, b in zip(t_f, t_b)]))
+    kinds = {k: {"ms": v["ms"], "launches": v["launches"],
+                 "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None}
+             for k, v in prof.items() if v["launches"]}
+    lg = prof["loss_gemm"]
+    achieved = lg["flops"] / (lg["ms"] * 1e-3) / 1e12
+    return {"workload": w["name"], "n_tokens": N, "d_model": D, "vocab": V, "tile_tokens": T, "dtype": "bf16",
+            "fwd_ms": float(np.median(t_f)), "bwd_ms": float(np.median(t_b)), "step_ms": step_ms,
+            "model_tflops": model / (step_ms * 1e-3) / 1e12, "model_flops": model, "kernels": kinds,
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                         "kernel": "gemm_nt_kernel (loss and store epilogues) + row reduction"},
+            "workspace_gb": {"tiled_bwd": api.loss_workspace_bytes(N, D, V, T, "bf16", True) / 1e9,
+                             "untiled_logits": N * V * 2 / 1e9}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,7 +241,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=1)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP measurement")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP and loss measurements")
     ap.add_argument("--n-tokens", type=int, default=None, help="override N (not the headline workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) so that "
@@ -302,11 +375,16 @@ def main():
                 "algorithmic_flops_per_launch": ab["flops"] / ab["launches"],
                 "avg_launch_ms": ab["ms"] / ab["launches"]}
 
-    mlp = None
+    mlp = loss = None
     if not args.no_mlp:
         mlp = mlp_bench(dev, max(2, args.steps // 2), 1)
         print(f"# mlp: fwd {mlp['fwd_ms']:.2f} ms, bwd {mlp['bwd_ms']:.2f} ms, {mlp['model_tflops']:.0f} TFLOP/s",
               file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        loss = loss_bench(dev, max(2, args.steps // 2), 1)
+        print(f"# loss: fwd {loss['fwd_ms']:.2f} ms, bwd {loss['bwd_ms']:.2f} ms, {loss['model_tflops']:.0f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
@@ -344,6 +422,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "mlp": mlp,
+        "loss": loss,
     }
     print(json.dumps(line), flush=True)
 
