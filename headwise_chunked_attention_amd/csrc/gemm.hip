@@ -41,6 +41,9 @@ template <int EPI> constexpr int nt_kb() { return EPI == EPI_ACCUM ? 64 : 128; }
 // gate/up halves of a gated B tile
 template <int EPI> constexpr bool nt_gated() { return EPI == EPI_GLU; }
 constexpr int EPI_ROWS = BM / 2;  // rows per epilogue pass
+constexpr float LOG2E_F = 1.4426950408889634f;
+// 1 / (1 + e^-z) from the hardware exp2 and reciprocal (about 1 ulp each)
+DEV float fast_sigmoid(float z) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-z * LOG2E_F)); }
 
 template <typename T, int BN, int EPI>
 constexpr int gemm_smem_bytes() {
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
             const float hh = Cs[row * SC + cv * VEC + e], uu = Cs[row * SC + BN / 2 + cv * VEC + e];
-            v[e] = hh / (1.0f + expf(-hh)) * uu;
+            v[e] = hh * fast_sigmoid(hh) * uu;
           }
           st16_f<T>(g.a + m * g.ldf + n0 / 2 + cv * VEC, v);
         }
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           const float da = Cs[row * SC + cv * VEC + e];
-          const float sg = 1.0f / (1.0f + expf(-hh[e]));
+          const float sg = fast_sigmoid(hh[e]);
           const float sh = hh[e] * sg;
           dh[e] = da * uu[e] * (sg * (1.0f + hh[e] * (1.0f - sg)));
           du[e] = da * sh;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
       mx = fmaxf(mx, __shfl_xor(mx, 2));
       float se = 0.f;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) se += expf(cr[j] - mx);
+      for (int j = 0; j < 32; ++j) se += fast_exp2((cr[j] - mx) * LOG2E_F);
       se += __shfl_xor(se, 1);
       se += __shfl_xor(se, 2);
       if (m < p.M) {
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
         float v[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float pr = expf(Cs[row * SC + cv * VEC + e] - l) - (tcol == e ? 1.0f : 0.0f);
+          const float pr = fast_exp2((Cs[row * SC + cv * VEC + e] - l) * LOG2E_F) - (tcol == e ? 1.0f : 0.0f);
           v[e] = pr * gg;
         }
         st16_f<T>(ce.dz + m * ce.ldz + n0 + cv * VEC, v);
