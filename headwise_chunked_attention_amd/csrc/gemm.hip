@@ -141,6 +141,123 @@ DEV void nt_store_tile(T* As, T* Bs, const u32x4 (&ra)[BM * G::CPR / NTHREADS], 
   }
 }
 
+// One epilogue pass of the plain-store, gated-SiLU and cross-entropy
+// epilogues over tile rows mr0 .. mr0+ROWS-1 (global row numbers), read from
+// the fp32 staging tile Cs[ROWS][BN + 4] by NTH threads.
+template <typename T, int BN, int EPI, int ROWS, int NTH>
+DEV void epi_pass(const GemmNT<T>& p, const float* Cs, int64_t mr0, int64_t n0, int tid) {
+  constexpr int VEC = 16 / (int)sizeof(T), SC = BN + 4;
+  if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+    for (int i = 0; i < ROWS * BN / VEC / NTH; ++i) {
+      const int c = tid + i * NTH;
+      const int row = c / (BN / VEC), cv = c % (BN / VEC);
+      const int64_t m = mr0 + row;
+      if (m >= p.M) continue;
+      float v[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+      st16_f<T>(p.c + m * p.ldc + n0 + cv * VEC, v);
+    }
+  } else if constexpr (EPI == EPI_GLU) {
+    const GluOut<T>& g = p.glu;
+    if (g.a) {  // a = silu(h) * u for the tile's 64 features
+      for (int c = tid; c < ROWS * (BN / 2) / VEC; c += NTH) {
+        const int row = c / (BN / 2 / VEC), cv = c % (BN / 2 / VEC);
+        const int64_t m = mr0 + row;
+        if (m >= p.M) continue;
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float hh = Cs[row * SC + cv * VEC + e], uu = Cs[row * SC + BN / 2 + cv * VEC + e];
+          v[e] = hh * fast_sigmoid(hh) * uu;
+        }
+        st16_f<T>(g.a + m * g.ldf + n0 / 2 + cv * VEC, v);
+      }
+    }
+    if (g.hu) {  // h and u as computed, in the tile's own column order
+      for (int c = tid; c < ROWS * BN / VEC; c += NTH) {
+        const int row = c / (BN / VEC), cv = c % (BN / VEC);
+        const int64_t m = mr0 + row;
+        if (m >= p.M) continue;
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+        st16_f<T>(g.hu + m * 2 * g.ldf + n0 + cv * VEC, v);
+      }
+    }
+  } else if constexpr (EPI == EPI_GLU_BWD) {
+    // C = da over features n0 .. n0+BN-1; h, u of feature f sit at columns
+    // 128 (f / 64) + f % 64 and that + 64 of hu
+    const GluOut<T>& g = p.glu;
+    for (int c = tid; c < ROWS * BN / VEC; c += NTH) {
+      const int row = c / (BN / VEC), cv = c % (BN / VEC);
+      const int64_t m = mr0 + row;
+      if (m >= p.M) continue;
+      const int64_t f0 = n0 + cv * VEC;
+      const T* hp = g.hu + m * 2 * g.ldf + (f0 / 64) * 128 + f0 % 64;
+      float hh[VEC], uu[VEC], dh[VEC], du[VEC], av[VEC];
+      ld16_f<T>(hp, hh);
+      ld16_f<T>(hp + 64, uu);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float da = Cs[row * SC + cv * VEC + e];
+        const float sg = fast_sigmoid(hh[e]);
+        const float sh = hh[e] * sg;
+        dh[e] = da * uu[e] * (sg * (1.0f + hh[e] * (1.0f - sg)));
+        du[e] = da * sh;
+        av[e] = sh * uu[e];
+      }
+      st16_f<T>(g.dh + m * g.ldf + f0, dh);
+      st16_f<T>(g.du + m * g.ldf + f0, du);
+      st16_f<T>(g.a + m * g.ldf + f0, av);
+    }
+  } else if constexpr (EPI == EPI_CE) {
+    // four threads per row, 32 logits each: the tile's row max and sum of
+    // exp(logit - max), and the target's logit where the tile holds it
+    static_assert(ROWS * 4 == NTH && BN == 128, "four threads per row");
+    const CeOut<T>& ce = p.ce;
+    const int row = tid >> 2, qq = tid & 3;
+    const int64_t m = mr0 + row;
+    const float* cr = Cs + row * SC + qq * 32;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) mx = fmaxf(mx, cr[j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    float se = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) se += fast_exp2((cr[j] - mx) * LOG2E_F);
+    se += __shfl_xor(se, 1);
+    se += __shfl_xor(se, 2);
+    if (m < p.M) {
+      if (qq == 0) {
+        float* pp = ce.part + (m * (p.N / BN) + n0 / BN) * 2;
+        pp[0] = mx;
+        pp[1] = se;
+      }
+      const int64_t t = (int64_t)ce.targets[m] - n0 - qq * 32;
+      if (t >= 0 && t < 32) ce.tgt[m] = cr[t];
+    }
+  } else if constexpr (EPI == EPI_CE_BWD) {
+    const CeOut<T>& ce = p.ce;
+    for (int c = tid; c < ROWS * BN / VEC; c += NTH) {
+      const int row = c / (BN / VEC), cv = c % (BN / VEC);
+      const int64_t m = mr0 + row;
+      if (m >= p.M) continue;
+      const float l = ce.lse[m], gg = ce.g[m];
+      const int64_t tcol = (int64_t)ce.targets[m] - n0 - cv * VEC;
+      float v[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float pr = fast_exp2((Cs[row * SC + cv * VEC + e] - l) * LOG2E_F) - (tcol == e ? 1.0f : 0.0f);
+        v[e] = pr * gg;
+      }
+      st16_f<T>(ce.dz + m * ce.ldz + n0 + cv * VEC, v);
+    }
+  }
+}
+
 template <typename T, int BN, int EPI>
 __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   using G = GemmGeo<T, nt_kb<EPI>()>;
@@ -245,114 +362,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
     acc_to_lds<BN>(Cs, r0, EPI_ROWS, wm, wn, acc);
     lds_barrier();
 
-    if constexpr (EPI == EPI_STORE) {
-#pragma unroll
-      for (int i = 0; i < EPI_ROWS * BN / VEC / NTHREADS; ++i) {
-        const int c = tid + i * NTHREADS;
-        const int row = c / (BN / VEC), cv = c % (BN / VEC);
-        const int64_t m = m0 + r0 + row;
-        if (m >= p.M) continue;
-        float v[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
-        st16_f<T>(p.c + m * p.ldc + n0 + cv * VEC, v);
-      }
-    } else if constexpr (EPI == EPI_GLU) {
-      const GluOut<T>& g = p.glu;
-      if (g.a) {  // a = silu(h) * u for the tile's 64 features
-        for (int c = tid; c < EPI_ROWS * (BN / 2) / VEC; c += NTHREADS) {
-          const int row = c / (BN / 2 / VEC), cv = c % (BN / 2 / VEC);
-          const int64_t m = m0 + r0 + row;
-          if (m >= p.M) continue;
-          float v[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const float hh = Cs[row * SC + cv * VEC + e], uu = Cs[row * SC + BN / 2 + cv * VEC + e];
-            v[e] = hh * fast_sigmoid(hh) * uu;
-          }
-          st16_f<T>(g.a + m * g.ldf + n0 / 2 + cv * VEC, v);
-        }
-      }
-      if (g.hu) {  // h and u as computed, in the tile's own column order
-        for (int c = tid; c < EPI_ROWS * BN / VEC; c += NTHREADS) {
-          const int row = c / (BN / VEC), cv = c % (BN / VEC);
-          const int64_t m = m0 + r0 + row;
-          if (m >= p.M) continue;
-          float v[VEC];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
-          st16_f<T>(g.hu + m * 2 * g.ldf + n0 + cv * VEC, v);
-        }
-      }
-    } else if constexpr (EPI == EPI_GLU_BWD) {
-      // C = da over features n0 .. n0+BN-1; h, u of feature f sit at columns
-      // 128 (f / 64) + f % 64 and that + 64 of hu
-      const GluOut<T>& g = p.glu;
-      for (int c = tid; c < EPI_ROWS * BN / VEC; c += NTHREADS) {
-        const int row = c / (BN / VEC), cv = c % (BN / VEC);
-        const int64_t m = m0 + r0 + row;
-        if (m >= p.M) continue;
-        const int64_t f0 = n0 + cv * VEC;
-        const T* hp = g.hu + m * 2 * g.ldf + (f0 / 64) * 128 + f0 % 64;
-        float hh[VEC], uu[VEC], dh[VEC], du[VEC], av[VEC];
-        ld16_f<T>(hp, hh);
-        ld16_f<T>(hp + 64, uu);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float da = Cs[row * SC + cv * VEC + e];
-          const float sg = fast_sigmoid(hh[e]);
-          const float sh = hh[e] * sg;
-          dh[e] = da * uu[e] * (sg * (1.0f + hh[e] * (1.0f - sg)));
-          du[e] = da * sh;
-          av[e] = sh * uu[e];
-        }
-        st16_f<T>(g.dh + m * g.ldf + f0, dh);
-        st16_f<T>(g.du + m * g.ldf + f0, du);
-        st16_f<T>(g.a + m * g.ldf + f0, av);
-      }
-    } else if constexpr (EPI == EPI_CE) {
-      // four threads per row, 32 logits each: the tile's row max and sum of
-      // exp(logit - max), and the target's logit where the tile holds it
-      static_assert(EPI_ROWS * 4 == NTHREADS && BN == 128, "four threads per row");
-      const CeOut<T>& ce = p.ce;
-      const int row = tid >> 2, qq = tid & 3;
-      const int64_t m = m0 + r0 + row;
-      const float* cr = Cs + row * SC + qq * 32;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) mx = fmaxf(mx, cr[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
-      float se = 0.f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) se += fast_exp2((cr[j] - mx) * LOG2E_F);
-      se += __shfl_xor(se, 1);
-      se += __shfl_xor(se, 2);
-      if (m < p.M) {
-        if (qq == 0) {
-          float* pp = ce.part + (m * (p.N / BN) + n0 / BN) * 2;
-          pp[0] = mx;
-          pp[1] = se;
-        }
-        const int64_t t = (int64_t)ce.targets[m] - n0 - qq * 32;
-        if (t >= 0 && t < 32) ce.tgt[m] = cr[t];
-      }
-    } else if constexpr (EPI == EPI_CE_BWD) {
-      const CeOut<T>& ce = p.ce;
-      for (int c = tid; c < EPI_ROWS * BN / VEC; c += NTHREADS) {
-        const int row = c / (BN / VEC), cv = c % (BN / VEC);
-        const int64_t m = m0 + r0 + row;
-        if (m >= p.M) continue;
-        const float l = ce.lse[m], gg = ce.g[m];
-        const int64_t tcol = (int64_t)ce.targets[m] - n0 - cv * VEC;
-        float v[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float pr = fast_exp2((Cs[row * SC + cv * VEC + e] - l) * LOG2E_F) - (tcol == e ? 1.0f : 0.0f);
-          v[e] = pr * gg;
-        }
-        st16_f<T>(ce.dz + m * ce.ldz + n0 + cv * VEC, v);
-      }
+    if constexpr (EPI == EPI_STORE || EPI == EPI_GLU || EPI == EPI_GLU_BWD || EPI == EPI_CE || EPI == EPI_CE_BWD) {
+      epi_pass<T, BN, EPI, EPI_ROWS, NTHREADS>(p, Cs, m0 + r0, n0, tid);
     } else if constexpr (EPI == EPI_ACCUM) {
       if (pass) load_old(1);
 #pragma unroll
