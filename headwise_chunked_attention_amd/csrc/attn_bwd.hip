@@ -174,6 +174,9 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   int64_t q0 = k0;
   // One step on LDS buffer B (a compile-time constant, so the step's LDS
   // addresses need no per-step arithmetic).
+  // bf16: lane offsets of the dO^T / Q^T column reads, computed once
+  Col4Plan<L, ND> cplan;
+  if constexpr (sizeof(T) == 2) cplan.init();
   auto step = [&](auto bc, int64_t it) {
     constexpr int B = decltype(bc)::value;
     int nh_next = hh;
@@ -234,9 +237,18 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       const int row0 = qt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
       for (int j = 0; j < ND; ++j) {
-        const Frag<T> ado = frag_from_col4<T>(ld_col4<L>(dOs, row0, j * 32), ld_col4<L>(dOs, row0 + 8, j * 32));
+        Frag<T> ado, aq;
+        if constexpr (sizeof(T) == 2) {
+          // rows qt*32 + 16*s2 + ... of dO and Q at the precomputed lane offsets
+          const T* dOr = dOs + (qt * 32 + 16 * s2) * L::STRIDE;
+          const T* Qr = Qs + (qt * 32 + 16 * s2) * L::STRIDE;
+          ado = frag_from_col4<T>(ld_col4_at(dOr, cplan.off[0][j]), ld_col4_at(dOr, cplan.off[1][j]));
+          aq = frag_from_col4<T>(ld_col4_at(Qr, cplan.off[0][j]), ld_col4_at(Qr, cplan.off[1][j]));
+        } else {
+          ado = frag_from_col4<T>(ld_col4<L>(dOs, row0, j * 32), ld_col4<L>(dOs, row0 + 8, j * 32));
+          aq = frag_from_col4<T>(ld_col4<L>(Qs, row0, j * 32), ld_col4<L>(Qs, row0 + 8, j * 32));
+        }
         mma(dv[j], ado, pb);
-        const Frag<T> aq = frag_from_col4<T>(ld_col4<L>(Qs, row0, j * 32), ld_col4<L>(Qs, row0 + 8, j * 32));
         mma(dk[j], aq, sb);
       }
     }
@@ -389,6 +401,9 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
   }
   lds_barrier();
   // one key tile on LDS stage BUF (a compile-time constant: immediate LDS offsets)
+  // bf16: lane offsets of the K^T column reads, computed once
+  Col4Plan<L, ND> kplan;
+  if constexpr (sizeof(T) == 2) kplan.init();
   auto step = [&](auto bc, int64_t kt_i) {
     constexpr int buf = decltype(bc)::value;
     const int64_t k0 = kt_i * BC;
@@ -429,10 +444,17 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const Frag<T> sb = frag_from_acc<T>(dpacc, s2, 1.0f);
-          const int row0 = kt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
           for (int j = 0; j < ND; ++j) {
-            const Frag<T> a = frag_from_col4<T>(ld_col4<L>(Ks, row0, j * 32), ld_col4<L>(Ks, row0 + 8, j * 32));
+            Frag<T> a;
+            if constexpr (sizeof(T) == 2) {
+              // rows kt*32 + 16*s2 + ... of K at the precomputed lane offsets
+              const T* Kr = Ks + (kt * 32 + 16 * s2) * L::STRIDE;
+              a = frag_from_col4<T>(ld_col4_at(Kr, kplan.off[0][j]), ld_col4_at(Kr, kplan.off[1][j]));
+            } else {
+              const int row0 = kt * 32 + 16 * s2 + 4 * h;
+              a = frag_from_col4<T>(ld_col4<L>(Ks, row0, j * 32), ld_col4<L>(Ks, row0 + 8, j * 32));
+            }
             mma(dq[j], a, sb);
           }
         }

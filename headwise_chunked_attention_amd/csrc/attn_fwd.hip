@@ -162,6 +162,9 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
 #pragma unroll
   for (int e = 0; e < 16; ++e) init[e] = (MODE == 1) ? -base_row[0] : 0.f;
   if constexpr (MODE == 1) base = base_row[0];
+  // bf16: lane offsets of the V^T column reads, computed once
+  Col4Plan<typename G::L, ND> vplan;
+  if constexpr (sizeof(T) == 2) vplan.init();
   auto step = [&](auto bc, int64_t kt_i) {
     constexpr int buf = decltype(bc)::value;  // LDS stage (immediate offsets)
     const int64_t k0 = kt_i * BC;
@@ -260,14 +263,13 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
           } else {
             make_p0();
           }
-          // O^T += V^T P^T over the half's keys
+          // O^T += V^T P^T over the half's keys (rows kt*32 + 16*s2 + ... of V)
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            const int row0 = kt * 32 + 16 * s2 + 4 * h;
+            const T* Vr = Vs + (kt * 32 + 16 * s2) * G::L::STRIDE;
 #pragma unroll
             for (int j = 0; j < ND; ++j) {
-              const Frag<T> a = frag_from_col4<T>(ld_col4<typename G::L>(Vs, row0, j * 32),
-                                                  ld_col4<typename G::L>(Vs, row0 + 8, j * 32));
+              const Frag<T> a = frag_from_col4<T>(ld_col4_at(Vr, vplan.off[0][j]), ld_col4_at(Vr, vplan.off[1][j]));
               mma(oacc[0][j], a, pf[s2]);
             }
           }

@@ -238,6 +238,28 @@ template <class L, typename T> DEV typename Vec4<T>::type ld_col4(const T* X, in
   else return ld_col4_f32<L>(X, k0, c0);
 }
 
+// Column reads at precomputed lane offsets. A bf16 swizzled tile's swizzle
+// depends only on the low four bits of the row, so ld_col4(X, R + k, c0) with
+// R a multiple of 16 and k < 16 reads X + R * STRIDE + (the lane offset of
+// ld_col4(X, k, c0)): the lane offsets of the few (k, c0) a loop uses can be
+// computed once, and R * STRIDE becomes an immediate offset of the read.
+template <class L, int NJ>
+struct Col4Plan {
+  int off[2][NJ];  // lane element offsets for k = 4 * (lane / 32) + 8x, c0 = 32j
+  DEV void init() {
+    static_assert(L::SWZ, "bf16 swizzled tiles only");
+    const int l = lane_id(), Ln = l & 15, h = l >> 5;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) off[x][j] = L::idx(4 * h + 8 * x + (Ln >> 2), j * 32 + 16 * ((l >> 4) & 1) + 4 * (Ln & 3));
+  }
+};
+DEV bf16x4 ld_col4_at(const bf16* X, int off) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(X + off));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 template <typename T> DEV Frag<T> frag_from_col4(typename Vec4<T>::type lo, typename Vec4<T>::type hi);
 template <> DEV Frag<bf16> frag_from_col4<bf16>(bf16x4 a, bf16x4 b) {
   Frag<bf16> f;
