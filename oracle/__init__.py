@@ -1,5 +1,6 @@
 """CPU fp64 oracle for headwise-chunked causal RoPE/GQA attention, the
-sequence-tiled gated-SiLU MLP and the sequence-tiled cross-entropy loss.
+sequence-tiled gated-SiLU MLP, the sequence-tiled cross-entropy loss and the
+checkpointed pre-norm transformer block built from the first two.
 
 TEST INFRASTRUCTURE ONLY. Nothing in the product package imports this; only
 ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -33,4 +34,8 @@ from .loss import (  # noqa: F401
     ce_bwd,
     ce_rows,
     ce_dh_rows,
+)
+from .block import (  # noqa: F401
+    block_fwd,
+    block_bwd,
 )
