@@ -22,6 +22,28 @@ _DTYPES = {torch.float32: UPIPE_F32, torch.bfloat16: UPIPE_BF16}
 _lib = None
 
 
+class BlockShape(ctypes.Structure):
+    """upipe_block_shape_t."""
+    _fields_ = [("n_tokens", ctypes.c_int64), ("d_model", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+                ("tile_tokens", ctypes.c_int64), ("n_q_heads", ctypes.c_int), ("n_kv_heads", ctypes.c_int),
+                ("head_dim", ctypes.c_int), ("chunk_heads", ctypes.c_int), ("rope_theta", ctypes.c_double),
+                ("norm_eps", ctypes.c_float), ("qk_norm_eps", ctypes.c_float)]
+
+
+_BLOCK_TENSORS = ("attn_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "mlp_norm", "w_gate", "w_up",
+                  "w_down")
+
+
+class BlockWeights(ctypes.Structure):
+    """upipe_block_weights_t (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in _BLOCK_TENSORS]
+
+
+class BlockGrads(ctypes.Structure):
+    """upipe_block_grads_t (device pointers to fp32)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in _BLOCK_TENSORS]
+
+
 class UpipeError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
@@ -62,6 +84,14 @@ def load():
     lib.upipe_loss_fwd.restype = i32
     lib.upipe_loss_bwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.upipe_loss_bwd.restype = i32
+    bp = ctypes.POINTER(BlockShape)
+    lib.upipe_block_workspace_bytes.argtypes = [bp, i32, i32, i32]
+    lib.upipe_block_workspace_bytes.restype = sz
+    lib.upipe_block_fwd.argtypes = [i32, bp, vp, ctypes.POINTER(BlockWeights), vp, vp, vp, vp, sz, vp]
+    lib.upipe_block_fwd.restype = i32
+    lib.upipe_block_bwd.argtypes = [i32, bp, vp, ctypes.POINTER(BlockWeights), vp, vp, vp, vp,
+                                    ctypes.POINTER(BlockGrads), vp, sz, vp]
+    lib.upipe_block_bwd.restype = i32
     lib.upipe_strerror.argtypes = [i32]
     lib.upipe_strerror.restype = ctypes.c_char_p
     lib.upipe_version.argtypes = []
@@ -231,7 +261,7 @@ def attn_bwd(x, wq, wk, wv, wo, dy, lse, *, n_q_heads, n_kv_heads, head_dim, rop
 
 
 KERNEL_KINDS = ("projection", "out_gemm", "attn_fwd", "attn_recompute", "attn_bwd_dkdv", "attn_bwd_dq", "wgrad",
-                "other", "mlp_gemm", "mlp_wgrad", "loss_gemm", "loss_wgrad")
+                "other", "mlp_gemm", "mlp_wgrad", "loss_gemm", "loss_wgrad", "block_norm")
 
 
 def loss_workspace_bytes(n_tokens, d_model, vocab, tile_tokens, dtype, backward) -> int:
@@ -344,6 +374,106 @@ def mlp_bwd(x, w_gate, w_up, w_down, dy, *, tile_tokens, out=None, workspace=Non
     if rc != 0:
         raise UpipeError(rc, "upipe_mlp_bwd")
     return dx, dwg, dwu, dwd
+
+
+def block_shape(n_tokens, d_model, d_ff, tile_tokens, n_q_heads, n_kv_heads, head_dim, chunk_heads, rope_theta,
+                norm_eps=1e-5, qk_norm_eps=1e-6) -> BlockShape:
+    return BlockShape(int(n_tokens), int(d_model), int(d_ff), int(tile_tokens), int(n_q_heads), int(n_kv_heads),
+                      int(head_dim), int(chunk_heads), float(rope_theta), float(norm_eps), float(qk_norm_eps))
+
+
+def block_workspace_bytes(shape: BlockShape, qk_norm, dtype, backward) -> int:
+    return int(load().upipe_block_workspace_bytes(ctypes.byref(shape), int(bool(qk_norm)), dtype_code(dtype),
+                                                   int(bool(backward))))
+
+
+def _block_weight_shapes(s: BlockShape):
+    D, F, d = s.d_model, s.d_ff, s.head_dim
+    return {"attn_norm": (D,), "wq": (s.n_q_heads * d, D), "wk": (s.n_kv_heads * d, D),
+            "wv": (s.n_kv_heads * d, D), "wo": (D, s.n_q_heads * d), "q_norm": (d,), "k_norm": (d,),
+            "mlp_norm": (D,), "w_gate": (F, D), "w_up": (F, D), "w_down": (D, F)}
+
+
+def _block_weights(shape: BlockShape, weights: dict, dt, dev):
+    if (weights.get("q_norm") is None) != (weights.get("k_norm") is None):
+        raise ValueError("q_norm and k_norm must both be given or both be None")
+    shapes = _block_weight_shapes(shape)
+    w = BlockWeights()
+    for n in _BLOCK_TENSORS:
+        t = weights.get(n)
+        if t is None and n in ("q_norm", "k_norm"):
+            continue
+        _check(t, n, dt, shapes[n], dev)
+        setattr(w, n, t.data_ptr())
+    return w
+
+
+def block_fwd(x, weights: dict, shape: BlockShape, *, y=None, h_mid=None, lse=None, workspace=None, stream=None):
+    """Forward of the pre-norm transformer block (upipe_block_fwd).
+
+    ``weights`` maps attn_norm, wq, wk, wv, wo, [q_norm, k_norm], mlp_norm,
+    w_gate, w_up, w_down to tensors of x's dtype. h_mid and lse are optional
+    outputs (pass tensors to keep them). Returns (y, h_mid, lse)."""
+    lib = load()
+    dev, dt = x.device, x.dtype
+    N, D = shape.n_tokens, shape.d_model
+    _check(x, "x", dt, (N, D), dev)
+    w = _block_weights(shape, weights, dt, dev)
+    y = torch.empty((N, D), dtype=dt, device=dev) if y is None else y
+    _check(y, "y", dt, (N, D), dev)
+    if h_mid is not None:
+        _check(h_mid, "h_mid", dt, (N, D), dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (shape.n_q_heads, N), dev)
+    qk = weights.get("q_norm") is not None
+    if workspace is None:
+        workspace = alloc_workspace(block_workspace_bytes(shape, qk, dt, False), dev)
+    rc = lib.upipe_block_fwd(dtype_code(dt), ctypes.byref(shape), _ptr(x), ctypes.byref(w), _ptr(y), _ptr(h_mid),
+                             _ptr(lse), _ptr(workspace), workspace.numel(), _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_block_fwd")
+    return y, h_mid, lse
+
+
+def block_bwd(x, weights: dict, shape: BlockShape, dy, *, h_mid=None, lse=None, dx=None, grads=None,
+              workspace=None, stream=None):
+    """Backward of the block (upipe_block_bwd): returns (dx, grads) with grads a
+    dict of fp32 tensors named like ``weights``. h_mid and lse: both None
+    (recompute from x) or both from block_fwd."""
+    lib = load()
+    dev, dt = x.device, x.dtype
+    N, D = shape.n_tokens, shape.d_model
+    _check(x, "x", dt, (N, D), dev)
+    _check(dy, "dy", dt, (N, D), dev)
+    w = _block_weights(shape, weights, dt, dev)
+    if (h_mid is None) != (lse is None):
+        raise ValueError("h_mid and lse must both be given or both be None")
+    if h_mid is not None:
+        _check(h_mid, "h_mid", dt, (N, D), dev)
+        _check(lse, "lse", torch.float32, (shape.n_q_heads, N), dev)
+    qk = weights.get("q_norm") is not None
+    shapes = _block_weight_shapes(shape)
+    f32 = torch.float32
+    if grads is None:
+        grads = {n: torch.empty(shapes[n], dtype=f32, device=dev) for n in _BLOCK_TENSORS
+                 if qk or n not in ("q_norm", "k_norm")}
+    g = BlockGrads()
+    for n in _BLOCK_TENSORS:
+        t = grads.get(n)
+        if t is None and not qk and n in ("q_norm", "k_norm"):
+            continue
+        _check(t, "grad " + n, f32, shapes[n], dev)
+        setattr(g, n, t.data_ptr())
+    dx = torch.empty((N, D), dtype=dt, device=dev) if dx is None else dx
+    _check(dx, "dx", dt, (N, D), dev)
+    if workspace is None:
+        workspace = alloc_workspace(block_workspace_bytes(shape, qk, dt, True), dev)
+    rc = lib.upipe_block_bwd(dtype_code(dt), ctypes.byref(shape), _ptr(x), ctypes.byref(w), _ptr(h_mid), _ptr(lse),
+                             _ptr(dy), _ptr(dx), ctypes.byref(g), _ptr(workspace), workspace.numel(),
+                             _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_block_bwd")
+    return dx, grads
 
 
 def profile_start():

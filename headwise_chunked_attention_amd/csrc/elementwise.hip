@@ -1,6 +1,7 @@
 // Element-wise and data-movement kernels of the chunk loop: the gradient
 // finish of the rotated/normalised heads (RoPE transpose, RMSNorm backward,
-// cast), weight-slice transposes and fp32 fills.
+// cast), weight-slice transposes and fp32 fills; the row RMSNorm of the
+// transformer block (forward with a fused residual add, and backward).
 #include <math.h>
 
 #include "common.h"
@@ -73,6 +74,133 @@ __global__ __launch_bounds__(256) void grad_finish_kernel(const GradFinish<T> p)
   if (p.gamma && p.dgamma && act) {
     atomicAdd(p.dgamma + i, dg0);
     atomicAdd(p.dgamma + i + D / 2, dg1);
+  }
+}
+
+// Sum over the 256 threads of a block; every thread gets the total. red holds
+// one partial per wave; the trailing barrier lets the caller reuse red.
+template <int NVAL>
+DEV void block_sum(float (&v)[NVAL], float (*red)[4]) {
+#pragma unroll
+  for (int k = 0; k < NVAL; ++k) v[k] = wave_sum(v[k]);
+  if (lane_id() == 0)
+#pragma unroll
+    for (int k = 0; k < NVAL; ++k) red[k][threadIdx.x >> 6] = v[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NVAL; ++k) v[k] = red[k][0] + red[k][1] + red[k][2] + red[k][3];
+  __syncthreads();
+}
+
+// Row RMSNorm: one 256-thread block per row (grid-stride over rows). Thread t
+// owns the 16-byte vectors t, t + 256, ... of the row (NV of them, the last
+// ones possibly past D), kept in registers between the reduction and the store.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void row_norm_kernel(const RowNorm<T> p) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  __shared__ float red[1][4];
+  const int tid = threadIdx.x;
+  float gm[NV][VEC];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t c = (int64_t)(tid + j * 256) * VEC;
+    if (c < p.D) ld16_f<T>(p.gamma + c, gm[j]);
+  }
+  for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
+    const int64_t base = row * p.D;
+    float u[NV][VEC];
+    float ss[1] = {0.f};
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c = (int64_t)(tid + j * 256) * VEC;
+      if (c >= p.D) continue;
+      ld16_f<T>(p.x + base + c, u[j]);
+      if (p.r) {
+        float t[VEC];
+        ld16_f<T>(p.r + base + c, t);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) u[j][e] += t[e];
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        u[j][e] = to_f<T>(from_f<T>(u[j][e]));  // the value the io dtype stores
+        ss[0] += u[j][e] * u[j][e];
+      }
+    }
+    block_sum<1>(ss, red);
+    const float rs = 1.0f / sqrtf(ss[0] / (float)p.D + p.eps);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c = (int64_t)(tid + j * 256) * VEC;
+      if (c >= p.D) continue;
+      if (p.u_out) st16_f<T>(p.u_out + base + c, u[j]);
+      if (p.u_out2) st16_f<T>(p.u_out2 + base + c, u[j]);
+      float n[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) n[e] = gm[j][e] * (u[j][e] * rs);
+      st16_f<T>(p.n_out + base + c, n);
+    }
+  }
+}
+
+// Row RMSNorm backward, same thread layout; dgamma partials stay in registers
+// over the block's rows and are added once per block.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void row_norm_bwd_kernel(const RowNormBwd<T> p) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x;
+  float gm[NV][VEC], dg[NV][VEC];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t c = (int64_t)(tid + j * 256) * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dg[j][e] = 0.f;
+    if (c < p.D) ld16_f<T>(p.gamma + c, gm[j]);
+  }
+  const float inv_d = 1.0f / (float)p.D;
+  for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
+    const int64_t base = row * p.D;
+    float u[NV][VEC], g[NV][VEC], rv[NV][VEC];
+    float s[2] = {0.f, 0.f};  // sum u^2, sum gamma g u
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c = (int64_t)(tid + j * 256) * VEC;
+      if (c >= p.D) continue;
+      ld16_f<T>(p.u + base + c, u[j]);
+      ld16_f<T>(p.g + base + c, g[j]);
+      if (p.res) ld16_f<T>(p.res + base + c, rv[j]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        s[0] += u[j][e] * u[j][e];
+        s[1] += gm[j][e] * g[j][e] * u[j][e];
+      }
+    }
+    block_sum<2>(s, red);
+    const float rs = 1.0f / sqrtf(s[0] * inv_d + p.eps);
+    const float k = rs * (s[1] * rs) * inv_d;  // rstd * sum(gamma g uh) / D
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c = (int64_t)(tid + j * 256) * VEC;
+      if (c >= p.D) continue;
+      float o[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float uh = u[j][e] * rs;
+        o[e] = rs * gm[j][e] * g[j][e] - uh * k + (p.res ? rv[j][e] : 0.f);
+        dg[j][e] += g[j][e] * uh;
+      }
+      st16_f<T>(p.out + base + c, o);
+    }
+  }
+  if (p.dgamma) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t c = (int64_t)(tid + j * 256) * VEC;
+      if (c >= p.D) continue;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) atomicAdd(p.dgamma + c + e, dg[j][e]);
+    }
   }
 }
 
@@ -161,6 +289,50 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Vectors per thread for rows of D elements: the smallest of 1, 2, 4, 8 that covers D.
+template <typename T>
+int row_norm_nv(int64_t D) {
+  const int64_t per = 256 * (16 / (int64_t)sizeof(T));
+  for (int nv = 1; nv <= 8; nv *= 2)
+    if (D <= per * nv) return nv;
+  return 0;
+}
+
+template <typename T>
+hipError_t launch_row_norm(const RowNorm<T>& p, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  if (p.D <= 0 || p.D % (16 / (int64_t)sizeof(T)) || p.D > ROW_NORM_MAX_D) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(p.rows < 8192 ? p.rows : 8192);
+  switch (row_norm_nv<T>(p.D)) {
+    case 1: hipLaunchKernelGGL((row_norm_kernel<T, 1>), dim3(grid), dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((row_norm_kernel<T, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((row_norm_kernel<T, 4>), dim3(grid), dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((row_norm_kernel<T, 8>), dim3(grid), dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_row_norm_bwd(const RowNormBwd<T>& p, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  if (p.D <= 0 || p.D % (16 / (int64_t)sizeof(T)) || p.D > ROW_NORM_MAX_D) return hipErrorInvalidValue;
+  // fewer blocks than the forward: each block adds its dgamma partials once
+  const unsigned grid = (unsigned)(p.rows < 1024 ? p.rows : 1024);
+  switch (row_norm_nv<T>(p.D)) {
+    case 1: hipLaunchKernelGGL((row_norm_bwd_kernel<T, 1>), dim3(grid), dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((row_norm_bwd_kernel<T, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((row_norm_bwd_kernel<T, 4>), dim3(grid), dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((row_norm_bwd_kernel<T, 8>), dim3(grid), dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t launch_row_norm<bf16>(const RowNorm<bf16>&, hipStream_t);
+template hipError_t launch_row_norm<float>(const RowNorm<float>&, hipStream_t);
+template hipError_t launch_row_norm_bwd<bf16>(const RowNormBwd<bf16>&, hipStream_t);
+template hipError_t launch_row_norm_bwd<float>(const RowNormBwd<float>&, hipStream_t);
 template hipError_t launch_grad_finish<bf16>(const GradFinish<bf16>&, int, hipStream_t);
 template hipError_t launch_grad_finish<float>(const GradFinish<float>&, int, hipStream_t);
 template hipError_t launch_transpose<bf16>(const bf16*, int64_t, int64_t, int64_t, bf16*, int64_t, hipStream_t);

@@ -157,6 +157,12 @@ DEV void epi_pass(const GemmNT<T>& p, const float* Cs, int64_t mr0, int64_t n0, 
       float v[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
+      if (p.add) {  // residual: read before the store, so add may be c itself
+        float o[VEC];
+        ld16_f<T>(p.add + m * p.ld_add + n0 + cv * VEC, o);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] += o[e];
+      }
       st16_f<T>(p.c + m * p.ldc + n0 + cv * VEC, v);
     }
   } else if constexpr (EPI == EPI_GLU) {

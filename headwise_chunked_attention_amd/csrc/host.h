@@ -64,6 +64,11 @@ hipError_t timed(int kind, double flops, hipStream_t st, F&& launch) {
 }
 
 }  // namespace host
+
+// The attention entry points' checks of their scalar arguments (shape,
+// rope_theta, q/k norm epsilon): UPIPE_OK or the code they would return.
+int attn_check_args(int dtype, int64_t N, int64_t D, int Hq, int Hkv, int d, double theta, int C, float eps);
+
 }  // namespace upipe
 
 #define HIP_TRY(x)                                 \

@@ -59,7 +59,8 @@ struct CeOut {
 //   A(m,k) = a + (k / a_kblk) * a_kblk_stride + m * lda + (k % a_kblk)
 //   B(n,k) = b[s] + (n - seg_begin(s)) * ldb[s] + k for the segment s holding n
 // EPI_ACCUM:  c[m * ldc + n] = (accumulate ? c : 0) + C   (rows m < M)
-// EPI_STORE:  c[m * ldc + n] = C (rows m < M); long k (128-byte k rows)
+// EPI_STORE:  c[m * ldc + n] = C (+ add[m * ld_add + n] if add; add may be c)
+//             (rows m < M); long k (128-byte k rows)
 // EPI_HEADS:  head-wise epilogue per segment (see HeadOut), rows m < Np.
 // EPI_GLU, EPI_GLU_BWD: see GluOut. EPI_CE, EPI_CE_BWD: see CeOut.
 template <typename T>
@@ -82,6 +83,8 @@ struct GemmNT {
   double log2_theta;
   GluOut<T> glu;
   CeOut<T> ce;
+  const T* add;
+  int64_t ld_add;
 };
 
 // out[m*ldm + n*ldn] += sum_{k in split} A(k,m) B(k,n)   (fp32 atomics)
@@ -169,6 +172,42 @@ struct GradFinish {
   double log2_theta;
 };
 
+// RMSNorm over rows of D elements (row stride D), optionally after a residual add:
+//   u = x + r (r may be null), rounded to the io dtype;
+//   u_out, u_out2 = u (either may be null, u_out may alias x or r);
+//   n_out = gamma * u / sqrt(mean(u^2) + eps).
+template <typename T>
+struct RowNorm {
+  const T* x;
+  const T* r;
+  const T* gamma;
+  T* u_out;
+  T* u_out2;
+  T* n_out;
+  int64_t rows, D;
+  float eps;
+};
+
+// Backward of RowNorm's n_out for upstream gradient g, plus a residual gradient:
+//   out = res + rstd (gamma g - uh sum(gamma g uh) / D),  uh = u rstd  (res may be null);
+//   dgamma[c] += sum over rows of g uh (fp32 atomics). out may alias u, g or res.
+template <typename T>
+struct RowNormBwd {
+  const T* u;
+  const T* g;
+  const T* gamma;
+  const T* res;
+  T* out;
+  float* dgamma;
+  int64_t rows, D;
+  float eps;
+};
+
+// Largest D the row kernels take: each thread keeps its share of a row in registers.
+constexpr int64_t ROW_NORM_MAX_D = 8192;
+
+template <typename T> hipError_t launch_row_norm(const RowNorm<T>& p, hipStream_t s);
+template <typename T> hipError_t launch_row_norm_bwd(const RowNormBwd<T>& p, hipStream_t s);
 template <typename T> hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s);
 template <typename T> hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s);
 template <typename T> hipError_t launch_attn_fwd(const AttnFwd<T>& p, int head_dim, int mode, hipStream_t s);

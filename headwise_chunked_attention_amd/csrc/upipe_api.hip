@@ -483,6 +483,17 @@ int check_ws(const Shape& s, bool bwd, const void* ws, size_t bytes) {
 
 }  // namespace
 
+namespace upipe {
+int attn_check_args(int dtype, int64_t N, int64_t D, int Hq, int Hkv, int d, double theta, int C, float eps) {
+  Shape s;
+  const int rc = check_shape(dtype, N, D, Hq, Hkv, d, C, &s);
+  if (rc) return rc;
+  if (!(theta > 0.0) || !isfinite(theta)) return UPIPE_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return UPIPE_ERR_INVALID_ARG;
+  return UPIPE_OK;
+}
+}  // namespace upipe
+
 extern "C" {
 
 size_t upipe_attn_workspace_bytes(int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,

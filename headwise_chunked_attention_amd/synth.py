@@ -8,7 +8,8 @@ input streams.
 Recipe (stated once, used everywhere):
   * every tensor has an integer "tensor id": x 0, Wq 1, Wk 2, Wv 3, Wo 4,
     dY 5, q-norm gamma 6, k-norm gamma 7, MLP gate/up/down weights 8/9/10,
-    LM-head weight 11, loss targets 12, per-token loss gradients 13;
+    LM-head weight 11, loss targets 12, per-token loss gradients 13, the
+    block's attention-norm and MLP-norm gammas 14/15;
   * a 2-D tensor is drawn in blocks of ``ROW_BLOCK`` rows; block ``b`` of
     tensor ``t`` under run seed ``s`` uses
     ``numpy.random.default_rng(SeedSequence([s, t, b]))`` and draws
@@ -30,7 +31,8 @@ ROW_BLOCK = 8192
 GEN_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 TENSOR_IDS = {"x": 0, "wq": 1, "wk": 2, "wv": 3, "wo": 4, "dy": 5, "q_norm": 6, "k_norm": 7,
-              "wg": 8, "wu": 9, "wd": 10, "w_lm": 11, "targets": 12, "g_loss": 13}
+              "wg": 8, "wu": 9, "wd": 10, "w_lm": 11, "targets": 12, "g_loss": 13,
+              "attn_norm": 14, "mlp_norm": 15}
 
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
@@ -184,3 +186,25 @@ class LossInputs:
         self.targets = rng.integers(0, vocab, N).astype(np.int32)
         rng = _block_rng(seed, TENSOR_IDS["g_loss"], 0)
         self.g = (rng.uniform(0.5, 1.5, N) / N).astype(np.float32)
+
+
+class BlockInputs:
+    """Inputs of one transformer-block problem, as float32 host arrays: the
+    attention layer's (``LayerInputs``), the MLP weights (as ``MlpInputs``)
+    and the two d_model-long norm weights ``g_attn``, ``g_mlp``
+    (``gen_gamma``: ones, or 1 + 0.1 N(0,1))."""
+
+    def __init__(self, n_tokens: int, d_model: int, d_ff: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                 dtype: str, seed: int = 0, w_std: float = 0.02, qk_norm: str | None = None,
+                 norm: str = "random", with_x: bool = True, with_dy: bool = True):
+        lay = LayerInputs(n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, dtype, seed=seed, w_std=w_std,
+                          qk_norm=qk_norm, with_x=with_x, with_dy=with_dy)
+        self.n_tokens, self.d_model, self.d_ff, self.dtype, self.seed = n_tokens, d_model, d_ff, dtype, seed
+        for k in ("x", "dy", "wq", "wk", "wv", "wo", "q_norm", "k_norm"):
+            setattr(self, k, getattr(lay, k))
+        D, F = d_model, d_ff
+        self.g_attn = gen_gamma("attn_norm", D, norm, dtype, seed)
+        self.g_mlp = gen_gamma("mlp_norm", D, norm, dtype, seed)
+        self.wg = gen_rows("wg", F, D, w_std, dtype, seed)
+        self.wu = gen_rows("wu", F, D, w_std, dtype, seed)
+        self.wd = gen_rows("wd", D, F, w_std, dtype, seed)

@@ -214,6 +214,83 @@ int upipe_loss_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int64
                    size_t workspace_bytes, void* stream);
 
 /*
+ * One pre-norm transformer block (Llama style, no biases) around the
+ * attention op and the tiled MLP above, trained with activation
+ * checkpointing: the talk recomputes each block's activations from its input
+ * in the backward pass and keeps (or offloads to the CPU) only the block
+ * inputs ("Road to 5 Million Tokens", talk transcript, the memory-
+ * optimization progression; liquidgold.cc notes, "Progression of
+ * Techniques", items 4 and 5). The pages do not write the block out; this is
+ * the plainest reading for the Llama models they train:
+ *   a = rmsnorm(x; attn_norm)      h = x + attention(a)
+ *   b = rmsnorm(h; mlp_norm)       y = h + mlp(b)
+ *   rmsnorm(u; g) = g * u / sqrt(mean over d_model of u^2 + norm_eps)
+ * with attention as upipe_attn_fwd (chunk_heads query heads at a time, q/k
+ * norm optional) and mlp as upipe_mlp_fwd (tile_tokens rows at a time).
+ * The residual stream h is rounded to the io dtype before its norm, as a
+ * stored activation would be. The MLP half runs tile by tile: per tile, the
+ * residual add, the norm, the MLP and the second residual add (fused into the
+ * MLP's last product); no [N][d_ff] buffer exists.
+ *
+ * Backward, from the block input alone (h_mid and lse NULL): the norm of x
+ * and the attention forward are recomputed (the talk's checkpointing), then
+ * per tile the MLP half's backward, then the attention backward (which
+ * recomputes O from the lse, as upipe_attn_bwd does) and the first norm's
+ * backward. With h_mid and lse from the forward, the attention forward is
+ * not rerun. Every gradient is overwritten.
+ *
+ *   x, y, dy, dx, h_mid [N][D] io dtype; lse [Hq][N] fp32
+ *   weights: attn_norm, mlp_norm [D]; wq, wk, wv, wo, q_norm, k_norm as in
+ *   upipe_attn_fwd; w_gate, w_up, w_down as in upipe_mlp_fwd (io dtype)
+ *   grads: the same shapes in fp32 (q_norm, k_norm iff those weights are given)
+ * Supported: the attention op's and the MLP's shapes, and d_model <= 8192.
+ * Pointers, streams, validation and error codes follow the conventions
+ * above; the workspace must hold upipe_block_workspace_bytes(...) bytes.
+ */
+typedef struct {
+  int64_t n_tokens, d_model, d_ff, tile_tokens;
+  int n_q_heads, n_kv_heads, head_dim, chunk_heads;
+  double rope_theta;
+  float norm_eps;    /* the block's two norms over d_model */
+  float qk_norm_eps; /* the per-head q/k norm (when its weights are given) */
+} upipe_block_shape_t;
+
+typedef struct {
+  const void* attn_norm;
+  const void *wq, *wk, *wv, *wo;
+  const void *q_norm, *k_norm; /* both NULL: no q/k norm */
+  const void* mlp_norm;
+  const void *w_gate, *w_up, *w_down;
+} upipe_block_weights_t;
+
+typedef struct {
+  float* attn_norm;
+  float *wq, *wk, *wv, *wo;
+  float *q_norm, *k_norm;
+  float* mlp_norm;
+  float *w_gate, *w_up, *w_down;
+} upipe_block_grads_t;
+
+/* Workspace bytes for upipe_block_fwd (backward = 0) or upipe_block_bwd
+ * (backward = 1); 0 when the entry point would reject the arguments. */
+size_t upipe_block_workspace_bytes(const upipe_block_shape_t* shape, int qk_norm, upipe_dtype_t dtype,
+                                   int backward);
+
+/* Forward: y (out). h_mid (out, may be NULL) = the residual stream after
+ * the attention; lse (out, may be NULL) = the attention's log-sum-exps. */
+int upipe_block_fwd(upipe_dtype_t dtype, const upipe_block_shape_t* shape, const void* x,
+                    const upipe_block_weights_t* w, void* y, void* h_mid, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward for upstream gradient dy: dx and every weight gradient (out).
+ * h_mid and lse: both NULL (recompute from x) or both as the forward wrote
+ * them for the same inputs. */
+int upipe_block_bwd(upipe_dtype_t dtype, const upipe_block_shape_t* shape, const void* x,
+                    const upipe_block_weights_t* w, const void* h_mid, const float* lse,
+                    const void* dy, void* dx, const upipe_block_grads_t* grads, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * Optional per-kernel timing (for benchmarks and profilers; off by default).
  * While enabled, every kernel the library enqueues is bracketed by two
  * hipEvents on the caller's stream, and its algorithmic work (flops of the
@@ -238,7 +315,8 @@ enum {
   UPIPE_KERNEL_MLP_WGRAD = 9,       /* MLP weight-gradient GEMMs */
   UPIPE_KERNEL_LOSS_GEMM = 10,      /* LM-head logits (loss epilogues), their reduction, dh */
   UPIPE_KERNEL_LOSS_WGRAD = 11,     /* LM-head weight-gradient GEMMs */
-  UPIPE_KERNEL_KINDS = 12
+  UPIPE_KERNEL_BLOCK_NORM = 12,     /* the block's row RMSNorms (forward, backward) */
+  UPIPE_KERNEL_KINDS = 13
 };
 int upipe_profile_start(void);
 int upipe_profile_stop(double* total_ms, int64_t* launches, double* flops, int n_kinds);

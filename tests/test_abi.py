@@ -20,7 +20,8 @@ def test_exports_every_header_symbol(lib):
     assert set(names) == {"upipe_attn_workspace_bytes", "upipe_choose_chunk_heads", "upipe_attn_fwd",
                           "upipe_attn_bwd", "upipe_strerror", "upipe_version", "upipe_profile_start",
                           "upipe_profile_stop", "upipe_mlp_workspace_bytes", "upipe_mlp_fwd", "upipe_mlp_bwd",
-                          "upipe_loss_workspace_bytes", "upipe_loss_fwd", "upipe_loss_bwd"}
+                          "upipe_loss_workspace_bytes", "upipe_loss_fwd", "upipe_loss_bwd",
+                          "upipe_block_workspace_bytes", "upipe_block_fwd", "upipe_block_bwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.upipe_version() == 100
@@ -310,3 +311,86 @@ def test_loss_validation_errors(lib):
     assert bwd(g=None) == INVALID
     assert bwd(dw=P + 8) == ALIGN
     assert bwd(wsb=api.loss_workspace_bytes(300, 256, 1024, 128, "fp32", True) - 256) == WORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# checkpointed transformer block
+# ---------------------------------------------------------------------------
+def _r256(b):
+    return (b + 255) // 256 * 256
+
+
+def _expected_block_ws(N, D, F, T, hq, hkv, d, C, norm, dt, es, bwd):
+    rows = min(T, (N + 127) // 128 * 128)
+    nd, td = _r256(N * D * es), _r256(rows * D * es)
+    t = nd + td + _r256(hq * N * 4)
+    if bwd:
+        t += nd + td
+    stage = max(_expected_ws(N, D, hq, hkv, d, C, norm, es, False), _expected_mlp_ws(N, D, F, T, es, bwd))
+    if bwd:
+        stage = max(stage, _expected_ws(N, D, hq, hkv, d, C, norm, es, True))
+    return t + _r256(stage)
+
+
+@pytest.mark.parametrize("N,D,F,T,hq,hkv,d,C,norm", [(300, 256, 384, 128, 4, 2, 64, 2, False),
+                                                    (131072, 4096, 14336, 4096, 4, 1, 128, 1, False),
+                                                    (1000, 1024, 2816, 256, 8, 2, 128, 4, True)])
+def test_block_workspace_formula(N, D, F, T, hq, hkv, d, C, norm):
+    s = api.block_shape(N, D, F, T, hq, hkv, d, C, 5e5)
+    for dt, es in (("fp32", 4), ("bf16", 2)):
+        for bwd in (False, True):
+            want = _expected_block_ws(N, D, F, T, hq, hkv, d, C, norm, dt, es, bwd)
+            assert api.block_workspace_bytes(s, norm, dt, bwd) == want
+
+
+def test_block_workspace_rejects_bad_shapes():
+    good = dict(n_tokens=300, d_model=256, d_ff=384, tile_tokens=128, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                chunk_heads=2, rope_theta=1e4)
+    assert api.block_workspace_bytes(api.block_shape(**good), False, "bf16", True) > 0
+    for k, v in (("n_tokens", 0), ("d_model", 200), ("d_ff", 200), ("tile_tokens", 64), ("head_dim", 96),
+                 ("chunk_heads", 3), ("n_kv_heads", 3), ("rope_theta", 0.0), ("d_model", 8192 + 128)):
+        bad = dict(good, **{k: v})
+        assert api.block_workspace_bytes(api.block_shape(**bad), False, "bf16", True) == 0, k
+    assert api.block_workspace_bytes(api.block_shape(**good, norm_eps=-1.0), False, "bf16", False) == 0
+    # d_model 8192 (the largest the row norm takes) is accepted
+    assert api.block_workspace_bytes(api.block_shape(**dict(good, d_model=8192)), False, "fp32", True) > 0
+
+
+def _block_call(lib, bwd=False, shape=None, weights=None, grads=None, **kw):
+    s = shape or api.block_shape(300, 256, 384, 128, 4, 2, 64, 2, 1e4)
+    w = weights or api.BlockWeights(**{n: P for n in api._BLOCK_TENSORS if n not in ("q_norm", "k_norm")})
+    a = dict(dtype=1, x=P, y=P, h=None, lse=None, dy=P, dx=P, ws=P, wsb=1 << 40)
+    a.update(kw)
+    if not bwd:
+        return lib.upipe_block_fwd(a["dtype"], ctypes.byref(s), a["x"], ctypes.byref(w), a["y"], a["h"], a["lse"],
+                                   a["ws"], a["wsb"], None)
+    g = grads or api.BlockGrads(**{n: P for n in api._BLOCK_TENSORS if n not in ("q_norm", "k_norm")})
+    return lib.upipe_block_bwd(a["dtype"], ctypes.byref(s), a["x"], ctypes.byref(w), a["h"], a["lse"], a["dy"],
+                               a["dx"], ctypes.byref(g), a["ws"], a["wsb"], None)
+
+
+def test_block_validation_errors(lib):
+    full = {n: P for n in api._BLOCK_TENSORS if n not in ("q_norm", "k_norm")}
+    assert _block_call(lib, dtype=7) == INVALID
+    assert _block_call(lib, x=None) == INVALID
+    assert _block_call(lib, y=P + 2) == ALIGN
+    assert _block_call(lib, h=P + 8) == ALIGN
+    assert _block_call(lib, shape=api.block_shape(300, 256, 384, 100, 4, 2, 64, 2, 1e4)) == UNSUPPORTED
+    assert _block_call(lib, shape=api.block_shape(300, 256, 384, 128, 4, 2, 64, 3, 1e4)) == UNSUPPORTED
+    assert _block_call(lib, shape=api.block_shape(0, 256, 384, 128, 4, 2, 64, 2, 1e4)) == INVALID
+    assert _block_call(lib, weights=api.BlockWeights(**dict(full, w_up=None))) == INVALID
+    assert _block_call(lib, weights=api.BlockWeights(**dict(full, q_norm=P))) == INVALID  # k_norm missing
+    assert _block_call(lib, weights=api.BlockWeights(**dict(full, mlp_norm=P + 4))) == ALIGN
+    need = api.block_workspace_bytes(api.block_shape(300, 256, 384, 128, 4, 2, 64, 2, 1e4), False, "bf16", False)
+    assert _block_call(lib, wsb=need - 1) == WORKSPACE
+    assert _block_call(lib, ws=None) == WORKSPACE
+    assert _block_call(lib, ws=P + 16) == ALIGN
+    # backward: h_mid and lse together, gradients complete, q/k norm grads only with q/k norm
+    assert _block_call(lib, bwd=True, h=P) == INVALID
+    assert _block_call(lib, bwd=True, lse=P) == INVALID
+    assert _block_call(lib, bwd=True, dy=None) == INVALID
+    assert _block_call(lib, bwd=True, grads=api.BlockGrads(**dict(full, wo=None))) == INVALID
+    assert _block_call(lib, bwd=True, grads=api.BlockGrads(**dict(full, q_norm=P, k_norm=P))) == INVALID
+    assert _block_call(lib, bwd=True, grads=api.BlockGrads(**dict(full, w_down=P + 4))) == ALIGN
+    need = api.block_workspace_bytes(api.block_shape(300, 256, 384, 128, 4, 2, 64, 2, 1e4), False, "bf16", True)
+    assert _block_call(lib, bwd=True, wsb=need - 256) == WORKSPACE
