@@ -14,7 +14,8 @@ attention-core and hardware (recompute included) rates; the workspace bytes
 per chunk size; a chunk-size sweep; per-kernel event timings (from a second,
 profiled run of the same steps); the roofline entry of the dominant kernel
 (attention backward); the CPU fp64 oracle timed on a bounded sample; and the
-sequence-tiled MLP and LM-head loss next to the op (``mlp``, ``loss``).
+sequence-tiled MLP and LM-head loss next to the op (``mlp``, ``loss``), and
+one checkpointed transformer block built from them (``block``).
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--chunk 1] [--no-sweep] [--no-cpu]
 """
@@ -161,6 +162,97 @@ def mlp_bench(dev, steps, warmup):
                              "untiled_intermediates": 5 * N * F * es / 1e9}}
 
 
+BLOCK_WORKLOAD = dict(name="llama3-8b-block-one-gpu-32k", n_tokens=32768, d_model=4096, d_ff=14336,
+                      n_q_heads=32, n_kv_heads=8, head_dim=128, chunk_heads=4, tile_tokens=4096, rope_theta=5e5,
+                      dtype="bf16")
+
+
+def block_bench(dev, steps, warmup):
+    """One checkpointed pre-norm Llama3-8B block with every head on one GPU
+    (no context parallelism) at 32768 tokens: 32 q / 8 kv heads of 128 in
+    chunks of 4 q heads (one kv group per chunk), MLP tile 4096, bf16. A
+    step is upipe_block_fwd (nothing kept) plus upipe_block_bwd from the
+    block input alone (norm and attention forward recomputed). Also timed:
+    the backward when the forward kept h and lse. Model flops: the attention
+    layer's (as in the headline step) plus 18 N D F for the MLP."""
+    import numpy as np
+    import torch
+
+    from headwise_chunked_attention_amd import api
+    from headwise_chunked_attention_amd.synth import BlockInputs
+
+    w = BLOCK_WORKLOAD
+    N, D, F, T = w["n_tokens"], w["d_model"], w["d_ff"], w["tile_tokens"]
+    hq, hkv, d, C = w["n_q_heads"], w["n_kv_heads"], w["head_dim"], w["chunk_heads"]
+    inp = BlockInputs(N, D, F, hq, hkv, d, "bf16", seed=0)
+    names = {"attn_norm": "g_attn", "wq": "wq", "wk": "wk", "wv": "wv", "wo": "wo", "mlp_norm": "g_mlp",
+             "w_gate": "wg", "w_up": "wu", "w_down": "wd"}
+    wt = {n: torch.from_numpy(getattr(inp, a)).to(dev).to(torch.bfloat16) for n, a in names.items()}
+    x = torch.from_numpy(inp.x).to(dev).to(torch.bfloat16)
+    dy = torch.from_numpy(inp.dy).to(dev).to(torch.bfloat16)
+    del inp
+    shape = api.block_shape(N, D, F, T, hq, hkv, d, C, w["rope_theta"])
+    ws_f = api.block_workspace_bytes(shape, False, "bf16", False)
+    ws_b = api.block_workspace_bytes(shape, False, "bf16", True)
+    ws = api.alloc_workspace(max(ws_f, ws_b), dev)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    grads = {n: torch.empty(t.shape, dtype=torch.float32, device=dev) for n, t in wt.items()}
+    h_mid = torch.empty_like(x)
+    lse = torch.empty((hq, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        api.block_fwd(x, wt, shape, y=y, workspace=ws)
+
+    def bwd():
+        api.block_bwd(x, wt, shape, dy, dx=dx, grads=grads, workspace=ws)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    # backward from the kept residual and lse
+    api.block_fwd(x, wt, shape, y=y, h_mid=h_mid, lse=lse, workspace=ws)
+    ek = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ek[0].record(stream)
+    api.block_bwd(x, wt, shape, dy, h_mid=h_mid, lse=lse, dx=dx, grads=grads, workspace=ws)
+    ek[1].record(stream)
+    torch.cuda.synchronize()
+    t_f = [e[0].elapsed_time(e[1]) for e in evs]
+    t_b = [e[1].elapsed_time(e[2]) for e in evs]
+    api.profile_start()
+    fwd()
+    bwd()
+    prof = api.profile_stop()
+    attn_fwd_model = 2.0 * d * hq * N * (N + 1) + 4.0 * N * D * d * (hq + hkv)
+    model = model_flops(N, D, hq, hkv, d) + 18.0 * N * D * F
+    # recomputed in the backward: the attention forward, O inside the
+    # attention backward, and the MLP's h|u
+    hw = model + attn_fwd_model + (hardware_flops(N, D, hq, hkv, d) - model_flops(N, D, hq, hkv, d)) \
+        + 4.0 * N * D * F
+    step_ms = float(np.median([a + b for a, b in zip(t_f, t_b)]))
+    kinds = {k: {"ms": v["ms"], "launches": v["launches"],
+                 "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None}
+             for k, v in prof.items() if v["launches"]}
+    return {"workload": w["name"], "n_tokens": N, "d_model": D, "d_ff": F, "n_q_heads": hq, "n_kv_heads": hkv,
+            "head_dim": d, "chunk_heads": C, "tile_tokens": T, "dtype": "bf16",
+            "fwd_ms": float(np.median(t_f)), "bwd_ms": float(np.median(t_b)), "step_ms": step_ms,
+            "bwd_kept_ms": ek[0].elapsed_time(ek[1]),
+            "model_tflops": model / (step_ms * 1e-3) / 1e12, "model_flops": model,
+            "hardware_tflops": hw / (step_ms * 1e-3) / 1e12,
+            "kernels": kinds,
+            "memory_gb": {"saved_per_block": N * D * 2 / 1e9, "saved_with_h_and_lse": (2 * N * D * 2 + hq * N * 4) / 1e9,
+                          "workspace_fwd": ws_f / 1e9, "workspace_bwd": ws_b / 1e9}}
+
+
 LOSS_WORKLOAD = dict(name="llama3-lm-head-loss-seq-shard-16k", n_tokens=16384, d_model=4096, vocab=128256,
                      tile_tokens=1024, dtype="bf16")
 
@@ -242,6 +334,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP and loss measurements")
+    ap.add_argument("--no-block", action="store_true", help="skip the transformer-block measurement")
     ap.add_argument("--n-tokens", type=int, default=None, help="override N (not the headline workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) so that "
@@ -385,6 +478,12 @@ def main():
         print(f"# loss: fwd {loss['fwd_ms']:.2f} ms, bwd {loss['bwd_ms']:.2f} ms, {loss['model_tflops']:.0f} TFLOP/s",
               file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
+    block = None
+    if not args.no_block:
+        block = block_bench(dev, max(2, args.steps // 3), 1)
+        print(f"# block: fwd {block['fwd_ms']:.1f} ms, bwd {block['bwd_ms']:.1f} ms (kept h: {block['bwd_kept_ms']:.1f}),"
+              f" {block['model_tflops']:.0f} model TFLOP/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
@@ -423,6 +522,7 @@ def main():
         "cpu_baseline": cpu,
         "mlp": mlp,
         "loss": loss,
+        "block": block,
     }
     print(json.dumps(line), flush=True)
 

@@ -91,7 +91,7 @@ DEV void store_rows(T* S, const u32x4 (&r)[G::PER]) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(const AttnBwd<T> p) {
+__global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(const AttnBwd<T> p, int hs) {
   using G = DkdvGeo<T, D>;
   constexpr int BQ = G::BQ, BKEY = G::BKEY, ND = D / 32, NS = D / 16;
   using L = typename G::L;
@@ -105,7 +105,10 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   const int w = wave_id();
   const int kt = w % G::KT, qt = w / G::KT;
   const int tid = threadIdx.x;
-  const int64_t k0 = xcd_remap(blockIdx.x, gridDim.x) * BKEY;  // block 0 has the most query tiles
+  // workgroup -> (key block, head group): the hs head groups of a key block
+  // are adjacent, and key block 0 (the most query tiles) comes first
+  const int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t k0 = (lin / hs) * BKEY;
   const int krel = kt * 32 + r;                   // this lane's key within the block
   const int64_t kw = k0 + krel;
 
@@ -123,7 +126,10 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
 
   const int64_t qend = ((p.N + BQ - 1) / BQ) * BQ;
   const int64_t nqt = (qend - k0) / BQ;  // k0 is a multiple of BQ
-  const int64_t total = nqt * p.nh;
+  // heads h0 .. h0 + nh_b - 1 of the nh (hs workgroups share a key block)
+  const int nh_b = p.nh / hs;
+  const int h0 = (int)(lin % hs) * nh_b;
+  const int64_t total = nqt * nh_b;
 
   constexpr bool DMA = L::SWZ;  // bf16: Q/dO tiles by direct global -> LDS loads
   u32x4 rq[DMA ? 1 : G::PER], rdo[DMA ? 1 : G::PER];
@@ -166,11 +172,11 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     }
   };
 
-  prefetch(0, k0, 0);
+  prefetch(h0, k0, 0);
   commit(0);
   lds_barrier();
 
-  int hh = 0;
+  int hh = h0;
   int64_t q0 = k0;
   // One step on LDS buffer B (a compile-time constant, so the step's LDS
   // addresses need no per-step arithmetic).
@@ -294,6 +300,14 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
         const int dd = j * 32 + 8 * i + 4 * h;
         f32x4 vk = (f32x4){dk[j][4 * i], dk[j][4 * i + 1], dk[j][4 * i + 2], dk[j][4 * i + 3]} * p.dk_mul;
         f32x4 vv = (f32x4){dv[j][4 * i], dv[j][4 * i + 1], dv[j][4 * i + 2], dv[j][4 * i + 3]} * p.dv_mul;
+        if (hs > 1) {  // several workgroups per key block: add (the launcher zeroed)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            atomicAdd(p.dk_acc + kw * D + dd + e, vk[e]);
+            atomicAdd(p.dv_acc + kw * D + dd + e, vv[e]);
+          }
+          continue;
+        }
         f32x4* pk = reinterpret_cast<f32x4*>(p.dk_acc + kw * D + dd);
         f32x4* pv = reinterpret_cast<f32x4*>(p.dv_acc + kw * D + dd);
         if (p.accumulate) {
@@ -485,11 +499,22 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
 template <typename T, int D>
 hipError_t launch_dkdv_d(const AttnBwd<T>& p, hipStream_t s) {
   using G = DkdvGeo<T, D>;
-  const dim3 grid((unsigned)((p.N + G::BKEY - 1) / G::BKEY));
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<T, D>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::SMEM);
+  const int64_t nkb = (p.N + G::BKEY - 1) / G::BKEY;
+  // Key block b holds (N - b BKEY) / BQ query tiles per head: the work falls
+  // off linearly with b, so the grid balances over the CUs only with several
+  // workgroups per CU. With fewer key blocks than that and several heads, the
+  // heads are split over hs workgroups and their partial sums added atomically.
+  int hs = 1;
+  while (nkb * hs < 4 * 256 && p.nh % (hs * 2) == 0) hs *= 2;
+  hipError_t e;
+  if (hs > 1 && !p.accumulate) {
+    if ((e = launch_fill_f32(p.dk_acc, nkb * G::BKEY * D, 0.f, s)) != hipSuccess) return e;
+    if ((e = launch_fill_f32(p.dv_acc, nkb * G::BKEY * D, 0.f, s)) != hipSuccess) return e;
+  }
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<T, D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::SMEM);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), grid, dim3(G::NT), G::SMEM, s, p);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3((unsigned)(nkb * hs)), dim3(G::NT), G::SMEM, s, p, hs);
   return hipGetLastError();
 }
 
