@@ -461,14 +461,40 @@ struct TnTile {
   static_assert((BK * RCH) % NTHREADS == 0, "tile chunks");
 };
 
-template <typename T, int COLS, typename AddrFn>
-DEV void tn_load(AddrFn addr, int64_t k0, int64_t K, u32x4 (&r)[TnTile<T, COLS>::PER]) {
+// Thread t loads the 16-byte chunk t % RCH of rows t / RCH + i * (NTHREADS / RCH)
+// of each k tile: the same column for every i. Its row pointers (relative to
+// k = 0) are set up once; a full tile then costs one 64-bit add per load.
+// On a tile that runs past K (uniform test) rows at or past K are read from
+// row K - 1, and the A operand replaces them with zeros.
+template <typename T, int COLS>
+struct TnPtrs {
+  const T* p[TnTile<T, COLS>::PER];
+};
+
+template <typename T, int COLS>
+DEV void tn_ptrs(const T* base, int64_t ld, TnPtrs<T, COLS>& q) {
   using G = TnTile<T, COLS>;
 #pragma unroll
-  for (int i = 0; i < G::PER; ++i) {
-    const int c = threadIdx.x + i * NTHREADS;
-    const int64_t k = k0 + c / G::RCH;
-    r[i] = (k < K) ? ld_raw16(addr(k, (c % G::RCH) * G::VEC)) : zero_raw16();
+  for (int i = 0; i < G::PER; ++i)
+    q.p[i] = base + (int64_t)(threadIdx.x / G::RCH + i * (NTHREADS / G::RCH)) * ld;
+}
+
+template <typename T, int COLS, bool ZERO_TAIL>
+DEV void tn_load(const TnPtrs<T, COLS>& q, int64_t ld, int64_t k0, int64_t K, u32x4 (&r)[TnTile<T, COLS>::PER]) {
+  using G = TnTile<T, COLS>;
+  const int64_t off = k0 * ld;
+  if (k0 + G::BK <= K) {
+#pragma unroll
+    for (int i = 0; i < G::PER; ++i) r[i] = ld_raw16(q.p[i] + off);
+  } else {
+    // the last tile of a split: clamp the rows, and zero them in one operand
+#pragma unroll
+    for (int i = 0; i < G::PER; ++i) {
+      const int64_t rel = threadIdx.x / G::RCH + i * (NTHREADS / G::RCH);
+      const bool in = k0 + rel < K;
+      r[i] = ld_raw16(q.p[i] + ((in ? k0 + rel : K - 1) - rel) * ld);
+      if (ZERO_TAIL && !in) r[i] = zero_raw16();
+    }
   }
 }
 
@@ -510,11 +536,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   const int64_t kb = (bid / (gm * gn)) * p.ksplit;
   const int64_t ke = (kb + p.ksplit < p.K) ? kb + p.ksplit : p.K;
 
-  auto aaddr = [&](int64_t k, int col) { return p.a + k * p.lda + m0 + col; };
-  auto baddr = [&](int64_t k, int col) {
-    const int64_t n = n0 + col;
-    return p.b + (n / p.b_nblk) * p.b_nblk_stride + k * p.ldb + (n % p.b_nblk);
-  };
+  // this thread's column of each operand (fixed over k) and its row pointers
+  TnPtrs<T, BM> pa;
+  TnPtrs<T, BN> pb;
+  {
+    const int col_a = (threadIdx.x % TnTile<T, BM>::RCH) * TnTile<T, BM>::VEC;
+    const int col_b = (threadIdx.x % TnTile<T, BN>::RCH) * TnTile<T, BN>::VEC;
+    const int64_t n = n0 + col_b;
+    tn_ptrs<T, BM>(p.a + m0 + col_a, p.lda, pa);
+    tn_ptrs<T, BN>(p.b + (n / p.b_nblk) * p.b_nblk_stride + (n % p.b_nblk), p.ldb, pb);
+  }
 
   const int w = wave_id();
   const int wm = w >> 1, wn = w & 1;
@@ -527,16 +558,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
 
   u32x4 ra[TnTile<T, BM>::PER], rb[TnTile<T, BN>::PER];
   const int64_t nk = (ke - kb + BK - 1) / BK;
-  tn_load<T, BM>(aaddr, kb, ke, ra);
-  tn_load<T, BN>(baddr, kb, ke, rb);
+  tn_load<T, BM, true>(pa, p.lda, kb, ke, ra);
+  tn_load<T, BN, false>(pb, p.ldb, kb, ke, rb);
   tn_store<T, BM>(As, ra);
   tn_store<T, BN>(Bs, rb);
   lds_barrier();
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int buf = (int)(kt & 1);
     if (kt + 1 < nk) {
-      tn_load<T, BM>(aaddr, kb + (kt + 1) * BK, ke, ra);
-      tn_load<T, BN>(baddr, kb + (kt + 1) * BK, ke, rb);
+      tn_load<T, BM, true>(pa, p.lda, kb + (kt + 1) * BK, ke, ra);
+      tn_load<T, BN, false>(pb, p.ldb, kb + (kt + 1) * BK, ke, rb);
     }
     const T* Ab = As + buf * A_EL;
     const T* Bb = Bs + buf * B_EL;
@@ -574,7 +605,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   float* out = p.out[seg];
   const int64_t nc0 = n0 - (seg ? p.seg_end[seg - 1] : 0);
   const int tid = threadIdx.x;
-  if (p.ldn == 1) {
+  if (p.ldn == 1 && p.ksplit >= p.K && (p.ldm & 3) == 0) {
+    // one k split: this workgroup is the only writer of its tile in this
+    // launch (launches on a stream run in order), so a plain read-modify-write
+    for (int c = tid; c < BM * BN / 4; c += NTHREADS) {
+      const int row = c / (BN / 4), col = (c % (BN / 4)) * 4;
+      f32x4* o = reinterpret_cast<f32x4*>(out + (m0 + row) * p.ldm + (nc0 + col));
+      *o += *reinterpret_cast<const f32x4*>(Cs + row * SC + col);
+    }
+  } else if (p.ldn == 1) {
     for (int c = tid; c < BM * BN; c += NTHREADS) {
       const int row = c / BN, col = c % BN;
       atomicAdd(out + (m0 + row) * p.ldm + (nc0 + col), Cs[row * SC + col]);
