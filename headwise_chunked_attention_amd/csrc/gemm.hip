@@ -90,49 +90,76 @@ DEV void acc_to_lds(float* Cs, int row0, int nrows, int wm, int wn, const f32x16
           Cs[(wm * 64 + mt * 32 + 8 * i + 4 * h + j - row0) * SC + col0 + nt * 32] = acc[mt][nt][4 * i + j];
 }
 
-// B rows 0 .. BN/2-1 come from blo, rows BN/2 .. BN-1 from bhi (the same
-// pointer plus BN/2 rows, except for a gated tile).
+// Per-thread row pointers of the A and B k tiles (fixed over k; a k tile
+// adds an offset). Rows of A past M read row M - 1, so no load depends on a
+// branch. B rows 0 .. BN/2-1
+// come from blo, rows BN/2 .. BN-1 from bhi (the same pointer plus BN/2
+// rows, except for a gated tile).
 template <typename T, int BN, class G>
-DEV void nt_load_tile(const GemmNT<T>& p, const T* blo, const T* bhi, int64_t ldb, int64_t m0,
-                      int64_t k0, u32x4 (&ra)[BM * G::CPR / NTHREADS], u32x4 (&rb)[BN * G::CPR / NTHREADS]) {
+struct NtPtrs {
+  const T* a[BM * G::CPR / NTHREADS];
+  const T* b[BN * G::CPR / NTHREADS];
+};
+
+template <typename T, int BN, class G>
+DEV void nt_ptrs(const GemmNT<T>& p, const T* blo, const T* bhi, int64_t ldb, int64_t m0, NtPtrs<T, BN, G>& q) {
   constexpr int VEC = G::VEC, CPR = G::CPR;
   const int tid = threadIdx.x;
-  const T* abase = p.a + (k0 / p.a_kblk) * p.a_kblk_stride + (k0 % p.a_kblk);
 #pragma unroll
   for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
     const int c = tid + i * NTHREADS;
-    const int row = c / CPR, cc = c % CPR;
-    // rows past M load row M-1 (no branch around the load, so the waits
-    // for a register slot can count it); the tile store zeroes them
-    const int64_t m = min(m0 + row, p.M - 1);
-    ra[i] = ld_raw16(abase + m * p.lda + cc * VEC);
+    const int64_t m = min(m0 + c / CPR, p.M - 1);
+    q.a[i] = p.a + m * p.lda + (c % CPR) * VEC;
   }
 #pragma unroll
   for (int i = 0; i < BN * CPR / NTHREADS; ++i) {
     const int c = tid + i * NTHREADS;
-    const int row = c / CPR, cc = c % CPR;
+    const int row = c / CPR;
+    q.b[i] = (row < BN / 2 ? blo + row * ldb : bhi + (row - BN / 2) * ldb) + (c % CPR) * VEC;
+  }
+}
+
+// One k tile into registers: A at element offset aoff (its k block and
+// column), B at column k0.
+template <typename T, int BN, class G>
+DEV void nt_load_tile(const NtPtrs<T, BN, G>& q, int64_t aoff, int64_t k0, u32x4 (&ra)[BM * G::CPR / NTHREADS],
+                      u32x4 (&rb)[BN * G::CPR / NTHREADS]) {
+#pragma unroll
+  for (int i = 0; i < BM * G::CPR / NTHREADS; ++i) ra[i] = ld_raw16(q.a[i] + aoff);
+#pragma unroll
+  for (int i = 0; i < BN * G::CPR / NTHREADS; ++i) rb[i] = ld_raw16(q.b[i] + k0);
+}
+
+// The same load with the addresses formed per call (no pointer registers
+// held across the k loop: the accumulating products have few k tiles and
+// need the registers for occupancy).
+template <typename T, int BN, class G>
+DEV void nt_load_tile_direct(const GemmNT<T>& p, const T* blo, const T* bhi, int64_t ldb, int64_t m0, int64_t aoff,
+                             int64_t k0, u32x4 (&ra)[BM * G::CPR / NTHREADS], u32x4 (&rb)[BN * G::CPR / NTHREADS]) {
+  constexpr int VEC = G::VEC, CPR = G::CPR;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
+    const int c = tid + i * NTHREADS;
+    ra[i] = ld_raw16(p.a + aoff + min(m0 + c / CPR, p.M - 1) * p.lda + (c % CPR) * VEC);
+  }
+#pragma unroll
+  for (int i = 0; i < BN * CPR / NTHREADS; ++i) {
+    const int c = tid + i * NTHREADS;
+    const int row = c / CPR;
     const T* base = row < BN / 2 ? blo + row * ldb : bhi + (row - BN / 2) * ldb;
-    rb[i] = ld_raw16(base + k0 + cc * VEC);
+    rb[i] = ld_raw16(base + k0 + (c % CPR) * VEC);
   }
 }
 
 template <typename T, int BN, class G>
-DEV void nt_store_tile(T* As, T* Bs, const u32x4 (&ra)[BM * G::CPR / NTHREADS], const u32x4 (&rb)[BN * G::CPR / NTHREADS],
-                       int64_t rows_left) {
+DEV void nt_store_tile(T* As, T* Bs, const u32x4 (&ra)[BM * G::CPR / NTHREADS], const u32x4 (&rb)[BN * G::CPR / NTHREADS]) {
   constexpr int VEC = G::VEC, SK = G::SK, CPR = G::CPR;
   const int tid = threadIdx.x;
-  if (rows_left >= BM) {
 #pragma unroll
-    for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
-      const int c = tid + i * NTHREADS;
-      st_raw16(As + (c / CPR) * SK + (c % CPR) * VEC, ra[i]);
-    }
-  } else {  // last row tile: rows past M are zero
-#pragma unroll
-    for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
-      const int c = tid + i * NTHREADS;
-      st_raw16(As + (c / CPR) * SK + (c % CPR) * VEC, c / CPR < rows_left ? ra[i] : zero_raw16());
-    }
+  for (int i = 0; i < BM * CPR / NTHREADS; ++i) {
+    const int c = tid + i * NTHREADS;
+    st_raw16(As + (c / CPR) * SK + (c % CPR) * VEC, ra[i]);
   }
 #pragma unroll
   for (int i = 0; i < BN * CPR / NTHREADS; ++i) {
@@ -327,10 +354,34 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   constexpr int RA = BM * CPR / NTHREADS, RB = BN * CPR / NTHREADS;
   u32x4 ra[NPF][RA], rb[NPF][RB];
   const int64_t nk = p.K / BK;
+  // A's offset of the k tile loaded last (its k block times the block
+  // stride, plus k within the block), stepped one tile at a time: the blocks
+  // hold whole k tiles, so no division
+  int64_t a_tile = 0, a_blk = 0, a_kin = 0;
+  auto a_next = [&]() {
+    if (a_tile + 1 < nk) {
+      ++a_tile;
+      a_kin += BK;
+      if (a_kin == p.a_kblk) {
+        a_kin = 0;
+        a_blk += p.a_kblk_stride;
+      }
+    }
+  };
+  NtPtrs<T, BN, G> q;  // with several slots (long k): row pointers set up once
+  if constexpr (NPF > 1) nt_ptrs<T, BN, G>(p, blo, bhi, ldb, m0, q);
+  auto load = [&](u32x4(&a)[RA], u32x4(&b)[RB]) {
+    if constexpr (NPF > 1)
+      nt_load_tile<T, BN, G>(q, a_blk + a_kin, a_tile * BK, a, b);
+    else
+      nt_load_tile_direct<T, BN, G>(p, blo, bhi, ldb, m0, a_blk + a_kin, a_tile * BK, a, b);
+  };
 #pragma unroll
-  for (int i = 0; i < NPF; ++i)
-    nt_load_tile<T, BN, G>(p, blo, bhi, ldb, m0, min((int64_t)i, nk - 1) * BK, ra[i], rb[i]);
-  nt_store_tile<T, BN, G>(As, Bs, ra[0], rb[0], p.M - m0);
+  for (int i = 0; i < NPF; ++i) {
+    if (i) a_next();
+    load(ra[i], rb[i]);
+  }
+  nt_store_tile<T, BN, G>(As, Bs, ra[0], rb[0]);
   lds_barrier();
   auto step = [&](auto slot_c, int64_t kt) {
     constexpr int SLOT = decltype(slot_c)::value, NEXT = (SLOT + 1) % NPF;
@@ -338,14 +389,16 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
     // With several slots, past the end the last tile is loaded again: every
     // step issues the same loads, so the wait before a slot's store counts
     // exactly the younger slots.
-    if (NPF > 1 || kt + 1 < nk)
-      nt_load_tile<T, BN, G>(p, blo, bhi, ldb, m0, min(kt + NPF, nk - 1) * BK, ra[SLOT], rb[SLOT]);
+    if (NPF > 1 || kt + 1 < nk) {  // tile min(kt + NPF, nk - 1)
+      a_next();
+      load(ra[SLOT], rb[SLOT]);
+    }
     const T* Ab = As + buf * BM * SK;
     const T* Bb = Bs + buf * BN * SK;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) mma_tile_step<T, BN>(Ab, Bb, SK, ks, wm, wn, acc);
     if (NPF > 1 || kt + 1 < nk)
-      nt_store_tile<T, BN, G>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra[NEXT], rb[NEXT], p.M - m0);
+      nt_store_tile<T, BN, G>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra[NEXT], rb[NEXT]);
     lds_barrier();
   };
   int64_t kt = 0;
@@ -358,6 +411,18 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
     if (kt < nk) step(std::integral_constant<int, 0>(), kt);
   if constexpr (NPF > 2)
     if (kt + 1 < nk) step(std::integral_constant<int, 1>(), kt + 1);
+  // Rows of C past M hold copies of row M - 1's products. Every epilogue but
+  // the head-wise one skips them; that one writes the padded rows, as zeros.
+  if (EPI == EPI_HEADS && p.M - m0 < BM) {
+    const int h = lane_id() >> 5;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (m0 + wm * 64 + mt * 32 + 8 * (e / 4) + 4 * h + e % 4 >= p.M) acc[mt][nt][e] = 0.f;
+  }
 
   // Epilogue in two passes of EPI_ROWS tile rows through Cs[EPI_ROWS][BN + 4].
   float* Cs = reinterpret_cast<float*>(smem);
@@ -636,6 +701,7 @@ hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
   // the k loop reads whole k tiles and clamps rows to M-1
   const int bk = (epi == EPI_ACCUM ? nt_kb<EPI_ACCUM>() : nt_kb<EPI_HEADS>()) / (int)sizeof(T);
   if (p.M <= 0 || p.K <= 0 || p.K % bk) return hipErrorInvalidValue;
+  if (p.a_kblk <= 0 || p.a_kblk % bk) return hipErrorInvalidValue;  // A's k blocks hold whole k tiles
   if ((epi == EPI_GLU || epi == EPI_GLU_BWD) && (bn != 128 || p.N % 128 || p.glu.ldf % 64))
     return hipErrorInvalidValue;
   if ((epi == EPI_CE || epi == EPI_CE_BWD) && (bn != 128 || p.N % 128)) return hipErrorInvalidValue;
