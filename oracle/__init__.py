@@ -38,4 +38,6 @@ from .loss import (  # noqa: F401
 from .block import (  # noqa: F401
     block_fwd,
     block_bwd,
+    stack_fwd,
+    stack_bwd,
 )

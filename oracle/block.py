@@ -28,11 +28,17 @@ forward for an upstream gradient dy,
 
 plus the weight gradients of both sublayers and of the two norm weights.
 
+``stack_fwd`` / ``stack_bwd`` chain blocks: the stack keeps only each
+block's input between the passes (what the talk offloads to the CPU), and
+block l's backward starts from that input and from the gradient block l + 1
+passes down.
+
 Parity pins: ``tests/test_oracle_block.py`` checks the composition through
 special cases that reduce it to the pinned sublayer oracles (zero output
 weights give y = x; a zero attention norm weight removes the attention
 branch), exact homogeneity identities of the weight gradients, and central
-finite differences of every gradient; none is "parity unpinned".
+finite differences of every gradient, and the stack's chain rule by
+finite differences through two blocks; none is "parity unpinned".
 
 Layouts: x, y, h, dy, dx [N][D]; g_attn, g_mlp [D]; attention weights as in
 ``oracle.attention``; MLP weights as in ``oracle.mlp``; lse [Hq][N].
@@ -89,3 +95,39 @@ def block_bwd(x, g_attn, wq, wk, wv, wo, g_mlp, wg, wu, wd, dy, n_q_heads, n_kv_
     dx_n, dg_attn = rmsnorm_bwd(x, g_attn, eps, da)
     return {"dx": dh + dx_n, "g_attn": dg_attn, "wq": dwq, "wk": dwk, "wv": dwv, "wo": dwo,
             "q_norm": dqn, "k_norm": dkn, "g_mlp": dg_mlp, "wg": dwg, "wu": dwu, "wd": dwd}
+
+
+def stack_fwd(x, layers, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads=1, qk_eps=1e-6,
+              eps=1e-5, tile=None):
+    """A stack of blocks: ``(y, inputs)`` with ``inputs[l]`` the input of block l.
+
+    ``layers`` is a list of dicts with the keys ``g_attn, wq, wk, wv, wo,
+    q_norm, k_norm, g_mlp, wg, wu, wd``. Checkpointing keeps exactly the
+    block inputs (the talk offloads them to the CPU between the passes).
+    """
+    inputs = []
+    h = np.asarray(x, dtype=F64)
+    for w in layers:
+        inputs.append(h)
+        h, _, _ = block_fwd(h, w["g_attn"], w["wq"], w["wk"], w["wv"], w["wo"], w["g_mlp"], w["wg"], w["wu"],
+                            w["wd"], n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads, w["q_norm"],
+                            w["k_norm"], qk_eps, eps, tile)
+    return h, inputs
+
+
+def stack_bwd(x, layers, dy, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads=1, qk_eps=1e-6,
+              eps=1e-5, tile=None):
+    """Backward of ``stack_fwd``: ``(dx, grads)`` with ``grads[l]`` the dict
+    ``block_bwd`` returns for block l (without its ``dx``). Block l's backward
+    starts from its kept input and the gradient that block l + 1 passed down."""
+    _, inputs = stack_fwd(x, layers, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads, qk_eps, eps, tile)
+    g = np.asarray(dy, dtype=F64)
+    grads = [None] * len(layers)
+    for i in range(len(layers) - 1, -1, -1):
+        w = layers[i]
+        r = block_bwd(inputs[i], w["g_attn"], w["wq"], w["wk"], w["wv"], w["wo"], w["g_mlp"], w["wg"], w["wu"],
+                      w["wd"], g, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads, w["q_norm"],
+                      w["k_norm"], qk_eps, eps, tile)
+        g = r.pop("dx")
+        grads[i] = r
+    return g, grads

@@ -8,7 +8,9 @@ The pages print no worked example of the block, so the pins are:
   y = h, a zero attention output weight leaves h = x;
 - exact homogeneity identities of the weight gradients (each holds at any
   size because the block is linear in that weight or in that norm weight);
-- central finite differences of every gradient along random directions.
+- central finite differences of every gradient along random directions;
+- for the stack of blocks: one block is the block, each block's kept input is
+  the previous block's output, and finite differences through two blocks.
 A plausible slip in the oracle (a norm on the wrong tensor, a lost residual
 term in dx or dh, the two norm weights swapped, the MLP reading h instead of
 its norm) fails at least one of them.
@@ -190,3 +192,54 @@ def test_chunk_and_tile_invariance():
     g1, g4 = _bwd(p, dy, chunk=1), _bwd(p, dy, chunk=2, tile=5)
     for k in ("dx",) + WEIGHTS:
         assert np.allclose(g1[k], g4[k], rtol=0, atol=1e-11), k
+
+
+def _layers(n, seed):
+    out = []
+    for i in range(n):
+        p, _ = _problem(seed=seed + i)
+        p.pop("x")
+        out.append(p)
+    return out
+
+
+def test_stack_of_one_is_the_block_and_inputs_chain():
+    p, dy = _problem(seed=30)
+    lay = [{k: v for k, v in p.items() if k != "x"}]
+    y, inputs = oracle.stack_fwd(p["x"], lay, SHAPE["Hq"], SHAPE["Hkv"], SHAPE["d"], THETA)
+    assert np.array_equal(y, _fwd(p)[0]) and np.array_equal(inputs[0], p["x"])
+    dx, grads = oracle.stack_bwd(p["x"], lay, dy, SHAPE["Hq"], SHAPE["Hkv"], SHAPE["d"], THETA)
+    ref = _bwd(p, dy)
+    assert np.array_equal(dx, ref["dx"])
+    for k in WEIGHTS:
+        assert np.array_equal(grads[0][k], ref[k]), k
+    # two blocks: block 1's input is block 0's output
+    lay2 = _layers(2, 40)
+    y2, inp2 = oracle.stack_fwd(p["x"], lay2, SHAPE["Hq"], SHAPE["Hkv"], SHAPE["d"], THETA)
+    q = dict(lay2[0], x=p["x"])
+    assert np.array_equal(inp2[1], _fwd(q)[0])
+
+
+def test_stack_gradients_central_finite_differences():
+    """Chain rule across blocks: the input gradient and a weight gradient of
+    the first of two blocks, against finite differences of <dy, y>."""
+    r = np.random.default_rng(50)
+    x = r.standard_normal((SHAPE["N"], SHAPE["D"]))
+    dy = r.standard_normal((SHAPE["N"], SHAPE["D"]))
+    lay = _layers(2, 60)
+    dx, grads = oracle.stack_bwd(x, lay, dy, SHAPE["Hq"], SHAPE["Hkv"], SHAPE["d"], THETA)
+    e = 1e-5
+
+    def loss(xx, ll):
+        return float(np.sum(oracle.stack_fwd(xx, ll, SHAPE["Hq"], SHAPE["Hkv"], SHAPE["d"], THETA)[0] * dy))
+
+    v = r.standard_normal(x.shape)
+    num = (loss(x + e * v, lay) - loss(x - e * v, lay)) / (2 * e)
+    assert abs(num - float(np.sum(dx * v))) < 1e-6 * (1 + abs(num))
+    for name in ("wq", "wd", "g_attn"):
+        v = r.standard_normal(lay[0][name].shape)
+        lp = [dict(lay[0], **{name: lay[0][name] + e * v}), lay[1]]
+        lm = [dict(lay[0], **{name: lay[0][name] - e * v}), lay[1]]
+        num = (loss(x, lp) - loss(x, lm)) / (2 * e)
+        ana = float(np.sum(grads[0][name] * v))
+        assert abs(num - ana) < 1e-6 * (1 + abs(ana)), name
