@@ -15,7 +15,8 @@ per chunk size; a chunk-size sweep; per-kernel event timings (from a second,
 profiled run of the same steps); the roofline entry of the dominant kernel
 (attention backward); the CPU fp64 oracle timed on a bounded sample; and the
 sequence-tiled MLP and LM-head loss next to the op (``mlp``, ``loss``), and
-one checkpointed transformer block built from them (``block``).
+one checkpointed transformer block built from them (``block``), and four
+such blocks with their inputs offloaded to host memory (``stack``).
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--chunk 1] [--no-sweep] [--no-cpu]
 """
@@ -253,6 +254,92 @@ def block_bench(dev, steps, warmup):
                           "workspace_fwd": ws_f / 1e9, "workspace_bwd": ws_b / 1e9}}
 
 
+STACK_LAYERS = 4
+
+
+def stack_bench(dev, steps):
+    """Four of the blocks above, stacked, with each block's input offloaded to
+    pinned host memory between the passes (upipe_stack_fwd/bwd, copies on a
+    second stream), against the same four blocks run one by one with their
+    inputs kept in HBM. The layers share one set of weights (the time does not
+    depend on the values). Reports both step times, the offload's overhead,
+    the HBM the offload frees and the host link rate of one input copy."""
+    import numpy as np
+    import torch
+
+    from headwise_chunked_attention_amd import api
+    from headwise_chunked_attention_amd.synth import BlockInputs
+
+    w = BLOCK_WORKLOAD
+    L = STACK_LAYERS
+    N, D, F, T = w["n_tokens"], w["d_model"], w["d_ff"], w["tile_tokens"]
+    hq, hkv, d, C = w["n_q_heads"], w["n_kv_heads"], w["head_dim"], w["chunk_heads"]
+    inp = BlockInputs(N, D, F, hq, hkv, d, "bf16", seed=1)
+    names = {"attn_norm": "g_attn", "wq": "wq", "wk": "wk", "wv": "wv", "wo": "wo", "mlp_norm": "g_mlp",
+             "w_gate": "wg", "w_up": "wu", "w_down": "wd"}
+    wt = {n: torch.from_numpy(getattr(inp, a)).to(dev).to(torch.bfloat16) for n, a in names.items()}
+    x = torch.from_numpy(inp.x).to(dev).to(torch.bfloat16)
+    dy = torch.from_numpy(inp.dy).to(dev).to(torch.bfloat16)
+    del inp
+    layers = [wt] * L
+    grads = [{n: torch.empty(t.shape, dtype=torch.float32, device=dev) for n, t in wt.items()} for _ in range(L)]
+    shape = api.block_shape(N, D, F, T, hq, hkv, d, C, w["rope_theta"])
+    ws = api.alloc_workspace(api.stack_workspace_bytes(shape, False, "bf16"), dev)
+    hin = torch.empty((L, N, D), dtype=torch.bfloat16, pin_memory=True)
+    side = torch.cuda.Stream(device=dev)
+    stream = torch.cuda.current_stream(dev)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    acts = [torch.empty_like(x) for _ in range(L)]  # the unoffloaded run's kept inputs
+
+    def offloaded():
+        api.stack_fwd(x, layers, shape, hin, y=y, workspace=ws, copy_stream=side)
+        api.stack_bwd(layers, shape, hin, dy, dx=dx, grads=grads, workspace=ws, copy_stream=side)
+
+    def resident():
+        a = x
+        for i in range(L):
+            out = acts[i] if i < L - 1 else y
+            api.block_fwd(a, layers[i], shape, y=out, workspace=ws)
+            a = out
+        g = dy
+        for i in range(L - 1, -1, -1):
+            src = x if i == 0 else acts[i - 1]
+            g, _ = api.block_bwd(src, layers[i], shape, g, dx=dx if i == 0 else None, grads=grads[i], workspace=ws)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    t_off = timed(offloaded)
+    t_res = timed(resident)
+    # one input's copy to host and back, alone (the link rate the overlap hides)
+    a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    with torch.cuda.stream(side):
+        a.record(side)
+        hin[0].copy_(x, non_blocking=True)
+        b.record(side)
+        acts[0].copy_(hin[0], non_blocking=True)
+        c.record(side)
+    torch.cuda.synchronize()
+    nbytes = N * D * 2
+    return {"workload": f"{L} x {w['name']}", "n_layers": L, "step_ms_offloaded": t_off, "step_ms_resident": t_res,
+            "offload_overhead": t_off / t_res - 1.0,
+            "hbm_gb_block_inputs": {"resident": L * nbytes / 1e9, "offloaded": 2 * nbytes / 1e9},
+            "host_gb": L * nbytes / 1e9,
+            "copy_gbs": {"to_host": nbytes / (a.elapsed_time(b) * 1e-3) / 1e9,
+                         "to_device": nbytes / (b.elapsed_time(c) * 1e-3) / 1e9}}
+
+
 LOSS_WORKLOAD = dict(name="llama3-lm-head-loss-seq-shard-16k", n_tokens=16384, d_model=4096, vocab=128256,
                      tile_tokens=1024, dtype="bf16")
 
@@ -478,11 +565,16 @@ def main():
         print(f"# loss: fwd {loss['fwd_ms']:.2f} ms, bwd {loss['bwd_ms']:.2f} ms, {loss['model_tflops']:.0f} TFLOP/s",
               file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-    block = None
+    block = stack = None
     if not args.no_block:
         block = block_bench(dev, max(2, args.steps // 3), 1)
         print(f"# block: fwd {block['fwd_ms']:.1f} ms, bwd {block['bwd_ms']:.1f} ms (kept h: {block['bwd_kept_ms']:.1f}),"
               f" {block['model_tflops']:.0f} model TFLOP/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        stack = stack_bench(dev, 2)
+        print(f"# stack of {stack['n_layers']}: offloaded {stack['step_ms_offloaded']:.1f} ms, resident "
+              f"{stack['step_ms_resident']:.1f} ms ({100 * stack['offload_overhead']:+.1f}%)", file=sys.stderr,
+              flush=True)
         torch.cuda.empty_cache()
 
     cpu = None
@@ -523,6 +615,7 @@ def main():
         "mlp": mlp,
         "loss": loss,
         "block": block,
+        "stack": stack,
     }
     print(json.dumps(line), flush=True)
 

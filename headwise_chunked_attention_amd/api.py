@@ -92,6 +92,13 @@ def load():
     lib.upipe_block_bwd.argtypes = [i32, bp, vp, ctypes.POINTER(BlockWeights), vp, vp, vp, vp,
                                     ctypes.POINTER(BlockGrads), vp, sz, vp]
     lib.upipe_block_bwd.restype = i32
+    lib.upipe_stack_workspace_bytes.argtypes = [bp, i32, i32]
+    lib.upipe_stack_workspace_bytes.restype = sz
+    lib.upipe_stack_fwd.argtypes = [i32, bp, i32, ctypes.POINTER(BlockWeights), vp, vp, vp, vp, sz, vp, vp]
+    lib.upipe_stack_fwd.restype = i32
+    lib.upipe_stack_bwd.argtypes = [i32, bp, i32, ctypes.POINTER(BlockWeights), vp, vp, vp,
+                                    ctypes.POINTER(BlockGrads), vp, sz, vp, vp]
+    lib.upipe_stack_bwd.restype = i32
     lib.upipe_strerror.argtypes = [i32]
     lib.upipe_strerror.restype = ctypes.c_char_p
     lib.upipe_version.argtypes = []
@@ -473,6 +480,82 @@ def block_bwd(x, weights: dict, shape: BlockShape, dy, *, h_mid=None, lse=None, 
                              _stream_handle(dev, stream))
     if rc != 0:
         raise UpipeError(rc, "upipe_block_bwd")
+    return dx, grads
+
+
+def stack_workspace_bytes(shape: BlockShape, qk_norm, dtype) -> int:
+    return int(load().upipe_stack_workspace_bytes(ctypes.byref(shape), int(bool(qk_norm)), dtype_code(dtype)))
+
+
+def _check_host(t, name, dtype, shape):
+    if t is None or t.is_cuda:
+        raise ValueError(f"{name} must be a host tensor (pinned: torch.empty(..., pin_memory=True))")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
+def _stream_ptr(dev, stream):
+    return None if stream is None else ctypes.c_void_p(stream.cuda_stream)
+
+
+def stack_fwd(x, layers, shape: BlockShape, host_inputs, *, y=None, workspace=None, stream=None,
+              copy_stream=None):
+    """Forward of a stack of blocks (upipe_stack_fwd); ``layers`` is a list of
+    weight dicts as for ``block_fwd``; ``host_inputs`` a host tensor
+    [n_layers][N][D] of x's dtype that receives each block's input. Returns y."""
+    lib = load()
+    dev, dt = x.device, x.dtype
+    N, D, L = shape.n_tokens, shape.d_model, len(layers)
+    _check(x, "x", dt, (N, D), dev)
+    _check_host(host_inputs, "host_inputs", dt, (L, N, D))
+    ws = (BlockWeights * L)(*[_block_weights(shape, w, dt, dev) for w in layers])
+    y = torch.empty((N, D), dtype=dt, device=dev) if y is None else y
+    _check(y, "y", dt, (N, D), dev)
+    qk = layers[0].get("q_norm") is not None
+    if workspace is None:
+        workspace = alloc_workspace(stack_workspace_bytes(shape, qk, dt), dev)
+    rc = lib.upipe_stack_fwd(dtype_code(dt), ctypes.byref(shape), L, ws, _ptr(x), _ptr(y),
+                             ctypes.c_void_p(host_inputs.data_ptr()), _ptr(workspace), workspace.numel(),
+                             _stream_handle(dev, stream), _stream_ptr(dev, copy_stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_stack_fwd")
+    return y
+
+
+def stack_bwd(layers, shape: BlockShape, host_inputs, dy, *, dx=None, grads=None, workspace=None, stream=None,
+              copy_stream=None):
+    """Backward of a stack of blocks (upipe_stack_bwd) from the inputs the
+    forward left in ``host_inputs``. Returns (dx, grads), grads a list of
+    per-layer dicts of fp32 tensors."""
+    lib = load()
+    dev, dt = dy.device, dy.dtype
+    N, D, L = shape.n_tokens, shape.d_model, len(layers)
+    _check(dy, "dy", dt, (N, D), dev)
+    _check_host(host_inputs, "host_inputs", dt, (L, N, D))
+    ws = (BlockWeights * L)(*[_block_weights(shape, w, dt, dev) for w in layers])
+    qk = layers[0].get("q_norm") is not None
+    shapes = _block_weight_shapes(shape)
+    f32 = torch.float32
+    if grads is None:
+        grads = [{n: torch.empty(shapes[n], dtype=f32, device=dev) for n in _BLOCK_TENSORS
+                  if qk or n not in ("q_norm", "k_norm")} for _ in range(L)]
+    gs = (BlockGrads * L)()
+    for i, gd in enumerate(grads):
+        for n in _BLOCK_TENSORS:
+            t = gd.get(n)
+            if t is None and not qk and n in ("q_norm", "k_norm"):
+                continue
+            _check(t, f"layer {i} grad {n}", f32, shapes[n], dev)
+            setattr(gs[i], n, t.data_ptr())
+    dx = torch.empty((N, D), dtype=dt, device=dev) if dx is None else dx
+    _check(dx, "dx", dt, (N, D), dev)
+    if workspace is None:
+        workspace = alloc_workspace(stack_workspace_bytes(shape, qk, dt), dev)
+    rc = lib.upipe_stack_bwd(dtype_code(dt), ctypes.byref(shape), L, ws, ctypes.c_void_p(host_inputs.data_ptr()),
+                             _ptr(dy), _ptr(dx), gs, _ptr(workspace), workspace.numel(), _stream_handle(dev, stream),
+                             _stream_ptr(dev, copy_stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_stack_bwd")
     return dx, grads
 
 

@@ -255,9 +255,207 @@ int check_ws(const BlockShape& b, upipe_dtype_t dt, bool bwd, const void* ws, si
   return UPIPE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// A stack of blocks with the block inputs offloaded to host memory (the
+// talk's CPU offload: block inputs leave the GPU between the passes and come
+// back, prefetched, for the backward; liquidgold.cc notes, "Progression of
+// Techniques", item 5; talk transcript, the part on CPU offloading).
+//
+// Device buffers, whatever the number of layers: two activation buffers P
+// (the forward's block outputs; the backward's prefetched block inputs), two
+// gradient buffers G, and one block workspace. Copies run on the caller's
+// copy stream, ordered against the compute stream by events:
+//   forward   copy of block l's input to host[l] overlaps block l; block l+1,
+//             which overwrites that input's buffer, waits for the copy;
+//   backward  the input of block l - 2 is fetched into the buffer block l
+//             has just finished with, while blocks l - 1 and l - 2 wait for
+//             their own inputs only.
+// ---------------------------------------------------------------------------
+struct StackPlan {
+  size_t act[2], grad[2], block, total;
+};
+
+StackPlan stack_plan(const BlockShape& b, upipe_dtype_t dt) {
+  StackPlan p;
+  memset(&p, 0, sizeof(p));
+  const size_t nd = (size_t)b.a.n_tokens * b.a.d_model * b.es;
+  Carver c;
+  p.act[0] = c.take(nd);
+  p.act[1] = c.take(nd);
+  p.grad[0] = c.take(nd);
+  p.grad[1] = c.take(nd);
+  size_t bw = block_plan(b, dt, false).total;
+  const size_t bb = block_plan(b, dt, true).total;
+  if (bb > bw) bw = bb;
+  p.block = c.take(bw);
+  p.total = c.off;
+  return p;
+}
+
+// Events of one call, destroyed when the call returns (a recorded event may
+// be destroyed before it completes; waits already enqueued keep their meaning).
+struct Events {
+  hipEvent_t e[6] = {};
+  int n = 0;
+  ~Events() {
+    for (int i = 0; i < n; ++i) hipEventDestroy(e[i]);
+  }
+  hipError_t make(int count) {
+    for (; n < count; ++n) {
+      const hipError_t r = hipEventCreateWithFlags(&e[n], hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+};
+
+template <typename T>
+int stack_fwd_impl(const BlockShape& b, upipe_dtype_t dt, int L, const upipe_block_weights_t* w, const T* x, T* y,
+                   T* host, char* ws, hipStream_t st, hipStream_t cs) {
+  const StackPlan pl = stack_plan(b, dt);
+  const size_t nd = (size_t)b.a.n_tokens * b.a.d_model;
+  T* P[2] = {reinterpret_cast<T*>(ws + pl.act[0]), reinterpret_cast<T*>(ws + pl.act[1])};
+  char* bws = ws + pl.block;
+  Events ev;
+  HIP_TRY(ev.make(3));
+  hipEvent_t ready = ev.e[0], copied[2] = {ev.e[1], ev.e[2]};
+  HIP_TRY(hipEventRecord(ready, st));  // x and the workspace, as the caller's stream left them
+  const T* in = x;
+  for (int l = 0; l < L; ++l) {
+    HIP_TRY(hipStreamWaitEvent(cs, ready, 0));
+    HIP_TRY(hipMemcpyAsync(host + (size_t)l * nd, in, nd * sizeof(T), hipMemcpyDefault, cs));
+    HIP_TRY(hipEventRecord(copied[l % 2], cs));
+    T* out = l == L - 1 ? y : P[l % 2];
+    // out's buffer holds block l-1's input (from l = 2 on): its copy must be done
+    if (l >= 2 && l < L - 1) HIP_TRY(hipStreamWaitEvent(st, copied[(l - 1) % 2], 0));
+    int rc = block_fwd_impl<T>(b, dt, in, w[l], out, nullptr, nullptr, bws, st);
+    if (rc) return rc;
+    HIP_TRY(hipEventRecord(ready, st));
+    in = out;
+  }
+  // the caller's stream covers the last copy: host is complete when it syncs
+  HIP_TRY(hipStreamWaitEvent(st, copied[(L - 1) % 2], 0));
+  return UPIPE_OK;
+}
+
+template <typename T>
+int stack_bwd_impl(const BlockShape& b, upipe_dtype_t dt, int L, const upipe_block_weights_t* w, const T* host,
+                   const T* dy, T* dx, const upipe_block_grads_t* g, char* ws, hipStream_t st, hipStream_t cs) {
+  const StackPlan pl = stack_plan(b, dt);
+  const size_t nd = (size_t)b.a.n_tokens * b.a.d_model;
+  T* P[2] = {reinterpret_cast<T*>(ws + pl.act[0]), reinterpret_cast<T*>(ws + pl.act[1])};
+  T* G[2] = {reinterpret_cast<T*>(ws + pl.grad[0]), reinterpret_cast<T*>(ws + pl.grad[1])};
+  char* bws = ws + pl.block;
+  Events ev;
+  HIP_TRY(ev.make(5));
+  hipEvent_t start = ev.e[0], in_ev[2] = {ev.e[1], ev.e[2]}, used[2] = {ev.e[3], ev.e[4]};
+  HIP_TRY(hipEventRecord(start, st));
+  HIP_TRY(hipStreamWaitEvent(cs, start, 0));  // the workspace is free of the caller's earlier work
+  auto fetch = [&](int l) -> hipError_t {
+    hipError_t e = hipMemcpyAsync(P[l % 2], host + (size_t)l * nd, nd * sizeof(T), hipMemcpyDefault, cs);
+    if (e != hipSuccess) return e;
+    return hipEventRecord(in_ev[l % 2], cs);
+  };
+  HIP_TRY(fetch(L - 1));
+  if (L >= 2) HIP_TRY(fetch(L - 2));
+  for (int l = L - 1; l >= 0; --l) {
+    HIP_TRY(hipStreamWaitEvent(st, in_ev[l % 2], 0));
+    const T* dyl = l == L - 1 ? dy : G[(l + 1) % 2];
+    T* dxl = l == 0 ? dx : G[l % 2];
+    int rc = block_bwd_impl<T>(b, dt, P[l % 2], w[l], nullptr, nullptr, dyl, dxl, g[l], bws, st);
+    if (rc) return rc;
+    if (l >= 2) {
+      HIP_TRY(hipEventRecord(used[l % 2], st));
+      HIP_TRY(hipStreamWaitEvent(cs, used[l % 2], 0));
+      HIP_TRY(fetch(l - 2));
+    }
+  }
+  return UPIPE_OK;
+}
+
+int check_grads(const upipe_block_grads_t* grads, bool qk) {
+  if (grads == nullptr) return UPIPE_ERR_INVALID_ARG;
+  const void* p[] = {grads->attn_norm, grads->wq, grads->wk, grads->wv, grads->wo, grads->mlp_norm,
+                     grads->w_gate, grads->w_up, grads->w_down};
+  int rc = check_ptrs(p, 9);
+  if (rc) return rc;
+  if (qk) {
+    const void* n[] = {grads->q_norm, grads->k_norm};
+    return check_ptrs(n, 2);
+  }
+  return (grads->q_norm != nullptr || grads->k_norm != nullptr) ? UPIPE_ERR_INVALID_ARG : UPIPE_OK;
+}
+
+// Shape and every layer's weights (and gradients, if given); all layers must
+// agree on having q/k norm.
+int stack_check(int dtype, const upipe_block_shape_t* shape, int L, const upipe_block_weights_t* w,
+                const upipe_block_grads_t* g, BlockShape* b) {
+  if (L < 1 || w == nullptr) return UPIPE_ERR_INVALID_ARG;
+  bool qk0 = false;
+  for (int l = 0; l < L; ++l) {
+    bool qk = false;
+    int rc = check_weights(&w[l], &qk);
+    if (rc) return rc;
+    if (l == 0) qk0 = qk;
+    if (qk != qk0) return UPIPE_ERR_INVALID_ARG;
+    if (g && (rc = check_grads(&g[l], qk))) return rc;
+  }
+  return block_check_shape(dtype, shape, qk0, b);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t upipe_stack_workspace_bytes(const upipe_block_shape_t* shape, int qk_norm, upipe_dtype_t dtype) {
+  BlockShape b;
+  if (block_check_shape(dtype, shape, qk_norm, &b)) return 0;
+  return stack_plan(b, dtype).total;
+}
+
+int upipe_stack_fwd(upipe_dtype_t dtype, const upipe_block_shape_t* shape, int n_layers,
+                    const upipe_block_weights_t* weights, const void* x, void* y, void* host_inputs,
+                    void* workspace, size_t workspace_bytes, void* stream, void* copy_stream) {
+  BlockShape b;
+  int rc = stack_check(dtype, shape, n_layers, weights, nullptr, &b);
+  if (rc) return rc;
+  const void* p[] = {x, y, host_inputs};
+  if ((rc = check_ptrs(p, 3))) return rc;
+  if (workspace == nullptr) return UPIPE_ERR_WORKSPACE;
+  if (!aligned(workspace, REGION_ALIGN)) return UPIPE_ERR_ALIGNMENT;
+  if (workspace_bytes < stack_plan(b, dtype).total) return UPIPE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t cs = copy_stream ? reinterpret_cast<hipStream_t>(copy_stream) : st;
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == UPIPE_BF16)
+    return stack_fwd_impl<bf16>(b, dtype, n_layers, weights, (const bf16*)x, (bf16*)y, (bf16*)host_inputs, ws, st,
+                                cs);
+  return stack_fwd_impl<float>(b, dtype, n_layers, weights, (const float*)x, (float*)y, (float*)host_inputs, ws, st,
+                               cs);
+}
+
+int upipe_stack_bwd(upipe_dtype_t dtype, const upipe_block_shape_t* shape, int n_layers,
+                    const upipe_block_weights_t* weights, const void* host_inputs, const void* dy, void* dx,
+                    const upipe_block_grads_t* grads, void* workspace, size_t workspace_bytes, void* stream,
+                    void* copy_stream) {
+  BlockShape b;
+  if (grads == nullptr) return UPIPE_ERR_INVALID_ARG;
+  int rc = stack_check(dtype, shape, n_layers, weights, grads, &b);
+  if (rc) return rc;
+  const void* p[] = {host_inputs, dy, dx};
+  if ((rc = check_ptrs(p, 3))) return rc;
+  if (workspace == nullptr) return UPIPE_ERR_WORKSPACE;
+  if (!aligned(workspace, REGION_ALIGN)) return UPIPE_ERR_ALIGNMENT;
+  if (workspace_bytes < stack_plan(b, dtype).total) return UPIPE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t cs = copy_stream ? reinterpret_cast<hipStream_t>(copy_stream) : st;
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == UPIPE_BF16)
+    return stack_bwd_impl<bf16>(b, dtype, n_layers, weights, (const bf16*)host_inputs, (const bf16*)dy, (bf16*)dx,
+                                grads, ws, st, cs);
+  return stack_bwd_impl<float>(b, dtype, n_layers, weights, (const float*)host_inputs, (const float*)dy,
+                               (float*)dx, grads, ws, st, cs);
+}
 
 size_t upipe_block_workspace_bytes(const upipe_block_shape_t* shape, int qk_norm, upipe_dtype_t dtype,
                                    int backward) {

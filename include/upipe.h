@@ -291,6 +291,46 @@ int upipe_block_bwd(upipe_dtype_t dtype, const upipe_block_shape_t* shape, const
                     size_t workspace_bytes, void* stream);
 
 /*
+ * A stack of n_layers blocks of one shape (each with its own weights), with
+ * the block inputs offloaded to host memory between the passes: the talk
+ * keeps each transformer block's input off the GPU after the forward and
+ * prefetches it back for the backward ("Road to 5 Million Tokens", talk
+ * transcript, the part on CPU offloading; liquidgold.cc notes, "Progression
+ * of Techniques", item 5). The GPU holds two activation and two gradient
+ * buffers and one block workspace, whatever n_layers is.
+ *
+ * Forward: block l's input is copied to host_inputs[l] on copy_stream while
+ * block l runs on stream; block l + 1, which reuses that input's buffer,
+ * waits for the copy. y = the last block's output.
+ * Backward: block l's input is copied back into a device buffer on
+ * copy_stream while the blocks above it run their backward (two layers
+ * ahead); block l runs upipe_block_bwd from its input alone (checkpointing)
+ * and passes its dx down. dx = the first block's input gradient.
+ *
+ *   weights, grads: host arrays of n_layers structs (device pointers inside)
+ *   x, y, dy, dx [N][D] io dtype (device)
+ *   host_inputs [n_layers][N][D] io dtype, written by the forward and read by
+ *   the backward. Host memory from hipHostMalloc (pinned) lets the copies run
+ *   beside the compute; any memory HIP can copy gives the same results.
+ *   copy_stream: a second stream for the copies (NULL: stream itself, no
+ *   overlap). Both calls order the copies against stream with events: every
+ *   output, host_inputs included, is complete once stream reaches the end of
+ *   the call's work.
+ * Every layer's weights (and gradients) are checked before anything is
+ * enqueued; all layers must agree on having q/k norm.
+ */
+size_t upipe_stack_workspace_bytes(const upipe_block_shape_t* shape, int qk_norm, upipe_dtype_t dtype);
+
+int upipe_stack_fwd(upipe_dtype_t dtype, const upipe_block_shape_t* shape, int n_layers,
+                    const upipe_block_weights_t* weights, const void* x, void* y, void* host_inputs,
+                    void* workspace, size_t workspace_bytes, void* stream, void* copy_stream);
+
+int upipe_stack_bwd(upipe_dtype_t dtype, const upipe_block_shape_t* shape, int n_layers,
+                    const upipe_block_weights_t* weights, const void* host_inputs, const void* dy, void* dx,
+                    const upipe_block_grads_t* grads, void* workspace, size_t workspace_bytes, void* stream,
+                    void* copy_stream);
+
+/*
  * Optional per-kernel timing (for benchmarks and profilers; off by default).
  * While enabled, every kernel the library enqueues is bracketed by two
  * hipEvents on the caller's stream, and its algorithmic work (flops of the

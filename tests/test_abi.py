@@ -21,7 +21,8 @@ def test_exports_every_header_symbol(lib):
                           "upipe_attn_bwd", "upipe_strerror", "upipe_version", "upipe_profile_start",
                           "upipe_profile_stop", "upipe_mlp_workspace_bytes", "upipe_mlp_fwd", "upipe_mlp_bwd",
                           "upipe_loss_workspace_bytes", "upipe_loss_fwd", "upipe_loss_bwd",
-                          "upipe_block_workspace_bytes", "upipe_block_fwd", "upipe_block_bwd"}
+                          "upipe_block_workspace_bytes", "upipe_block_fwd", "upipe_block_bwd",
+                          "upipe_stack_workspace_bytes", "upipe_stack_fwd", "upipe_stack_bwd"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.upipe_version() == 100
@@ -394,3 +395,49 @@ def test_block_validation_errors(lib):
     assert _block_call(lib, bwd=True, grads=api.BlockGrads(**dict(full, w_down=P + 4))) == ALIGN
     need = api.block_workspace_bytes(api.block_shape(300, 256, 384, 128, 4, 2, 64, 2, 1e4), False, "bf16", True)
     assert _block_call(lib, bwd=True, wsb=need - 256) == WORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# stack of blocks with offloaded inputs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,D,F,T,hq,hkv,d,C", [(300, 256, 384, 128, 4, 2, 64, 2),
+                                               (32768, 4096, 14336, 4096, 32, 8, 128, 4)])
+def test_stack_workspace_formula(N, D, F, T, hq, hkv, d, C):
+    s = api.block_shape(N, D, F, T, hq, hkv, d, C, 5e5)
+    for dt, es in (("fp32", 4), ("bf16", 2)):
+        blk = max(api.block_workspace_bytes(s, False, dt, False), api.block_workspace_bytes(s, False, dt, True))
+        assert api.stack_workspace_bytes(s, False, dt) == 4 * _r256(N * D * es) + blk
+    assert api.stack_workspace_bytes(api.block_shape(N, 200, F, T, hq, hkv, d, C, 5e5), False, "bf16") == 0
+
+
+def test_stack_validation_errors(lib):
+    s = api.block_shape(300, 256, 384, 128, 4, 2, 64, 2, 1e4)
+    full = {n: P for n in api._BLOCK_TENSORS if n not in ("q_norm", "k_norm")}
+    need = api.stack_workspace_bytes(s, False, "bf16")
+
+    def fwd(L=3, layers=None, x=P, y=P, host=P, ws=P, wsb=need, dtype=1):
+        w = (api.BlockWeights * max(L, 1))(*(layers or [api.BlockWeights(**full)] * max(L, 1)))
+        return lib.upipe_stack_fwd(dtype, ctypes.byref(s), L, w, x, y, host, ws, wsb, None, None)
+
+    def bwd(L=3, grads=None, host=P, dy=P, dx=P, wsb=need):
+        w = (api.BlockWeights * L)(*[api.BlockWeights(**full)] * L)
+        g = (api.BlockGrads * L)(*(grads or [api.BlockGrads(**full)] * L))
+        return lib.upipe_stack_bwd(1, ctypes.byref(s), L, w, host, dy, dx, g, P, wsb, None, None)
+
+    assert fwd(L=0) == INVALID
+    assert fwd(dtype=9) == INVALID
+    # a bad weight in the last layer is found before anything is enqueued
+    bad = [api.BlockWeights(**full), api.BlockWeights(**full), api.BlockWeights(**dict(full, w_down=None))]
+    assert fwd(layers=bad) == INVALID
+    mixed = [api.BlockWeights(**full), api.BlockWeights(**dict(full, q_norm=P, k_norm=P)), api.BlockWeights(**full)]
+    assert fwd(layers=mixed) == INVALID
+    assert fwd(host=None) == INVALID
+    assert fwd(host=P + 8) == ALIGN
+    assert fwd(y=None) == INVALID
+    assert fwd(wsb=need - 256) == WORKSPACE
+    assert fwd(ws=None) == WORKSPACE
+    assert bwd(grads=[api.BlockGrads(**full), api.BlockGrads(**dict(full, wq=None)), api.BlockGrads(**full)]) \
+        == INVALID
+    assert bwd(host=None) == INVALID
+    assert bwd(dx=P + 2) == ALIGN
+    assert bwd(wsb=need - 1) == WORKSPACE
