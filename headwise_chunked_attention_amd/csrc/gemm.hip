@@ -54,21 +54,37 @@ constexpr int gemm_smem_bytes() {
 
 // One 16-wide k step of a 2 x 2 wave grid over a BM x BN tile held in LDS as
 // As[m][k], Bs[n][k] (row stride SK).
+// The wave's A and B fragments of k step ks (16 k) of a tile in LDS.
 template <typename T, int BN>
-DEV void mma_tile_step(const T* As, const T* Bs, int SK, int ks, int wm, int wn,
-                       f32x16 (&acc)[2][BN / 64]) {
-  constexpr int NTW = BN / 64;
+struct TileFrags {
+  Frag<T> a[2], b[BN / 64];
+};
+
+template <typename T, int BN>
+DEV void load_frags(const T* As, const T* Bs, int SK, int ks, int wm, int wn, TileFrags<T, BN>& f) {
   const int l = lane_id();
   const int r = l & 31, h = l >> 5;
-  Frag<T> a[2], b[NTW];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) a[mt] = ld_frag(As + (wm * 64 + mt * 32 + r) * SK + ks * 16 + 8 * h);
+  for (int mt = 0; mt < 2; ++mt) f.a[mt] = ld_frag(As + (wm * 64 + mt * 32 + r) * SK + ks * 16 + 8 * h);
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) b[nt] = ld_frag(Bs + (wn * (BN / 2) + nt * 32 + r) * SK + ks * 16 + 8 * h);
+  for (int nt = 0; nt < BN / 64; ++nt) f.b[nt] = ld_frag(Bs + (wn * (BN / 2) + nt * 32 + r) * SK + ks * 16 + 8 * h);
+}
+
+// All k steps of one LDS tile, the fragments of step ks + 1 read before the
+// MFMAs of step ks are issued (their LDS latency overlaps those MFMAs).
+template <typename T, int BN, int KS>
+DEV void mma_tile(const T* As, const T* Bs, int SK, int wm, int wn, f32x16 (&acc)[2][BN / 64]) {
+  TileFrags<T, BN> f[2];
+  load_frags<T, BN>(As, Bs, SK, 0, wm, wn, f[0]);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) load_frags<T, BN>(As, Bs, SK, ks + 1, wm, wn, f[(ks + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this step's MFMAs
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) mma(acc[mt][nt], a[mt], b[nt]);
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < BN / 64; ++nt) mma(acc[mt][nt], f[ks & 1].a[mt], f[ks & 1].b[nt]);
+  }
 }
 
 // Accumulators -> fp32 LDS tile Cs[rows][BN + 4]; row0 is the tile row of
@@ -395,8 +411,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
     }
     const T* Ab = As + buf * BM * SK;
     const T* Bb = Bs + buf * BN * SK;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) mma_tile_step<T, BN>(Ab, Bb, SK, ks, wm, wn, acc);
+    mma_tile<T, BN, BK / 16>(Ab, Bb, SK, wm, wn, acc);
     if (NPF > 1 || kt + 1 < nk)
       nt_store_tile<T, BN, G>(As + (buf ^ 1) * BM * SK, Bs + (buf ^ 1) * BN * SK, ra[NEXT], rb[NEXT]);
     lds_barrier();
