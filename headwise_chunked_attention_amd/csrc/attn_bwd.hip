@@ -435,12 +435,25 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
       // (or -Delta) of this lane's query, so the MFMAs do the subtraction.
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x16 sacc = mma_first(ld_frag(Ks + L::idx(kt * 32 + r, 8 * h)), qf[0], init_s);
-        f32x16 dpacc = mma_first(ld_frag(Vs + L::idx(kt * 32 + r, 8 * h)), df[0], init_dp);
+        // the K and V fragments of step s + 1 are read before the MFMAs of step s
+        f32x16 sacc, dpacc;
+        Frag<T> kf[2], vf[2];
+        kf[0] = ld_frag(Ks + L::idx(kt * 32 + r, 8 * h));
+        vf[0] = ld_frag(Vs + L::idx(kt * 32 + r, 8 * h));
 #pragma unroll
-        for (int s = 1; s < NS; ++s) {
-          mma(sacc, ld_frag(Ks + L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[s]);
-          mma(dpacc, ld_frag(Vs + L::idx(kt * 32 + r, s * 16 + 8 * h)), df[s]);
+        for (int s = 0; s < NS; ++s) {
+          if (s + 1 < NS) {
+            kf[(s + 1) & 1] = ld_frag(Ks + L::idx(kt * 32 + r, (s + 1) * 16 + 8 * h));
+            vf[(s + 1) & 1] = ld_frag(Vs + L::idx(kt * 32 + r, (s + 1) * 16 + 8 * h));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (s == 0) {
+            sacc = mma_first(kf[0], qf[0], init_s);
+            dpacc = mma_first(vf[0], df[0], init_dp);
+          } else {
+            mma(sacc, kf[s & 1], qf[s]);
+            mma(dpacc, vf[s & 1], df[s]);
+          }
         }
         // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d) (log2 units and the
         // 1/sqrt(d) come with the pre-scaled q and dout)

@@ -182,14 +182,26 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
         // S^T of both 32-key halves (two independent chains), each chain
         // started from the splat of -base, so it holds S - base (log2 units);
         // then softmax and P V half by half.
+        // The K fragments of step s + 1 are read before the MFMAs of step s
+        // issue, so their LDS latency overlaps those MFMAs.
         f32x16 sacc2[2];
+        Frag<T> kf[2][2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) sacc2[kt] = mma_first(ld_frag(Ks + G::L::idx(kt * 32 + r, 8 * h)), qf[0][0], init);
+        for (int kt = 0; kt < 2; ++kt) kf[0][kt] = ld_frag(Ks + G::L::idx(kt * 32 + r, 8 * h));
 #pragma unroll
-        for (int s = 1; s < NS; ++s)
+        for (int s = 0; s < NS; ++s) {
+          if (s + 1 < NS)
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-            mma(sacc2[kt], ld_frag(Ks + G::L::idx(kt * 32 + r, s * 16 + 8 * h)), qf[0][s]);
+            for (int kt = 0; kt < 2; ++kt) kf[(s + 1) & 1][kt] = ld_frag(Ks + G::L::idx(kt * 32 + r, (s + 1) * 16 + 8 * h));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            if (s == 0)
+              sacc2[kt] = mma_first(kf[0][kt], qf[0][0], init);
+            else
+              mma(sacc2[kt], kf[s & 1][kt], qf[0][s]);
+          }
+        }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           f32x16& sacc = sacc2[kt];
