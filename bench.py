@@ -235,10 +235,9 @@ def block_bench(dev, steps, warmup):
     prof = api.profile_stop()
     attn_fwd_model = 2.0 * d * hq * N * (N + 1) + 4.0 * N * D * d * (hq + hkv)
     model = model_flops(N, D, hq, hkv, d) + 18.0 * N * D * F
-    # recomputed in the backward: the attention forward, O inside the
-    # attention backward, and the MLP's h|u
-    hw = model + attn_fwd_model + (hardware_flops(N, D, hq, hkv, d) - model_flops(N, D, hq, hkv, d)) \
-        + 4.0 * N * D * F
+    # recomputed in the backward: the attention forward (which keeps O for
+    # the attention backward) and the MLP's h|u
+    hw = model + attn_fwd_model + 4.0 * N * D * F
     step_ms = float(np.median([a + b for a, b in zip(t_f, t_b)]))
     kinds = {k: {"ms": v["ms"], "launches": v["launches"],
                  "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None}

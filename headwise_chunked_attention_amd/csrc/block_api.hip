@@ -16,6 +16,9 @@
 //   B   [T][D]   one tile of b (the MLP's input)
 //   DB  [T][D]   one tile of the MLP's dx (backward)
 //   LSE [Hq][N]  fp32, the lse when the caller keeps none
+//   O   [Hq][Np][d]  backward from the block input alone: every head's O,
+//                kept by the rerun attention forward so that the attention
+//                backward does not recompute it (Np = N padded)
 //   stage        shared by the attention op and the MLP, which never run at
 //                the same time: the larger of their workspaces
 // Buffers reused across steps of the backward: dx first holds the
@@ -42,7 +45,7 @@ struct BlockShape {
 };
 
 struct BlockPlan {
-  size_t A, DA, B, DB, lse, stage, total;
+  size_t A, DA, B, DB, lse, O, stage, total;
 };
 
 int block_check_shape(int dtype, const upipe_block_shape_t* sh, int qk_norm, BlockShape* out) {
@@ -80,6 +83,7 @@ BlockPlan block_plan(const BlockShape& b, upipe_dtype_t dt, bool backward) {
   p.B = c.take(td);
   if (backward) p.DB = c.take(td);
   p.lse = c.take((size_t)s.n_q_heads * s.n_tokens * 4);
+  if (backward) p.O = c.take((size_t)s.n_q_heads * attn_padded_rows(s.n_tokens) * s.head_dim * b.es);
   size_t stage = attn_ws(b, dt, 0);
   const size_t mw = mlp::plan(b.m, backward).total;
   if (mw > stage) stage = mw;
@@ -187,9 +191,14 @@ int block_bwd_impl(const BlockShape& b, upipe_dtype_t dt, const T* x, const upip
   int rc = row_norm<T>(x, nullptr, gm_attn, nullptr, nullptr, A, N, D, eps, st);
   if (rc) return rc;
   const float* L = lse;
+  T* Okept = nullptr;
+  const AttnCall ac = {dt, N, D, s.n_q_heads, s.n_kv_heads, s.head_dim, s.rope_theta, s.chunk_heads, s.qk_norm_eps};
   if (recompute) {
     float* Lw = reinterpret_cast<float*>(ws + pl.lse);
-    if ((rc = attn_fwd_call<T>(b, dt, A, w, dx, Lw, stage, stage_bytes, st))) return rc;
+    Okept = reinterpret_cast<T*>(ws + pl.O);
+    if ((rc = attn_fwd_keep_o<T>(ac, A, w.wq, w.wk, w.wv, w.wo, w.q_norm, w.k_norm, dx, Lw, Okept, stage,
+                                 stage_bytes, st)))
+      return rc;
     L = Lw;
   }
   // MLP half, tile by tile: b = rmsnorm(h), db = mlp_bwd(b, dy),
@@ -212,10 +221,14 @@ int block_bwd_impl(const BlockShape& b, upipe_dtype_t dt, const T* x, const upip
     if ((rc = row_norm_bwd<T>(ht, DB, gm_mlp, dy + t0 * D, dxt, g.mlp_norm, rows, D, eps, st))) return rc;
   }
   // attention half: da = attention_bwd(a, dh); dx = dh + rmsnorm_bwd(x, da)
-  if ((rc = upipe_attn_bwd(dt, N, D, s.n_q_heads, s.n_kv_heads, s.head_dim, s.rope_theta, s.chunk_heads, A, w.wq,
-                           w.wk, w.wv, w.wo, w.q_norm, w.k_norm, s.qk_norm_eps, dx, L, DA, g.wq, g.wk, g.wv, g.wo,
-                           g.q_norm, g.k_norm, stage, stage_bytes, st)))
-    return rc;
+  if (Okept)
+    rc = attn_bwd_kept_o<T>(ac, A, w.wq, w.wk, w.wv, w.wo, w.q_norm, w.k_norm, dx, L, Okept, DA, g.wq, g.wk, g.wv,
+                            g.wo, g.q_norm, g.k_norm, stage, stage_bytes, st);
+  else
+    rc = upipe_attn_bwd(dt, N, D, s.n_q_heads, s.n_kv_heads, s.head_dim, s.rope_theta, s.chunk_heads, A, w.wq, w.wk,
+                        w.wv, w.wo, w.q_norm, w.k_norm, s.qk_norm_eps, dx, L, DA, g.wq, g.wk, g.wv, g.wo, g.q_norm,
+                        g.k_norm, stage, stage_bytes, st);
+  if (rc) return rc;
   return row_norm_bwd<T>(x, DA, gm_attn, dx, dx, g.attn_norm, N, D, eps, st);
 }
 

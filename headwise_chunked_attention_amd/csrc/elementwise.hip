@@ -226,6 +226,19 @@ __global__ __launch_bounds__(256) void fill_f32_kernel(float* p, int64_t n, floa
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
+// One wave per row: out[r] = a[r] . b[r] over d <= 128 elements (each lane
+// takes d / 64 of them).
+template <typename T>
+__global__ __launch_bounds__(256) void row_dot_kernel(const T* a, const T* b, int64_t rows, int d, float* out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (row >= rows) return;
+  float v = 0.f;
+  for (int k = l; k < d; k += 64) v += to_f<T>(a[row * d + k]) * to_f<T>(b[row * d + k]);
+  v = wave_sum(v);
+  if (l == 0) out[row] = v;
+}
+
 // One wave per row: combine the row's per-tile (max, sum exp) partials.
 __global__ __launch_bounds__(256) void ce_reduce_kernel(const float* part, const float* tgt, int64_t rows,
                                                         int64_t ntiles, float* lse, float* loss) {
@@ -329,6 +342,16 @@ hipError_t launch_row_norm_bwd(const RowNormBwd<T>& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_row_dot(const T* a, const T* b, int64_t rows, int d, float* out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (d < 1 || d > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((row_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, b, rows, d, out);
+  return hipGetLastError();
+}
+
+template hipError_t launch_row_dot<bf16>(const bf16*, const bf16*, int64_t, int, float*, hipStream_t);
+template hipError_t launch_row_dot<float>(const float*, const float*, int64_t, int, float*, hipStream_t);
 template hipError_t launch_row_norm<bf16>(const RowNorm<bf16>&, hipStream_t);
 template hipError_t launch_row_norm<float>(const RowNorm<float>&, hipStream_t);
 template hipError_t launch_row_norm_bwd<bf16>(const RowNormBwd<bf16>&, hipStream_t);

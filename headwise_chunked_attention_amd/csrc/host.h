@@ -69,6 +69,33 @@ hipError_t timed(int kind, double flops, hipStream_t st, F&& launch) {
 // rope_theta, q/k norm epsilon): UPIPE_OK or the code they would return.
 int attn_check_args(int dtype, int64_t N, int64_t D, int Hq, int Hkv, int d, double theta, int C, float eps);
 
+// Token rows of the attention engine's per-head buffers (N padded).
+int64_t attn_padded_rows(int64_t N);
+
+// Scalar arguments of one attention call.
+struct AttnCall {
+  int dtype;
+  int64_t N, D;
+  int Hq, Hkv, d;
+  double theta;
+  int C;
+  float eps;  // q/k norm
+};
+
+// The attention forward that also keeps every head's O in o_keep
+// ([Hq][attn_padded_rows(N)][d], io dtype), and the backward that takes that O
+// instead of recomputing it (Delta = rowsum(dO o O) from it, and dWo). Same
+// checks, workspace and results as upipe_attn_fwd / upipe_attn_bwd.
+template <typename T>
+int attn_fwd_keep_o(const AttnCall& c, const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                    const void* qn, const void* kn, void* y, float* lse, T* o_keep, void* ws, size_t bytes,
+                    hipStream_t st);
+template <typename T>
+int attn_bwd_kept_o(const AttnCall& c, const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                    const void* qn, const void* kn, const void* dy, const float* lse, const T* o_kept, void* dx,
+                    float* dwq, float* dwk, float* dwv, float* dwo, float* dqn, float* dkn, void* ws, size_t bytes,
+                    hipStream_t st);
+
 }  // namespace upipe
 
 #define HIP_TRY(x)                                 \

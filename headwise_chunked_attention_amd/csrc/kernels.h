@@ -218,6 +218,9 @@ template <typename T>
 hipError_t launch_transpose(const T* src, int64_t rows, int64_t cols, int64_t ld_src, T* dst,
                             int64_t ld_dst, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// out[r] = sum_k a[r * d + k] * b[r * d + k] for rows r < rows (d = 64 or 128), fp32.
+template <typename T>
+hipError_t launch_row_dot(const T* a, const T* b, int64_t rows, int d, float* out, hipStream_t s);
 // Per row m < rows: lse[m] = log sum over the ntiles tiles of the row's
 // (max, sum exp) partials; loss[m] = lse[m] - tgt[m].
 hipError_t launch_ce_reduce(const float* part, const float* tgt, int64_t rows, int64_t ntiles, float* lse,

@@ -212,12 +212,12 @@ int run_weight_grad(const Shape& s, const T* rows, const T* heads, int nheads, f
 template <typename T>
 int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T* wk, const T* wv,
                   const T* wo, const T* qn, const T* kn, float eps, T* y, float* lse, char* ws,
-                  hipStream_t st) {
+                  hipStream_t st, T* o_keep = nullptr) {
   const Plan pl = make_plan(s, false);
   T* Q = reinterpret_cast<T*>(ws + pl.q);
   T* K = reinterpret_cast<T*>(ws + pl.k);
   T* V = reinterpret_cast<T*>(ws + pl.v);
-  T* O = reinterpret_cast<T*>(ws + pl.o);
+  T* Ows = reinterpret_cast<T*>(ws + pl.o);
   const double l2t = log2(theta);
   const int64_t head = s.Np * s.d;
   const int nh = s.C < s.G ? s.C : s.G;  // q heads of the chunk per kv head
@@ -225,6 +225,8 @@ int attn_fwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   for (int c0 = 0; c0 < s.Hq; c0 += s.C) {
     const int g0 = c0 / s.G;
     const bool new_kv = (c0 % s.G) == 0;
+    // the chunk's O: the reused workspace buffer, or its heads of the kept O
+    T* O = o_keep ? o_keep + (int64_t)c0 * head : Ows;
     const T* w[3] = {wq + (int64_t)c0 * s.d * s.D, wk + (int64_t)g0 * s.d * s.D, wv + (int64_t)g0 * s.d * s.D};
     const int nheads[3] = {s.C, s.kvC, s.kvC};
     HeadOut<T> ho[3];
@@ -266,7 +268,7 @@ template <typename T>
 int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T* wk, const T* wv,
                   const T* wo, const T* qn, const T* kn, float eps, const T* dy, const float* lse,
                   T* dx, float* dwq, float* dwk, float* dwv, float* dwo, float* dqn, float* dkn,
-                  char* ws, hipStream_t st) {
+                  char* ws, hipStream_t st, const T* o_kept = nullptr) {
   const Plan pl = make_plan(s, true);
   T* Q = reinterpret_cast<T*>(ws + pl.q);
   T* Uq = s.norm ? reinterpret_cast<T*>(ws + pl.uq) : nullptr;
@@ -274,7 +276,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   T* V = reinterpret_cast<T*>(ws + pl.v);
   T* Uk = s.norm ? reinterpret_cast<T*>(ws + pl.uk) : nullptr;
   T* dO = reinterpret_cast<T*>(ws + pl.dout);
-  T* O = reinterpret_cast<T*>(ws + pl.o);
+  T* Ows = reinterpret_cast<T*>(ws + pl.o);
   float* Delta = reinterpret_cast<float*>(ws + pl.delta);
   float* dQa = reinterpret_cast<float*>(ws + pl.dq_acc);
   float* dKa = reinterpret_cast<float*>(ws + pl.dk_acc);
@@ -347,14 +349,19 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       int rc = run_projection<T>(s, dy, 1, w, nheads, ho, eps, l2t, st);
       if (rc) return rc;
     }
-    // recompute O_c from the saved LSE, and Delta = rowsum(dO o O)
-    for (int j = 0; j < s.kvC; ++j) {
+    // recompute O_c from the saved LSE, and Delta = rowsum(dO o O); with O
+    // kept by the forward, only Delta
+    const T* O = o_kept ? o_kept + (int64_t)c0 * head : Ows;
+    if (o_kept)
+      HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st,
+                    [&] { return launch_row_dot<T>(dO, O, (int64_t)s.C * s.Np, s.d, Delta, st); }));
+    for (int j = 0; j < s.kvC && !o_kept; ++j) {
       AttnFwd<T> a;
       memset(&a, 0, sizeof(a));
       a.q = Q + (int64_t)j * nh * head;
       a.k = K + (int64_t)j * head;
       a.v = V + (int64_t)j * head;
-      a.o = O + (int64_t)j * nh * head;
+      a.o = Ows + (int64_t)j * nh * head;
       a.lse = const_cast<float*>(lse) + (int64_t)(c0 + j * nh) * s.N;
       a.lse_stride = s.N;
       a.dout = dO + (int64_t)j * nh * head;
@@ -484,6 +491,56 @@ int check_ws(const Shape& s, bool bwd, const void* ws, size_t bytes) {
 }  // namespace
 
 namespace upipe {
+int64_t attn_padded_rows(int64_t N) { return round_up(N, ROW_PAD); }
+
+template <typename T>
+int attn_fwd_keep_o(const AttnCall& c, const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                    const void* qn, const void* kn, void* y, float* lse, T* o_keep, void* ws, size_t bytes,
+                    hipStream_t st) {
+  Shape s;
+  int rc = check_common(c.dtype, c.N, c.D, c.Hq, c.Hkv, c.d, c.theta, c.C, qn, kn, c.eps, &s);
+  if (rc) return rc;
+  const void* ptrs[] = {x, wq, wk, wv, wo, y, lse, o_keep};
+  if ((rc = check_ptrs(ptrs, 8))) return rc;
+  if ((rc = check_ws(s, false, ws, bytes))) return rc;
+  return attn_fwd_impl<T>(s, c.theta, (const T*)x, (const T*)wq, (const T*)wk, (const T*)wv, (const T*)wo,
+                          (const T*)qn, (const T*)kn, c.eps, (T*)y, lse, (char*)ws, st, o_keep);
+}
+
+template <typename T>
+int attn_bwd_kept_o(const AttnCall& c, const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                    const void* qn, const void* kn, const void* dy, const float* lse, const T* o_kept, void* dx,
+                    float* dwq, float* dwk, float* dwv, float* dwo, float* dqn, float* dkn, void* ws, size_t bytes,
+                    hipStream_t st) {
+  Shape s;
+  int rc = check_common(c.dtype, c.N, c.D, c.Hq, c.Hkv, c.d, c.theta, c.C, qn, kn, c.eps, &s);
+  if (rc) return rc;
+  const void* ptrs[] = {x, wq, wk, wv, wo, dy, lse, o_kept, dx, dwq, dwk, dwv, dwo};
+  if ((rc = check_ptrs(ptrs, 13))) return rc;
+  if (s.norm) {
+    const void* np[] = {dqn, dkn};
+    if ((rc = check_ptrs(np, 2))) return rc;
+  }
+  if ((rc = check_ws(s, true, ws, bytes))) return rc;
+  return attn_bwd_impl<T>(s, c.theta, (const T*)x, (const T*)wq, (const T*)wk, (const T*)wv, (const T*)wo,
+                          (const T*)qn, (const T*)kn, c.eps, (const T*)dy, lse, (T*)dx, dwq, dwk, dwv, dwo, dqn, dkn,
+                          (char*)ws, st, o_kept);
+}
+
+template int attn_fwd_keep_o<bf16>(const AttnCall&, const void*, const void*, const void*, const void*,
+                                   const void*, const void*, const void*, void*, float*, bf16*, void*, size_t,
+                                   hipStream_t);
+template int attn_fwd_keep_o<float>(const AttnCall&, const void*, const void*, const void*, const void*,
+                                    const void*, const void*, const void*, void*, float*, float*, void*, size_t,
+                                    hipStream_t);
+template int attn_bwd_kept_o<bf16>(const AttnCall&, const void*, const void*, const void*, const void*,
+                                   const void*, const void*, const void*, const void*, const float*, const bf16*,
+                                   void*, float*, float*, float*, float*, float*, float*, void*, size_t, hipStream_t);
+template int attn_bwd_kept_o<float>(const AttnCall&, const void*, const void*, const void*, const void*,
+                                    const void*, const void*, const void*, const void*, const float*, const float*,
+                                    void*, float*, float*, float*, float*, float*, float*, void*, size_t,
+                                    hipStream_t);
+
 int attn_check_args(int dtype, int64_t N, int64_t D, int Hq, int Hkv, int d, double theta, int C, float eps) {
   Shape s;
   const int rc = check_shape(dtype, N, D, Hq, Hkv, d, C, &s);

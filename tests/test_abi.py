@@ -325,8 +325,8 @@ def _expected_block_ws(N, D, F, T, hq, hkv, d, C, norm, dt, es, bwd):
     rows = min(T, (N + 127) // 128 * 128)
     nd, td = _r256(N * D * es), _r256(rows * D * es)
     t = nd + td + _r256(hq * N * 4)
-    if bwd:
-        t += nd + td
+    if bwd:  # da, the db tile, and every head's O kept by the rerun forward
+        t += nd + td + _r256(hq * ((N + 255) // 256 * 256) * d * es)
     stage = max(_expected_ws(N, D, hq, hkv, d, C, norm, es, False), _expected_mlp_ws(N, D, F, T, es, bwd))
     if bwd:
         stage = max(stage, _expected_ws(N, D, hq, hkv, d, C, norm, es, True))
