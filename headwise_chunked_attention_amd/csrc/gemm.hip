@@ -746,6 +746,8 @@ hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s) {
+  // whole tiles along M and N; every split holds at least one k row
+  if (p.K <= 0 || p.ksplit <= 0 || p.M <= 0 || p.M % BM || bn <= 0 || p.N <= 0 || p.N % bn) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((p.M / BM) * (p.N / bn) * ((p.K + p.ksplit - 1) / p.ksplit)));
   if (bn == 128)
     hipLaunchKernelGGL((gemm_tn_kernel<T, 128>), grid, dim3(NTHREADS), 0, s, p);
