@@ -439,6 +439,12 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
           if (m0 + wm * 64 + mt * 32 + 8 * (e / 4) + 4 * h + e % 4 >= p.M) acc[mt][nt][e] = 0.f;
   }
 
+  // Head-wise epilogue: the rotary frequencies theta^(-2i/d) of the tile's
+  // columns, once per workgroup (read after the first pass's barrier).
+  __shared__ double omega_s[EPI == EPI_HEADS ? BN / 2 : 1];
+  if constexpr (EPI == EPI_HEADS)
+    if (tid < BN / 2) omega_s[tid] = exp2(-(2.0 * tid / BN) * p.log2_theta);
+
   // Epilogue in two passes of EPI_ROWS tile rows through Cs[EPI_ROWS][BN + 4].
   float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -498,12 +504,14 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
           }
         }
         if (ho.rope) {
+          // angle p * omega_i in fp64, reduced mod 2 pi in fp64 (|r| <= pi);
+          // sin and cos of the reduced angle in fp32
           const double pos = (double)(mr + row);
           for (int i = qq * PP; i < qq * PP + PP; ++i) {
-            const double omega = exp2(-(2.0 * i / BN) * p.log2_theta);
-            double sd, cd;
-            sincos(pos * omega, &sd, &cd);
-            const float c = (float)cd, sn = (float)sd;
+            const double ang = pos * omega_s[i];
+            const double red = fma(-rint(ang * 0.15915494309189535), 6.283185307179586, ang);
+            float sn, c;
+            sincosf((float)red, &sn, &c);
             const float u = cr[i], wv = cr[i + BN / 2];
             cr[i] = u * c - wv * sn;
             cr[i + BN / 2] = wv * c + u * sn;
