@@ -275,15 +275,27 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
           } else {
             make_p0();
           }
-          // O^T += V^T P^T over the half's keys (rows kt*32 + 16*s2 + ... of V)
+          // O^T += V^T P^T over the half's keys (rows kt*32 + 16*s2 + ... of V):
+          // 2*ND products t = (s2, j). In the recompute the V^T fragment of
+          // product t + 2 is read before product t issues (faster there,
+          // slower in the training forward, which keeps the compiler's order).
+          auto vfrag = [&](int t) {
+            const T* Vr = Vs + (kt * 32 + 16 * (t / ND)) * G::L::STRIDE;
+            return frag_from_col4<T>(ld_col4_at(Vr, vplan.off[0][t % ND]), ld_col4_at(Vr, vplan.off[1][t % ND]));
+          };
+          if constexpr (MODE == 1) {
+            Frag<T> vf[3];
+            vf[0] = vfrag(0);
+            vf[1] = vfrag(1);
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const T* Vr = Vs + (kt * 32 + 16 * s2) * G::L::STRIDE;
-#pragma unroll
-            for (int j = 0; j < ND; ++j) {
-              const Frag<T> a = frag_from_col4<T>(ld_col4_at(Vr, vplan.off[0][j]), ld_col4_at(Vr, vplan.off[1][j]));
-              mma(oacc[0][j], a, pf[s2]);
+            for (int t = 0; t < 2 * ND; ++t) {
+              if (t + 2 < 2 * ND) vf[(t + 2) % 3] = vfrag(t + 2);
+              __builtin_amdgcn_sched_barrier(0);
+              mma(oacc[0][t % ND], vf[t % 3], pf[t / ND]);
             }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 2 * ND; ++t) mma(oacc[0][t % ND], vfrag(t), pf[t / ND]);
           }
         }
       }
