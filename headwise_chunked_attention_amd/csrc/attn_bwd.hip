@@ -467,23 +467,33 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) dpacc[e] = sacc[e] * dpacc[e];
-        // dQ^T += K^T dS^T (contraction over the half's keys = accumulator rows)
+        // dQ^T += K^T dS^T (contraction over the half's keys = accumulator
+        // rows): 2*ND products t = (s2, j); bf16 reads the K^T fragment of
+        // product t + 2 before product t issues
+        const Frag<T> sbf[2] = {frag_from_acc<T>(dpacc, 0, 1.0f), frag_from_acc<T>(dpacc, 1, 1.0f)};
+        if constexpr (sizeof(T) == 2) {
+          auto kfrag = [&](int t) {
+            // rows kt*32 + 16*s2 + ... of K at the precomputed lane offsets
+            const T* Kr = Ks + (kt * 32 + 16 * (t / ND)) * L::STRIDE;
+            return frag_from_col4<T>(ld_col4_at(Kr, kplan.off[0][t % ND]), ld_col4_at(Kr, kplan.off[1][t % ND]));
+          };
+          Frag<T> kf3[3];
+          kf3[0] = kfrag(0);
+          kf3[1] = kfrag(1);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const Frag<T> sb = frag_from_acc<T>(dpacc, s2, 1.0f);
-#pragma unroll
-          for (int j = 0; j < ND; ++j) {
-            Frag<T> a;
-            if constexpr (sizeof(T) == 2) {
-              // rows kt*32 + 16*s2 + ... of K at the precomputed lane offsets
-              const T* Kr = Ks + (kt * 32 + 16 * s2) * L::STRIDE;
-              a = frag_from_col4<T>(ld_col4_at(Kr, kplan.off[0][j]), ld_col4_at(Kr, kplan.off[1][j]));
-            } else {
-              const int row0 = kt * 32 + 16 * s2 + 4 * h;
-              a = frag_from_col4<T>(ld_col4<L>(Ks, row0, j * 32), ld_col4<L>(Ks, row0 + 8, j * 32));
-            }
-            mma(dq[j], a, sb);
+          for (int t = 0; t < 2 * ND; ++t) {
+            if (t + 2 < 2 * ND) kf3[(t + 2) % 3] = kfrag(t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(dq[t % ND], kf3[t % 3], sbf[t / ND]);
           }
+        } else {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int j = 0; j < ND; ++j) {
+              const int row0 = kt * 32 + 16 * s2 + 4 * h;
+              mma(dq[j], frag_from_col4<T>(ld_col4<L>(Ks, row0, j * 32), ld_col4<L>(Ks, row0 + 8, j * 32)), sbf[s2]);
+            }
         }
       }
     }
