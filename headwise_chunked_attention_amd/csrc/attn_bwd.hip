@@ -236,26 +236,40 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
 #pragma unroll
     for (int e = 0; e < 16; ++e) dpacc[e] = sacc[e] * dpacc[e];
     // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries.
+    if constexpr (sizeof(T) == 2) {
+      // 2*ND product pairs t = (s2, j); the dO^T and Q^T fragments of pair
+      // t + 1 are read before pair t issues
+      const Frag<T> pbf[2] = {frag_from_acc<T>(sacc, 0, 1.0f), frag_from_acc<T>(sacc, 1, 1.0f)};
+      const Frag<T> sbf[2] = {frag_from_acc<T>(dpacc, 0, 1.0f), frag_from_acc<T>(dpacc, 1, 1.0f)};
+      Frag<T> ado[2], aq[2];
+      auto frags = [&](int t, int i) {
+        // rows qt*32 + 16*s2 + ... of dO and Q at the precomputed lane offsets
+        const T* dOr = dOs + (qt * 32 + 16 * (t / ND)) * L::STRIDE;
+        const T* Qr = Qs + (qt * 32 + 16 * (t / ND)) * L::STRIDE;
+        ado[i] = frag_from_col4<T>(ld_col4_at(dOr, cplan.off[0][t % ND]), ld_col4_at(dOr, cplan.off[1][t % ND]));
+        aq[i] = frag_from_col4<T>(ld_col4_at(Qr, cplan.off[0][t % ND]), ld_col4_at(Qr, cplan.off[1][t % ND]));
+      };
+      frags(0, 0);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const Frag<T> pb = frag_from_acc<T>(sacc, s2, 1.0f);
-      const Frag<T> sb = frag_from_acc<T>(dpacc, s2, 1.0f);
-      const int row0 = qt * 32 + 16 * s2 + 4 * h;
+      for (int t = 0; t < 2 * ND; ++t) {
+        if (t + 1 < 2 * ND) frags(t + 1, (t + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(dv[t % ND], ado[t & 1], pbf[t / ND]);
+        mma(dk[t % ND], aq[t & 1], sbf[t / ND]);
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < ND; ++j) {
-        Frag<T> ado, aq;
-        if constexpr (sizeof(T) == 2) {
-          // rows qt*32 + 16*s2 + ... of dO and Q at the precomputed lane offsets
-          const T* dOr = dOs + (qt * 32 + 16 * s2) * L::STRIDE;
-          const T* Qr = Qs + (qt * 32 + 16 * s2) * L::STRIDE;
-          ado = frag_from_col4<T>(ld_col4_at(dOr, cplan.off[0][j]), ld_col4_at(dOr, cplan.off[1][j]));
-          aq = frag_from_col4<T>(ld_col4_at(Qr, cplan.off[0][j]), ld_col4_at(Qr, cplan.off[1][j]));
-        } else {
-          ado = frag_from_col4<T>(ld_col4<L>(dOs, row0, j * 32), ld_col4<L>(dOs, row0 + 8, j * 32));
-          aq = frag_from_col4<T>(ld_col4<L>(Qs, row0, j * 32), ld_col4<L>(Qs, row0 + 8, j * 32));
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const Frag<T> pb = frag_from_acc<T>(sacc, s2, 1.0f);
+        const Frag<T> sb = frag_from_acc<T>(dpacc, s2, 1.0f);
+        const int row0 = qt * 32 + 16 * s2 + 4 * h;
+#pragma unroll
+        for (int j = 0; j < ND; ++j) {
+          const Frag<T> ado = frag_from_col4<T>(ld_col4<L>(dOs, row0, j * 32), ld_col4<L>(dOs, row0 + 8, j * 32));
+          const Frag<T> aq = frag_from_col4<T>(ld_col4<L>(Qs, row0, j * 32), ld_col4<L>(Qs, row0 + 8, j * 32));
+          mma(dv[j], ado, pb);
+          mma(dk[j], aq, sb);
         }
-        mma(dv[j], ado, pb);
-        mma(dk[j], aq, sb);
       }
     }
     if (it + 1 < total) commit(B ^ 1);
