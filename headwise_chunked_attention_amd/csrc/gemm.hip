@@ -316,9 +316,21 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
   T* As = reinterpret_cast<T*>(smem);
   T* Bs = As + 2 * BM * SK;
 
+  // Consecutive blocks run on one XCD and share the operand of the slower
+  // index in its L2: the n tiles of one m tile share that A tile, or (when A
+  // is the smaller operand, M < N) the m tiles of one n tile share that B
+  // tile, so that the larger operand is streamed from HBM once.
   const int64_t ntn = p.N / BN;
-  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);  // n-tiles of one m-tile share an XCD's L2
-  const int64_t mtile = bid / ntn, ntile = bid % ntn;
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  int64_t mtile, ntile;
+  if (p.M < p.N) {
+    const int64_t mtn = gridDim.x / ntn;
+    mtile = bid % mtn;
+    ntile = bid / mtn;
+  } else {
+    mtile = bid / ntn;
+    ntile = bid % ntn;
+  }
   const int64_t m0 = mtile * BM, n0 = ntile * BN;
   int seg = 0;
   while (seg + 1 < p.nseg && n0 >= p.seg_end[seg]) ++seg;
@@ -615,12 +627,15 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   T* As = reinterpret_cast<T*>(smem);  // [2][BK tokens][BM]
   T* Bs = As + 2 * A_EL;               // [2][BK tokens][BN]
 
-  // 1-D grid: m-tile fastest, so the blocks that read the same head tile (B)
-  // are consecutive logical blocks and run on one XCD together.
+  // 1-D grid, consecutive logical blocks on one XCD: the faster tile index
+  // runs over the smaller operand, so the blocks that share a tile of the
+  // larger one (m tiles of one n tile when M <= N, else n tiles of one m
+  // tile) run together and it is streamed from HBM once.
   const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t gm = p.M / BM, gn = p.N / BN;
-  const int64_t m0 = (bid % gm) * BM;
-  const int64_t n0 = ((bid / gm) % gn) * BN;
+  const bool mfast = p.M <= p.N;
+  const int64_t m0 = (mfast ? bid % gm : (bid / gn) % gm) * BM;
+  const int64_t n0 = (mfast ? (bid / gm) % gn : bid % gn) * BN;
   const int64_t kb = (bid / (gm * gn)) * p.ksplit;
   const int64_t ke = (kb + p.ksplit < p.K) ? kb + p.ksplit : p.K;
 
