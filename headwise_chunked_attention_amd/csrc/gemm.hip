@@ -376,8 +376,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
 
   // Register-staged k tiles, NPF of them in flight: at step kt the tiles
   // kt+1 .. kt+NPF are loading into register slots while tile kt is in LDS.
-  // Two slots for the long-k (d_model) projection of bf16 rows, which waits
-  // on HBM; one elsewhere (the accumulating GEMM has only a few k tiles).
+  // Two slots for the bf16 products with long k (every epilogue but the
+  // accumulating one), which wait on HBM; one for the accumulating product
+  // (only a few k tiles) and for fp32.
   constexpr int NPF = (sizeof(T) == 2 && EPI != EPI_ACCUM) ? 2 : 1;
   constexpr int RA = BM * CPR / NTHREADS, RB = BN * CPR / NTHREADS;
   u32x4 ra[NPF][RA], rb[NPF][RB];
