@@ -183,6 +183,10 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   // bf16: lane offsets of the dO^T / Q^T column reads, computed once
   Col4Plan<L, ND> cplan;
   if constexpr (sizeof(T) == 2) cplan.init();
+  // the K and V fragments of the first d step stay in registers: the first
+  // MFMAs of a step then wait only for the Q and dO reads
+  const Frag<T> kb0 = ld_frag(Ks + L::idx(krel, 8 * h));
+  const Frag<T> vb0 = ld_frag(Vs + L::idx(krel, 8 * h));
   auto step = [&](auto bc, int64_t it) {
     constexpr int B = decltype(bc)::value;
     int nh_next = hh;
@@ -218,8 +222,8 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const Frag<T> kb = ld_frag(Ks + L::idx(krel, s * 16 + 8 * h));
-      const Frag<T> vb = ld_frag(Vs + L::idx(krel, s * 16 + 8 * h));
+      const Frag<T> kb = s == 0 ? kb0 : ld_frag(Ks + L::idx(krel, s * 16 + 8 * h));
+      const Frag<T> vb = s == 0 ? vb0 : ld_frag(Vs + L::idx(krel, s * 16 + 8 * h));
       mma(sacc, ld_frag(Qs + L::idx(qt * 32 + r, s * 16 + 8 * h)), kb);
       mma(dpacc, ld_frag(dOs + L::idx(qt * 32 + r, s * 16 + 8 * h)), vb);
     }
