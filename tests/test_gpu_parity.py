@@ -64,3 +64,18 @@ def test_bf16_llama_share_reduced_n(C):
 def test_bf16_qwen_share_reduced_n(C):
     """Qwen3-32B-shaped share (d_model 5120, 8 q / 1 kv, q/k RMSNorm, theta 1e6) at N=1536."""
     _run(Case(1536, 5120, 8, 1, 128, "bf16", theta=1e6, norm="random", seed=2), C)
+
+
+@pytest.mark.parametrize("C", [1, 2])
+def test_fp32_mha_group_of_one(C):
+    """Multi-head attention (as many kv heads as q heads: kv groups of one head),
+    so every chunk projects its own K/V and C kv heads sit side by side."""
+    _run(Case(600, 256, 4, 4, 64, "fp32", seed=11), C)
+
+
+@pytest.mark.parametrize("C", [1, 4])
+def test_bf16_group_of_two(C):
+    """kv groups of two q heads at head_dim 128: at C=1 a group spans two chunks
+    (K/V and their gradients stay resident between them); at C=4 one chunk holds
+    two groups. N not a multiple of any tile."""
+    _run(Case(900, 256, 4, 2, 128, "bf16", seed=12), C)
