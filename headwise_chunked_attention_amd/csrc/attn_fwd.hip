@@ -205,6 +205,19 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           f32x16& sacc = sacc2[kt];
+          // V^T fragments of the P V products below. The training forward
+          // reads the first two before its softmax, whose VALU work (row sums,
+          // base checks) then covers their latency
+          auto vfrag = [&](int t) {
+            const T* Vr = Vs + (kt * 32 + 16 * (t / ND)) * G::L::STRIDE;
+            return frag_from_col4<T>(ld_col4_at(Vr, vplan.off[0][t % ND]), ld_col4_at(Vr, vplan.off[1][t % ND]));
+          };
+          Frag<T> vf[3];
+          if constexpr (MODE == 0) {
+            vf[0] = vfrag(0);
+            vf[1] = vfrag(1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
           if (k0 + kt * 32 + 31 > q0w) {  // the half crosses this wave's diagonal
             const int qrel = (int)(q0w - k0) + r - kt * 32;  // query minus the half's first key
 #pragma unroll
@@ -277,14 +290,10 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
           }
           // O^T += V^T P^T over the half's keys (rows kt*32 + 16*s2 + ... of V):
           // 2*ND products t = (s2, j). In the recompute the V^T fragment of
-          // product t + 2 is read before product t issues (faster there,
-          // slower in the training forward, which keeps the compiler's order).
-          auto vfrag = [&](int t) {
-            const T* Vr = Vs + (kt * 32 + 16 * (t / ND)) * G::L::STRIDE;
-            return frag_from_col4<T>(ld_col4_at(Vr, vplan.off[0][t % ND]), ld_col4_at(Vr, vplan.off[1][t % ND]));
-          };
+          // product t + 2 is read before product t issues; the training
+          // forward, where that ring was slower, reads the rest in the
+          // compiler's order.
           if constexpr (MODE == 1) {
-            Frag<T> vf[3];
             vf[0] = vfrag(0);
             vf[1] = vfrag(1);
 #pragma unroll
@@ -295,7 +304,7 @@ __global__ __launch_bounds__((FwdGeo<T, D>::NTHREADS)) void attn_fwd_kernel(cons
             }
           } else {
 #pragma unroll
-            for (int t = 0; t < 2 * ND; ++t) mma(oacc[0][t % ND], vfrag(t), pf[t / ND]);
+            for (int t = 0; t < 2 * ND; ++t) mma(oacc[0][t % ND], t < 2 ? vf[t] : vfrag(t), pf[t / ND]);
           }
         }
       }
