@@ -227,6 +227,20 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       mma(sacc, ld_frag(Qs + L::idx(qt * 32 + r, s * 16 + 8 * h)), kb);
       mma(dpacc, ld_frag(dOs + L::idx(qt * 32 + r, s * 16 + 8 * h)), vb);
     }
+    // bf16: the first dO^T / Q^T fragment pair of the dV/dK products is read
+    // before the softmax, whose VALU work then covers its latency
+    Frag<T> ado[2], aq[2];
+    auto frags = [&](auto t, int i) {
+      // rows qt*32 + 16*s2 + ... of dO and Q at the precomputed lane offsets
+      const T* dOr = dOs + (qt * 32 + 16 * (t / ND)) * L::STRIDE;
+      const T* Qr = Qs + (qt * 32 + 16 * (t / ND)) * L::STRIDE;
+      ado[i] = frag_from_col4<T>(ld_col4_at(dOr, cplan.off[0][t % ND]), ld_col4_at(dOr, cplan.off[1][t % ND]));
+      aq[i] = frag_from_col4<T>(ld_col4_at(Qr, cplan.off[0][t % ND]), ld_col4_at(Qr, cplan.off[1][t % ND]));
+    };
+    if constexpr (sizeof(T) == 2) {
+      frags(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d), the same values the dQ
     // kernel forms
 #pragma unroll
@@ -245,15 +259,6 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       // t + 1 are read before pair t issues
       const Frag<T> pbf[2] = {frag_from_acc<T>(sacc, 0, 1.0f), frag_from_acc<T>(sacc, 1, 1.0f)};
       const Frag<T> sbf[2] = {frag_from_acc<T>(dpacc, 0, 1.0f), frag_from_acc<T>(dpacc, 1, 1.0f)};
-      Frag<T> ado[2], aq[2];
-      auto frags = [&](int t, int i) {
-        // rows qt*32 + 16*s2 + ... of dO and Q at the precomputed lane offsets
-        const T* dOr = dOs + (qt * 32 + 16 * (t / ND)) * L::STRIDE;
-        const T* Qr = Qs + (qt * 32 + 16 * (t / ND)) * L::STRIDE;
-        ado[i] = frag_from_col4<T>(ld_col4_at(dOr, cplan.off[0][t % ND]), ld_col4_at(dOr, cplan.off[1][t % ND]));
-        aq[i] = frag_from_col4<T>(ld_col4_at(Qr, cplan.off[0][t % ND]), ld_col4_at(Qr, cplan.off[1][t % ND]));
-      };
-      frags(0, 0);
 #pragma unroll
       for (int t = 0; t < 2 * ND; ++t) {
         if (t + 1 < 2 * ND) frags(t + 1, (t + 1) & 1);
@@ -473,6 +478,19 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
             mma(dpacc, vf[s & 1], df[s]);
           }
         }
+        // bf16: the first two K^T fragments of the dQ products are read
+        // before the softmax, whose VALU work then covers their latency
+        auto kfrag = [&](auto t) {
+          // rows kt*32 + 16*s2 + ... of K at the precomputed lane offsets
+          const T* Kr = Ks + (kt * 32 + 16 * (t / ND)) * L::STRIDE;
+          return frag_from_col4<T>(ld_col4_at(Kr, kplan.off[0][t % ND]), ld_col4_at(Kr, kplan.off[1][t % ND]));
+        };
+        Frag<T> kf3[3];
+        if constexpr (sizeof(T) == 2) {
+          kf3[0] = kfrag(0);
+          kf3[1] = kfrag(1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d) (log2 units and the
         // 1/sqrt(d) come with the pre-scaled q and dout)
 #pragma unroll
@@ -490,14 +508,6 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
         // product t + 2 before product t issues
         const Frag<T> sbf[2] = {frag_from_acc<T>(dpacc, 0, 1.0f), frag_from_acc<T>(dpacc, 1, 1.0f)};
         if constexpr (sizeof(T) == 2) {
-          auto kfrag = [&](int t) {
-            // rows kt*32 + 16*s2 + ... of K at the precomputed lane offsets
-            const T* Kr = Ks + (kt * 32 + 16 * (t / ND)) * L::STRIDE;
-            return frag_from_col4<T>(ld_col4_at(Kr, kplan.off[0][t % ND]), ld_col4_at(Kr, kplan.off[1][t % ND]));
-          };
-          Frag<T> kf3[3];
-          kf3[0] = kfrag(0);
-          kf3[1] = kfrag(1);
 #pragma unroll
           for (int t = 0; t < 2 * ND; ++t) {
             if (t + 2 < 2 * ND) kf3[(t + 2) % 3] = kfrag(t + 2);
