@@ -44,7 +44,7 @@ KERNEL_NAMES = {"attn_fwd": "attn_fwd_kernel<bf16,128,0>", "attn_recompute": "at
 # HBM bytes per launch of a kernel from rocprofv3 counters (FETCH_SIZE +
 # WRITE_SIZE, scaled by a plain copy of known size), measured on the kernel as
 # it now stands; absent (null) until measured again after a kernel change.
-TRAFFIC_BYTES = {"attn_bwd_dkdv": 5.193e9}  # fetch 5.059 GB + write 0.134 GB
+TRAFFIC_BYTES = {"attn_bwd_dkdv": 4.239e9}  # fetch 4.105 GB + write 0.134 GB
 
 
 def model_flops(N, D, hq, hkv, d):

@@ -227,8 +227,8 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       mma(sacc, ld_frag(Qs + L::idx(qt * 32 + r, s * 16 + 8 * h)), kb);
       mma(dpacc, ld_frag(dOs + L::idx(qt * 32 + r, s * 16 + 8 * h)), vb);
     }
-    // bf16: the first dO^T / Q^T fragment pair of the dV/dK products is read
-    // before the softmax, whose VALU work then covers its latency
+    // bf16: the dO^T / Q^T fragment pairs of the first two dV/dK products are
+    // read before the softmax, whose VALU work then covers their latency
     Frag<T> ado[2], aq[2];
     auto frags = [&](auto t, int i) {
       // rows qt*32 + 16*s2 + ... of dO and Q at the precomputed lane offsets
@@ -239,6 +239,7 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     };
     if constexpr (sizeof(T) == 2) {
       frags(0, 0);
+      frags(1, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d), the same values the dQ
@@ -255,13 +256,14 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     for (int e = 0; e < 16; ++e) dpacc[e] = sacc[e] * dpacc[e];
     // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries.
     if constexpr (sizeof(T) == 2) {
-      // 2*ND product pairs t = (s2, j); the dO^T and Q^T fragments of pair
-      // t + 1 are read before pair t issues
+      // 2*ND product pairs t = (s2, j); pairs 0 and 1 have their fragments
+      // already, and from pair 1 on the fragments of pair t + 1 are read
+      // before pair t issues
       const Frag<T> pbf[2] = {frag_from_acc<T>(sacc, 0, 1.0f), frag_from_acc<T>(sacc, 1, 1.0f)};
       const Frag<T> sbf[2] = {frag_from_acc<T>(dpacc, 0, 1.0f), frag_from_acc<T>(dpacc, 1, 1.0f)};
 #pragma unroll
       for (int t = 0; t < 2 * ND; ++t) {
-        if (t + 1 < 2 * ND) frags(t + 1, (t + 1) & 1);
+        if (t >= 1 && t + 1 < 2 * ND) frags(t + 1, (t + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
         mma(dv[t % ND], ado[t & 1], pbf[t / ND]);
         mma(dk[t % ND], aq[t & 1], sbf[t / ND]);
@@ -478,7 +480,7 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
             mma(dpacc, vf[s & 1], df[s]);
           }
         }
-        // bf16: the first two K^T fragments of the dQ products are read
+        // bf16: the K^T fragments of the first three dQ products are read
         // before the softmax, whose VALU work then covers their latency
         auto kfrag = [&](auto t) {
           // rows kt*32 + 16*s2 + ... of K at the precomputed lane offsets
@@ -489,6 +491,7 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
         if constexpr (sizeof(T) == 2) {
           kf3[0] = kfrag(0);
           kf3[1] = kfrag(1);
+          kf3[2] = kfrag(2);
           __builtin_amdgcn_sched_barrier(0);
         }
         // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d) (log2 units and the
@@ -504,13 +507,14 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
 #pragma unroll
         for (int e = 0; e < 16; ++e) dpacc[e] = sacc[e] * dpacc[e];
         // dQ^T += K^T dS^T (contraction over the half's keys = accumulator
-        // rows): 2*ND products t = (s2, j); bf16 reads the K^T fragment of
-        // product t + 2 before product t issues
+        // rows): 2*ND products t = (s2, j); bf16 has the fragments of products
+        // 0-2 already and from product 1 on reads the K^T fragment of product
+        // t + 2 before product t issues
         const Frag<T> sbf[2] = {frag_from_acc<T>(dpacc, 0, 1.0f), frag_from_acc<T>(dpacc, 1, 1.0f)};
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int t = 0; t < 2 * ND; ++t) {
-            if (t + 2 < 2 * ND) kf3[(t + 2) % 3] = kfrag(t + 2);
+            if (t >= 1 && t + 2 < 2 * ND) kf3[(t + 2) % 3] = kfrag(t + 2);
             __builtin_amdgcn_sched_barrier(0);
             mma(dq[t % ND], kf3[t % 3], sbf[t / ND]);
           }
