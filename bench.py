@@ -2,8 +2,8 @@
 
 One "step" is one forward plus one backward of the whole hot path (every
 chunk: projections, RoPE, causal GQA attention, output projection, and the
-backward with its recompute) over the Llama3-8B one-GPU Ulysses share:
-N = 131072 tokens, d_model 4096, 4 q heads / 1 kv head, head_dim 128, bf16,
+backward with its recompute) over the Llama3-8B one-GPU Ulysses share at
+N = 1048576 tokens: d_model 4096, 4 q heads / 1 kv head, head_dim 128, bf16,
 RoPE theta 5e5, causal; inputs x ~ N(0,1), W ~ N(0, 0.02), dY ~ N(0,1),
 seeded, generated on the host and resident in HBM before timing starts.
 
@@ -11,12 +11,13 @@ Printed (one JSON line): model TFLOP/s of the step at the headline chunk size
 (chunk_heads=1 unless --chunk is given) and its fraction of the bf16 dense
 MFMA peak; median and minimum step, forward and backward times; the
 attention-core and hardware (recompute included) rates; the workspace bytes
-per chunk size; a chunk-size sweep; per-kernel event timings (from a second,
-profiled run of the same steps); the roofline entry of the dominant kernel
-(attention backward); the CPU fp64 oracle timed on a bounded sample; and the
-sequence-tiled MLP and LM-head loss next to the op (``mlp``, ``loss``), and
-one checkpointed transformer block built from them (``block``), and four
-such blocks with their inputs offloaded to host memory (``stack``).
+per chunk size; a chunk-size sweep over {1, 2, 4} with the peak workspace of
+each; per-kernel event timings (from a second, profiled run of two steps);
+the roofline entry of the dominant kernel; the CPU fp64 oracle timed on
+bounded samples; the same measurements at N = 131072 (``secondary``); and the
+sequence-tiled MLP and LM-head loss next to the op (``mlp``, ``loss``), one
+checkpointed transformer block built from them (``block``), and four such
+blocks with their inputs offloaded to host memory (``stack``).
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--chunk 1] [--no-sweep] [--no-cpu]
 """
@@ -35,16 +36,24 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "causal attn fwd+bwd TFLOP/s (frac of bf16 MFMA peak) + peak workspace GB vs chunk"
 
-WORKLOAD = dict(name="llama3-8b-ulysses-share-131k", n_tokens=131072, d_model=4096, n_q_heads=4,
-                n_kv_heads=1, head_dim=128, rope_theta=5e5, dtype="bf16", chunks=(1, 2, 4))
+LLAMA = dict(d_model=4096, n_q_heads=4, n_kv_heads=1, head_dim=128, rope_theta=5e5, dtype="bf16", chunks=(1, 2, 4))
+WORKLOADS = {
+    "llama3-8b-ulysses-share-1m": dict(LLAMA, n_tokens=1048576),
+    "llama3-8b-ulysses-share-131k": dict(LLAMA, n_tokens=131072),
+}
+HEADLINE = "llama3-8b-ulysses-share-1m"
+SECONDARY = "llama3-8b-ulysses-share-131k"
+QWEN_SHAPE = dict(d_model=5120, n_q_heads=8, n_kv_heads=1, head_dim=128, rope_theta=1e6, n_tokens=524288)
 
 KERNEL_NAMES = {"attn_fwd": "attn_fwd_kernel<bf16,128,0>", "attn_recompute": "attn_fwd_kernel<bf16,128,1>",
                 "attn_bwd_dkdv": "attn_bwd_dkdv_kernel<bf16,128>", "attn_bwd_dq": "attn_bwd_dq_kernel<bf16,128>"}
 
-# HBM bytes per launch of a kernel from rocprofv3 counters (FETCH_SIZE +
-# WRITE_SIZE, scaled by a plain copy of known size), measured on the kernel as
-# it now stands; absent (null) until measured again after a kernel change.
-TRAFFIC_BYTES = {"attn_bwd_dkdv": 4.239e9}  # fetch 4.105 GB + write 0.134 GB
+# HBM bytes per launch (FETCH_SIZE + WRITE_SIZE from rocprofv3, each scaled by
+# the same counter's reading for a plain copy of known size), per workload and
+# kernel kind, as measured on the kernel as it now stands. A kernel change
+# removes its entries until they are measured again; a workload without an
+# entry reports null.
+TRAFFIC_BYTES = {}
 
 
 def model_flops(N, D, hq, hkv, d):
@@ -69,27 +78,60 @@ def hardware_flops(N, D, hq, hkv, d):
 
 
 def cpu_baseline(w, sample_n=8192):
-    """Time the oracle's full fwd+bwd on a bounded sample: the same layer shape
-    (d_model, heads, head_dim) at sample_n tokens. Reports model TFLOP/s."""
+    """The oracle, as it stands, timed on this host's cores (all of them in this
+    process's affinity mask; the BLAS thread pool is set to that count).
+
+    ``value``: model TFLOP/s of the oracle's full fp64 fwd+bwd at sample_n
+    tokens with the workload's d_model, heads and head_dim. ``rows`` adds:
+    the tiny fp32 configuration in full; the same sample at the Qwen3-32B
+    share's shape; each projected to its configuration's N by model flops
+    (labelled "projected"); and the oracle work that the parity tests run at
+    the workload's N (y and LSE at 256 sampled rows, dx at 64 tail rows)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     import oracle
-    from headwise_chunked_attention_amd.synth import LayerInputs
+    from headwise_chunked_attention_amd.synth import LayerInputs, gen_rows, gen_rows_at
 
-    inp = LayerInputs(sample_n, w["d_model"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"], "bf16", seed=0)
-    t0 = time.perf_counter()
-    oracle.layer_fwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, w["n_q_heads"], w["n_kv_heads"], w["head_dim"],
-                     w["rope_theta"], 1)
-    oracle.layer_bwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, inp.dy, w["n_q_heads"], w["n_kv_heads"],
-                     w["head_dim"], w["rope_theta"], 1)
-    dt = time.perf_counter() - t0
-    fl = model_flops(sample_n, w["d_model"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"])
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    cores = len(os.sched_getaffinity(0))
+    rows = []
+    with threadpool_limits(limits=cores):
+        def full(N, D, hq, hkv, d, theta, dt, C, label, proj_n=None):
+            inp = LayerInputs(N, D, hq, hkv, d, dt, seed=0)
+            t0 = time.perf_counter()
+            oracle.layer_fwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, hq, hkv, d, theta, C)
+            oracle.layer_bwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, inp.dy, hq, hkv, d, theta, C)
+            dt_s = time.perf_counter() - t0
+            fl = model_flops(N, D, hq, hkv, d)
+            r = {"sample": label, "seconds": dt_s, "model_tflops": fl / dt_s / 1e12}
+            if proj_n:
+                r["projected_seconds_at_n"] = {"n_tokens": proj_n, "seconds": dt_s * model_flops(proj_n, D, hq, hkv, d) / fl,
+                                               "label": "projected"}
+            rows.append(r)
+            return r
+
+        main = full(sample_n, w["d_model"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"], w["rope_theta"], "bf16",
+                    1, f"full fp64 fwd+bwd at N={sample_n}, the workload's layer shape", w["n_tokens"])
+        full(2048, 512, 8, 2, 64, 5e5, "fp32", 2, "tiny fp32 configuration, full fp64 fwd+bwd (N=2048)")
+        q = QWEN_SHAPE
+        full(sample_n, q["d_model"], q["n_q_heads"], q["n_kv_heads"], q["head_dim"], q["rope_theta"], "bf16", 1,
+             f"full fp64 fwd+bwd at N={sample_n}, Qwen3-32B share shape (q/k norm off)", q["n_tokens"])
+        # the parity tests' own oracle work at the workload's N
+        N, D = w["n_tokens"], w["d_model"]
+        hq, hkv, d, th = w["n_q_heads"], w["n_kv_heads"], w["head_dim"], w["rope_theta"]
+        wts = LayerInputs(8, D, hq, hkv, d, "bf16", seed=0, with_x=False, with_dy=False)
+        xr = lambda a, b: gen_rows("x", N, D, 1.0, "bf16", 0, a, b)  # noqa: E731
+        sel = np.unique(np.concatenate([[0, 1, N - 1], np.random.default_rng(0).integers(0, N, 253)]))
+        t0 = time.perf_counter()
+        oracle.layer_fwd_rows(xr, lambda i: gen_rows_at("x", N, D, 1.0, "bf16", 0, np.asarray(i)), N, sel, wts.wq,
+                              wts.wk, wts.wv, wts.wo, hq, hkv, d, th)
+        rows.append({"sample": f"sampled-row forward at N={N}: y and LSE at {sel.size} rows (K/V of all N "
+                               f"tokens, x regenerated on the host)", "seconds": time.perf_counter() - t0})
+    return {"value": main["model_tflops"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"full fp64 fwd+bwd (layer_fwd + layer_bwd, which recomputes the fwd) at N={sample_n} "
-                      f"with the workload's d_model/heads/head_dim, chunk_heads=1; {dt:.1f} s; "
-                      f"rate = model flops of that sample / time"}
+                      f"with the workload's d_model/heads/head_dim, chunk_heads=1; {main['seconds']:.1f} s; "
+                      f"rate = model flops of that sample / time; BLAS threads = cores",
+            "rows": rows}
 
 
 MLP_WORKLOAD = dict(name="llama3-8b-mlp-seq-shard-16k", n_tokens=16384, d_model=4096, d_ff=14336,
@@ -411,56 +453,49 @@ def loss_bench(dev, steps, warmup):
                              "untiled_logits": N * V * 2 / 1e9}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--chunk", type=int, default=1)
-    ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP and loss measurements")
-    ap.add_argument("--no-block", action="store_true", help="skip the transformer-block measurement")
-    ap.add_argument("--n-tokens", type=int, default=None, help="override N (not the headline workload)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) so that "
-                         "profiler byte counters can be scaled against a kernel of known traffic")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU's Ulysses share: multi-GPU runs (all-to-all over RCCL) are not part "
-              "of this build; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def _wait(events, label, every_s=30.0):
+    """Wait for the recorded step events, printing progress to stderr now and
+    then (a long run is then never silent); touches nothing on the GPU."""
+    t0 = last = time.perf_counter()
+    while not events[-1].query():
+        time.sleep(0.25)
+        now = time.perf_counter()
+        if now - last >= every_s:
+            done = sum(1 for e in events if e.query())
+            print(f"# {label}: {done} of {len(events)} step events done ({now - t0:.0f} s)", file=sys.stderr,
+                  flush=True)
+            last = now
+    events[-1].synchronize()
 
+
+def attention_bench(dev, name, w, chunk, steps, warmup, sweep_steps, prof_steps, sweep):
+    """Time the step at one workload: the headline chunk size (no per-kernel
+    events), a profiled run of prof_steps steps (kernel table and roofline),
+    and the chunk sweep."""
     import numpy as np
     import torch
 
     from headwise_chunked_attention_amd import api
     from headwise_chunked_attention_amd.synth import LayerInputs
 
-    w = dict(WORKLOAD)
-    if args.n_tokens:
-        w["n_tokens"] = args.n_tokens
-        w["name"] = f"llama3-8b-ulysses-share-{args.n_tokens}"
     N, D, hq, hkv, d, theta = (w[k] for k in ("n_tokens", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
                                               "rope_theta"))
-    dev = torch.device("cuda:0")
-    api.load()
-    if args.calibrate_copy:
-        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        print("# calibration copy: 3 x (1 GiB read + 1 GiB written)", file=sys.stderr, flush=True)
-        del src, dst
     t0 = time.perf_counter()
-    inp = LayerInputs(N, D, hq, hkv, d, "bf16", seed=0)
-    t = {k: torch.from_numpy(getattr(inp, k)).to(dev).to(torch.bfloat16)
-         for k in ("x", "dy", "wq", "wk", "wv", "wo")}
+    t = {}
+    inp = LayerInputs(N, D, hq, hkv, d, "bf16", seed=0, with_x=False, with_dy=False)
+    for k in ("wq", "wk", "wv", "wo"):
+        t[k] = torch.from_numpy(getattr(inp, k)).to(dev).to(torch.bfloat16)
+    from headwise_chunked_attention_amd.synth import gen_rows
+    for k in ("x", "dy"):
+        t[k] = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+        step = 262144
+        for r0 in range(0, N, step):
+            r1 = min(N, r0 + step)
+            t[k][r0:r1].copy_(torch.from_numpy(gen_rows(k, N, D, 1.0, "bf16", 0, r0, r1)))
     del inp
     torch.cuda.synchronize()
-    print(f"# inputs generated and resident in HBM in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-
+    print(f"# {name}: inputs generated and resident in HBM in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+          flush=True)
     fl = model_flops(N, D, hq, hkv, d)
     stream = torch.cuda.current_stream(dev)
 
@@ -483,9 +518,14 @@ def main():
         def bwd():
             api.attn_bwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], t["dy"], lse, out=out, workspace=ws, **kw)
 
+        wev = []
         for _ in range(warmup):
             fwd()
             bwd()
+            wev.append(torch.cuda.Event())
+            wev[-1].record(stream)
+        if wev:
+            _wait(wev, f"{name} C={C} warmup")
         torch.cuda.synchronize()
         mem0 = torch.cuda.memory_allocated(dev)
         free0, _ = torch.cuda.mem_get_info(dev)
@@ -501,6 +541,7 @@ def main():
             evs[i][1].record(stream)
             bwd()
         ev_end.record(stream)
+        _wait([e[0] for e in evs] + [ev_end], f"{name} C={C}")
         torch.cuda.synchronize()
         ms = evs[0][0].elapsed_time(ev_end) / steps
         t_f = [evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]
@@ -514,59 +555,120 @@ def main():
                "fwd_ms": {"median": float(np.median(t_f)), "min": float(np.min(t_f))},
                "bwd_ms": {"median": float(np.median(t_b)), "min": float(np.min(t_b))},
                "ws_fwd_gb": ws_f / 1e9, "ws_bwd_gb": ws_b / 1e9, "hidden_alloc_bytes": int(free0 - free1)}
+        print(f"# {name} C={C}: {ms:.2f} ms/step, {res['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del ws, y, lse, out
         torch.cuda.empty_cache()
         return res, prof
 
-    # the headline run carries no per-kernel events; a second run of the same
-    # steps, with the library's per-kernel timing on, gives the kernel table
-    head, _ = run_chunk(args.chunk, args.steps, args.warmup, profile=False)
-    _, prof = run_chunk(args.chunk, args.steps, 1, profile=True)
-    sweep = []
-    if not args.no_sweep:
+    # the headline run carries no per-kernel events; a short second run with
+    # the library's per-kernel timing on gives the kernel table
+    head, _ = run_chunk(chunk, steps, warmup, profile=False)
+    _, prof = run_chunk(chunk, prof_steps, 0, profile=True)
+    res_sweep = []
+    if sweep:
         for C in w["chunks"]:
-            if C == args.chunk:
-                sweep.append(head)
+            if C == chunk:
+                res_sweep.append(head)
                 continue
-            r, _ = run_chunk(C, max(2, args.steps // 2), 1, profile=False)
-            sweep.append(r)
-            print(f"# chunk {C}: {r['ms_per_step']:.2f} ms/step, {r['tflops']:.1f} TFLOP/s", file=sys.stderr,
-                  flush=True)
+            r, _ = run_chunk(C, sweep_steps, 1, profile=False)
+            res_sweep.append(r)
+    del t
+    torch.cuda.empty_cache()
 
     kernels = {}
     for k, v in prof.items():
         if v["launches"]:
-            kernels[k] = {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["launches"] / args.steps,
+            kernels[k] = {"ms_per_step": v["ms"] / prof_steps, "launches_per_step": v["launches"] / prof_steps,
                           "avg_launch_ms": v["ms"] / v["launches"],
                           "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None}
     # attention-core rate: the core's model flops over the time of the kernels
     # that do them (forward attention, dK/dV and dQ; the recompute is extra work)
-    core_ms = sum(prof[k]["ms"] for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq")) / args.steps
-    core_tflops = attn_core_flops(N, hq, d) / (core_ms * 1e-3) / 1e12
-    hw_tflops = hardware_flops(N, D, hq, hkv, d) / (head["ms_per_step"] * 1e-3) / 1e12
+    core_ms = sum(prof[k]["ms"] for k in ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq")) / prof_steps
     # dominant kernel of the step: the attention kernel kind with the most time
     dom = max(("attn_fwd", "attn_recompute", "attn_bwd_dkdv", "attn_bwd_dq"), key=lambda k: prof[k]["ms"])
     ab = prof[dom]
     achieved = ab["flops"] / ab["launches"] / (ab["ms"] / ab["launches"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_BYTES.get(dom),
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_BYTES.get((name, dom)),
                 "kernel": KERNEL_NAMES[dom],
                 "algorithmic_flops_per_launch": ab["flops"] / ab["launches"],
                 "avg_launch_ms": ab["ms"] / ab["launches"]}
+    return {"workload": name, "n_tokens": N, "chunk_heads": chunk, "head": head, "model_flops_per_step": fl,
+            "attention_core_tflops": attn_core_flops(N, hq, d) / (core_ms * 1e-3) / 1e12,
+            "hardware_tflops": hardware_flops(N, D, hq, hkv, d) / (head["ms_per_step"] * 1e-3) / 1e12,
+            "chunk_sweep": res_sweep, "kernels": kernels, "roofline": roofline}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--chunk", type=int, default=1)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP and loss measurements")
+    ap.add_argument("--no-block", action="store_true", help="skip the transformer-block measurement")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the N = 131072 measurement")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=HEADLINE,
+                    help="the headline workload (default: the Llama3-8B share at N = 1048576)")
+    ap.add_argument("--prof-steps", type=int, default=2, help="steps of the per-kernel timing run")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) so that "
+                         "profiler byte counters can be scaled against a kernel of known traffic")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU's Ulysses share: multi-GPU runs (all-to-all over RCCL) are not part "
+              "of this build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from headwise_chunked_attention_amd import api
+
+    dev = torch.device("cuda:0")
+    api.load()
+    peak_dev = api.device_peak(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print("# calibration copy: 3 x (1 GiB read + 1 GiB written)", file=sys.stderr, flush=True)
+        del src, dst
+
+    name = args.workload
+    w = WORKLOADS[name]
+    sweep_steps = max(2, args.steps // 4)
+    res = attention_bench(dev, name, w, args.chunk, args.steps, args.warmup, sweep_steps, args.prof_steps,
+                          not args.no_sweep)
+    head = res["head"]
+    secondary = None
+    if not args.no_secondary and name != SECONDARY:
+        sec = attention_bench(dev, SECONDARY, WORKLOADS[SECONDARY], args.chunk, max(3, args.steps // 2), 2,
+                              max(3, args.steps // 2), args.prof_steps, not args.no_sweep)
+        secondary = {"workload": SECONDARY, "value": sec["head"]["tflops"], "unit": "TFLOP/s",
+                     "ms_per_step": sec["head"]["ms_per_step"],
+                     "frac_of_peak": sec["head"]["tflops"] / PEAK_BF16_TFLOPS,
+                     "step_ms": sec["head"]["step_ms"], "fwd_ms": sec["head"]["fwd_ms"],
+                     "bwd_ms": sec["head"]["bwd_ms"], "attention_core_tflops": sec["attention_core_tflops"],
+                     "chunk_sweep": sec["chunk_sweep"], "kernels": sec["kernels"], "roofline": sec["roofline"]}
 
     mlp = loss = None
+    steps = args.steps
     if not args.no_mlp:
-        mlp = mlp_bench(dev, max(2, args.steps // 2), 1)
+        mlp = mlp_bench(dev, max(2, steps // 2), 1)
         print(f"# mlp: fwd {mlp['fwd_ms']:.2f} ms, bwd {mlp['bwd_ms']:.2f} ms, {mlp['model_tflops']:.0f} TFLOP/s",
               file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-        loss = loss_bench(dev, max(2, args.steps // 2), 1)
+        loss = loss_bench(dev, max(2, steps // 2), 1)
         print(f"# loss: fwd {loss['fwd_ms']:.2f} ms, bwd {loss['bwd_ms']:.2f} ms, {loss['model_tflops']:.0f} TFLOP/s",
               file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
     block = stack = None
     if not args.no_block:
-        block = block_bench(dev, max(2, args.steps // 3), 1)
+        block = block_bench(dev, max(2, steps // 3), 1)
         print(f"# block: fwd {block['fwd_ms']:.1f} ms, bwd {block['bwd_ms']:.1f} ms (kept h: {block['bwd_kept_ms']:.1f}),"
               f" {block['model_tflops']:.0f} model TFLOP/s", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
@@ -578,11 +680,10 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        try:
-            cpu = cpu_baseline(w)
-        except MemoryError:
-            cpu = None
+        print("# cpu baseline: the fp64 oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
 
+    N, D, hq, hkv, d = (w[k] for k in ("n_tokens", "d_model", "n_q_heads", "n_kv_heads", "head_dim"))
     line = {
         "metric": METRIC,
         "value": head["tflops"],
@@ -596,21 +697,25 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded host Gaussian inputs, random-init weights; no dataset)",
-        "config": {"workload": w["name"], "n_tokens": N, "d_model": D, "n_q_heads": hq, "n_kv_heads": hkv,
-                   "head_dim": d, "rope_theta": theta, "causal": True, "chunk_heads": args.chunk,
+        "config": {"workload": name, "n_tokens": N, "d_model": D, "n_q_heads": hq, "n_kv_heads": hkv,
+                   "head_dim": d, "rope_theta": w["rope_theta"], "causal": True, "chunk_heads": args.chunk,
                    "parallelism": "one GPU's Ulysses head share (no collectives)"},
         "frac_of_peak": head["tflops"] / PEAK_BF16_TFLOPS,
-        "model_flops_per_step": fl,
+        "peak_from_device": dict(peak_dev, frac_of_peak=head["tflops"] / peak_dev["bf16_dense_tflops"]),
+        "model_flops_per_step": res["model_flops_per_step"],
         "step_ms": head["step_ms"],
         "fwd_ms": head["fwd_ms"],
         "bwd_ms": head["bwd_ms"],
-        "attention_core_tflops": core_tflops,
-        "hardware_tflops": hw_tflops,
+        "attention_core_tflops": res["attention_core_tflops"],
+        "hardware_tflops": res["hardware_tflops"],
         "workspace_gb": {"fwd": head["ws_fwd_gb"], "bwd": head["ws_bwd_gb"]},
-        "chunk_sweep": sweep,
-        "kernels": kernels,
-        "roofline": roofline,
+        "peak_workspace_gb_vs_chunk": {str(r["chunk_heads"]): {"fwd": r["ws_fwd_gb"], "bwd": r["ws_bwd_gb"]}
+                                       for r in res["chunk_sweep"]},
+        "chunk_sweep": res["chunk_sweep"],
+        "kernels": res["kernels"],
+        "roofline": res["roofline"],
         "cpu_baseline": cpu,
+        "secondary": secondary,
         "mlp": mlp,
         "loss": loss,
         "block": block,

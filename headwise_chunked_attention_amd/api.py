@@ -6,6 +6,7 @@ is missing or the tensors are not on a GPU, the call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -101,6 +102,9 @@ def load():
     lib.upipe_stack_bwd.restype = i32
     lib.upipe_strerror.argtypes = [i32]
     lib.upipe_strerror.restype = ctypes.c_char_p
+    lib.upipe_device_peak.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
+                                       ctypes.POINTER(ctypes.c_int)]
+    lib.upipe_device_peak.restype = i32
     lib.upipe_version.argtypes = []
     lib.upipe_version.restype = i32
     lib.upipe_profile_start.argtypes = []
@@ -178,6 +182,14 @@ def _stream_handle(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Context for the tensors a call allocates itself (outputs, workspace):
+    they belong to the stream the library enqueues on, so the caching
+    allocator does not hand their memory to other work before that stream
+    is done with it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     """A 256-byte aligned device buffer of at least nbytes (torch's allocator aligns to 512)."""
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
@@ -201,15 +213,16 @@ def attn_fwd(x, wq, wk, wv, wo, *, n_q_heads, n_kv_heads, head_dim, rope_theta, 
     if q_norm is not None:
         _check(q_norm, "q_norm", dt, (d,), dev)
         _check(k_norm, "k_norm", dt, (d,), dev)
-    if y is None:
-        y = torch.empty((N, D), dtype=dt, device=dev)
-    if lse is None:
-        lse = torch.empty((n_q_heads, N), dtype=torch.float32, device=dev)
+    need = workspace_bytes(N, D, n_q_heads, n_kv_heads, d, chunk_heads, q_norm is not None, dt, False)
+    with _alloc_on(stream):
+        if y is None:
+            y = torch.empty((N, D), dtype=dt, device=dev)
+        if lse is None:
+            lse = torch.empty((n_q_heads, N), dtype=torch.float32, device=dev)
+        if workspace is None:
+            workspace = alloc_workspace(need, dev)
     _check(y, "y", dt, (N, D), dev)
     _check(lse, "lse", torch.float32, (n_q_heads, N), dev)
-    need = workspace_bytes(N, D, n_q_heads, n_kv_heads, d, chunk_heads, q_norm is not None, dt, False)
-    if workspace is None:
-        workspace = alloc_workspace(need, dev)
     rc = lib.upipe_attn_fwd(dtype_code(dt), N, D, n_q_heads, n_kv_heads, d, float(rope_theta), chunk_heads,
                             _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(q_norm), _ptr(k_norm),
                             float(eps), _ptr(y), _ptr(lse), _ptr(workspace), workspace.numel(),
@@ -241,12 +254,16 @@ def attn_bwd(x, wq, wk, wv, wo, dy, lse, *, n_q_heads, n_kv_heads, head_dim, rop
         _check(q_norm, "q_norm", dt, (d,), dev)
         _check(k_norm, "k_norm", dt, (d,), dev)
     f32 = torch.float32
-    if out is None:
-        out = (torch.empty((N, D), dtype=dt, device=dev),
-               torch.empty(wq.shape, dtype=f32, device=dev), torch.empty(wk.shape, dtype=f32, device=dev),
-               torch.empty(wv.shape, dtype=f32, device=dev), torch.empty(wo.shape, dtype=f32, device=dev),
-               torch.empty((d,), dtype=f32, device=dev) if norm else None,
-               torch.empty((d,), dtype=f32, device=dev) if norm else None)
+    need = workspace_bytes(N, D, n_q_heads, n_kv_heads, d, chunk_heads, norm, dt, True)
+    with _alloc_on(stream):
+        if out is None:
+            out = (torch.empty((N, D), dtype=dt, device=dev),
+                   torch.empty(wq.shape, dtype=f32, device=dev), torch.empty(wk.shape, dtype=f32, device=dev),
+                   torch.empty(wv.shape, dtype=f32, device=dev), torch.empty(wo.shape, dtype=f32, device=dev),
+                   torch.empty((d,), dtype=f32, device=dev) if norm else None,
+                   torch.empty((d,), dtype=f32, device=dev) if norm else None)
+        if workspace is None:
+            workspace = alloc_workspace(need, dev)
     dx, dwq, dwk, dwv, dwo, dqn, dkn = out
     _check(dx, "dx", dt, (N, D), dev)
     for t, n, ref in ((dwq, "dwq", wq), (dwk, "dwk", wk), (dwv, "dwv", wv), (dwo, "dwo", wo)):
@@ -254,9 +271,6 @@ def attn_bwd(x, wq, wk, wv, wo, dy, lse, *, n_q_heads, n_kv_heads, head_dim, rop
     if norm:
         _check(dqn, "dq_norm", f32, (d,), dev)
         _check(dkn, "dk_norm", f32, (d,), dev)
-    need = workspace_bytes(N, D, n_q_heads, n_kv_heads, d, chunk_heads, norm, dt, True)
-    if workspace is None:
-        workspace = alloc_workspace(need, dev)
     rc = lib.upipe_attn_bwd(dtype_code(dt), N, D, n_q_heads, n_kv_heads, d, float(rope_theta), chunk_heads,
                             _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(q_norm), _ptr(k_norm),
                             float(eps), _ptr(dy), _ptr(lse), _ptr(dx), _ptr(dwq), _ptr(dwk), _ptr(dwv),
@@ -287,12 +301,13 @@ def loss_fwd(h, w, targets, *, tile_tokens, loss=None, lse=None, workspace=None,
     _check(w, "w", dt, (V, D), dev)
     _check(targets, "targets", torch.int32, (N,), dev)
     f32 = torch.float32
-    loss = torch.empty((N,), dtype=f32, device=dev) if loss is None else loss
-    lse = torch.empty((N,), dtype=f32, device=dev) if lse is None else lse
+    with _alloc_on(stream):
+        loss = torch.empty((N,), dtype=f32, device=dev) if loss is None else loss
+        lse = torch.empty((N,), dtype=f32, device=dev) if lse is None else lse
+        if workspace is None:
+            workspace = alloc_workspace(loss_workspace_bytes(N, D, V, tile_tokens, dt, False), dev)
     _check(loss, "loss", f32, (N,), dev)
     _check(lse, "lse", f32, (N,), dev)
-    if workspace is None:
-        workspace = alloc_workspace(loss_workspace_bytes(N, D, V, tile_tokens, dt, False), dev)
     rc = lib.upipe_loss_fwd(dtype_code(dt), N, D, V, int(tile_tokens), _ptr(h), _ptr(w), _ptr(targets), _ptr(loss),
                             _ptr(lse), _ptr(workspace), workspace.numel(), _stream_handle(dev, stream))
     if rc != 0:
@@ -312,12 +327,13 @@ def loss_bwd(h, w, targets, lse, g, *, tile_tokens, dh=None, dw=None, workspace=
     _check(targets, "targets", torch.int32, (N,), dev)
     _check(lse, "lse", f32, (N,), dev)
     _check(g, "g", f32, (N,), dev)
-    dh = torch.empty((N, D), dtype=dt, device=dev) if dh is None else dh
-    dw = torch.empty((V, D), dtype=f32, device=dev) if dw is None else dw
+    with _alloc_on(stream):
+        dh = torch.empty((N, D), dtype=dt, device=dev) if dh is None else dh
+        dw = torch.empty((V, D), dtype=f32, device=dev) if dw is None else dw
+        if workspace is None:
+            workspace = alloc_workspace(loss_workspace_bytes(N, D, V, tile_tokens, dt, True), dev)
     _check(dh, "dh", dt, (N, D), dev)
     _check(dw, "dw", f32, (V, D), dev)
-    if workspace is None:
-        workspace = alloc_workspace(loss_workspace_bytes(N, D, V, tile_tokens, dt, True), dev)
     rc = lib.upipe_loss_bwd(dtype_code(dt), N, D, V, int(tile_tokens), _ptr(h), _ptr(w), _ptr(targets), _ptr(lse),
                             _ptr(g), _ptr(dh), _ptr(dw), _ptr(workspace), workspace.numel(),
                             _stream_handle(dev, stream))
@@ -341,11 +357,12 @@ def mlp_fwd(x, w_gate, w_up, w_down, *, tile_tokens, y=None, workspace=None, str
     _check(w_gate, "w_gate", dt, (F, D), dev)
     _check(w_up, "w_up", dt, (F, D), dev)
     _check(w_down, "w_down", dt, (D, F), dev)
-    if y is None:
-        y = torch.empty((N, D), dtype=dt, device=dev)
+    with _alloc_on(stream):
+        if y is None:
+            y = torch.empty((N, D), dtype=dt, device=dev)
+        if workspace is None:
+            workspace = alloc_workspace(mlp_workspace_bytes(N, D, F, tile_tokens, dt, False), dev)
     _check(y, "y", dt, (N, D), dev)
-    if workspace is None:
-        workspace = alloc_workspace(mlp_workspace_bytes(N, D, F, tile_tokens, dt, False), dev)
     rc = lib.upipe_mlp_fwd(dtype_code(dt), N, D, F, int(tile_tokens), _ptr(x), _ptr(w_gate), _ptr(w_up),
                            _ptr(w_down), _ptr(y), _ptr(workspace), workspace.numel(), _stream_handle(dev, stream))
     if rc != 0:
@@ -365,16 +382,17 @@ def mlp_bwd(x, w_gate, w_up, w_down, dy, *, tile_tokens, out=None, workspace=Non
     _check(w_down, "w_down", dt, (D, F), dev)
     _check(dy, "dy", dt, (N, D), dev)
     f32 = torch.float32
-    if out is None:
-        out = (torch.empty((N, D), dtype=dt, device=dev), torch.empty((F, D), dtype=f32, device=dev),
-               torch.empty((F, D), dtype=f32, device=dev), torch.empty((D, F), dtype=f32, device=dev))
+    with _alloc_on(stream):
+        if out is None:
+            out = (torch.empty((N, D), dtype=dt, device=dev), torch.empty((F, D), dtype=f32, device=dev),
+                   torch.empty((F, D), dtype=f32, device=dev), torch.empty((D, F), dtype=f32, device=dev))
+        if workspace is None:
+            workspace = alloc_workspace(mlp_workspace_bytes(N, D, F, tile_tokens, dt, True), dev)
     dx, dwg, dwu, dwd = out
     _check(dx, "dx", dt, (N, D), dev)
     _check(dwg, "dw_gate", f32, (F, D), dev)
     _check(dwu, "dw_up", f32, (F, D), dev)
     _check(dwd, "dw_down", f32, (D, F), dev)
-    if workspace is None:
-        workspace = alloc_workspace(mlp_workspace_bytes(N, D, F, tile_tokens, dt, True), dev)
     rc = lib.upipe_mlp_bwd(dtype_code(dt), N, D, F, int(tile_tokens), _ptr(x), _ptr(w_gate), _ptr(w_up),
                            _ptr(w_down), _ptr(dy), _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd), _ptr(workspace),
                            workspace.numel(), _stream_handle(dev, stream))
@@ -426,15 +444,16 @@ def block_fwd(x, weights: dict, shape: BlockShape, *, y=None, h_mid=None, lse=No
     N, D = shape.n_tokens, shape.d_model
     _check(x, "x", dt, (N, D), dev)
     w = _block_weights(shape, weights, dt, dev)
-    y = torch.empty((N, D), dtype=dt, device=dev) if y is None else y
+    qk = weights.get("q_norm") is not None
+    with _alloc_on(stream):
+        y = torch.empty((N, D), dtype=dt, device=dev) if y is None else y
+        if workspace is None:
+            workspace = alloc_workspace(block_workspace_bytes(shape, qk, dt, False), dev)
     _check(y, "y", dt, (N, D), dev)
     if h_mid is not None:
         _check(h_mid, "h_mid", dt, (N, D), dev)
     if lse is not None:
         _check(lse, "lse", torch.float32, (shape.n_q_heads, N), dev)
-    qk = weights.get("q_norm") is not None
-    if workspace is None:
-        workspace = alloc_workspace(block_workspace_bytes(shape, qk, dt, False), dev)
     rc = lib.upipe_block_fwd(dtype_code(dt), ctypes.byref(shape), _ptr(x), ctypes.byref(w), _ptr(y), _ptr(h_mid),
                              _ptr(lse), _ptr(workspace), workspace.numel(), _stream_handle(dev, stream))
     if rc != 0:
@@ -461,9 +480,13 @@ def block_bwd(x, weights: dict, shape: BlockShape, dy, *, h_mid=None, lse=None, 
     qk = weights.get("q_norm") is not None
     shapes = _block_weight_shapes(shape)
     f32 = torch.float32
-    if grads is None:
-        grads = {n: torch.empty(shapes[n], dtype=f32, device=dev) for n in _BLOCK_TENSORS
-                 if qk or n not in ("q_norm", "k_norm")}
+    with _alloc_on(stream):
+        if grads is None:
+            grads = {n: torch.empty(shapes[n], dtype=f32, device=dev) for n in _BLOCK_TENSORS
+                     if qk or n not in ("q_norm", "k_norm")}
+        dx = torch.empty((N, D), dtype=dt, device=dev) if dx is None else dx
+        if workspace is None:
+            workspace = alloc_workspace(block_workspace_bytes(shape, qk, dt, True), dev)
     g = BlockGrads()
     for n in _BLOCK_TENSORS:
         t = grads.get(n)
@@ -471,10 +494,7 @@ def block_bwd(x, weights: dict, shape: BlockShape, dy, *, h_mid=None, lse=None, 
             continue
         _check(t, "grad " + n, f32, shapes[n], dev)
         setattr(g, n, t.data_ptr())
-    dx = torch.empty((N, D), dtype=dt, device=dev) if dx is None else dx
     _check(dx, "dx", dt, (N, D), dev)
-    if workspace is None:
-        workspace = alloc_workspace(block_workspace_bytes(shape, qk, dt, True), dev)
     rc = lib.upipe_block_bwd(dtype_code(dt), ctypes.byref(shape), _ptr(x), ctypes.byref(w), _ptr(h_mid), _ptr(lse),
                              _ptr(dy), _ptr(dx), ctypes.byref(g), _ptr(workspace), workspace.numel(),
                              _stream_handle(dev, stream))
@@ -509,11 +529,12 @@ def stack_fwd(x, layers, shape: BlockShape, host_inputs, *, y=None, workspace=No
     _check(x, "x", dt, (N, D), dev)
     _check_host(host_inputs, "host_inputs", dt, (L, N, D))
     ws = (BlockWeights * L)(*[_block_weights(shape, w, dt, dev) for w in layers])
-    y = torch.empty((N, D), dtype=dt, device=dev) if y is None else y
-    _check(y, "y", dt, (N, D), dev)
     qk = layers[0].get("q_norm") is not None
-    if workspace is None:
-        workspace = alloc_workspace(stack_workspace_bytes(shape, qk, dt), dev)
+    with _alloc_on(stream):
+        y = torch.empty((N, D), dtype=dt, device=dev) if y is None else y
+        if workspace is None:
+            workspace = alloc_workspace(stack_workspace_bytes(shape, qk, dt), dev)
+    _check(y, "y", dt, (N, D), dev)
     rc = lib.upipe_stack_fwd(dtype_code(dt), ctypes.byref(shape), L, ws, _ptr(x), _ptr(y),
                              ctypes.c_void_p(host_inputs.data_ptr()), _ptr(workspace), workspace.numel(),
                              _stream_handle(dev, stream), _stream_ptr(dev, copy_stream))
@@ -536,9 +557,13 @@ def stack_bwd(layers, shape: BlockShape, host_inputs, dy, *, dx=None, grads=None
     qk = layers[0].get("q_norm") is not None
     shapes = _block_weight_shapes(shape)
     f32 = torch.float32
-    if grads is None:
-        grads = [{n: torch.empty(shapes[n], dtype=f32, device=dev) for n in _BLOCK_TENSORS
-                  if qk or n not in ("q_norm", "k_norm")} for _ in range(L)]
+    with _alloc_on(stream):
+        if grads is None:
+            grads = [{n: torch.empty(shapes[n], dtype=f32, device=dev) for n in _BLOCK_TENSORS
+                      if qk or n not in ("q_norm", "k_norm")} for _ in range(L)]
+        dx = torch.empty((N, D), dtype=dt, device=dev) if dx is None else dx
+        if workspace is None:
+            workspace = alloc_workspace(stack_workspace_bytes(shape, qk, dt), dev)
     gs = (BlockGrads * L)()
     for i, gd in enumerate(grads):
         for n in _BLOCK_TENSORS:
@@ -547,16 +572,22 @@ def stack_bwd(layers, shape: BlockShape, host_inputs, dy, *, dx=None, grads=None
                 continue
             _check(t, f"layer {i} grad {n}", f32, shapes[n], dev)
             setattr(gs[i], n, t.data_ptr())
-    dx = torch.empty((N, D), dtype=dt, device=dev) if dx is None else dx
     _check(dx, "dx", dt, (N, D), dev)
-    if workspace is None:
-        workspace = alloc_workspace(stack_workspace_bytes(shape, qk, dt), dev)
     rc = lib.upipe_stack_bwd(dtype_code(dt), ctypes.byref(shape), L, ws, ctypes.c_void_p(host_inputs.data_ptr()),
                              _ptr(dy), _ptr(dx), gs, _ptr(workspace), workspace.numel(), _stream_handle(dev, stream),
                              _stream_ptr(dev, copy_stream))
     if rc != 0:
         raise UpipeError(rc, "upipe_stack_bwd")
     return dx, grads
+
+
+def device_peak(device: int = 0) -> dict:
+    """Dense bf16 MFMA peak of a device from its properties (upipe_device_peak)."""
+    tf, cu, clk = ctypes.c_double(0), ctypes.c_int(0), ctypes.c_int(0)
+    rc = load().upipe_device_peak(int(device), ctypes.byref(tf), ctypes.byref(cu), ctypes.byref(clk))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_device_peak")
+    return {"bf16_dense_tflops": tf.value, "compute_units": cu.value, "clock_khz": clk.value}
 
 
 def profile_start():

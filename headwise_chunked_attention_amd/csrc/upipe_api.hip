@@ -656,6 +656,15 @@ const char* upipe_strerror(int code) {
 
 int upipe_version(void) { return 100; }
 
+int upipe_device_peak(int device, double* bf16_dense_tflops, int* compute_units, int* clock_khz) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return UPIPE_ERR_HIP;
+  if (bf16_dense_tflops) *bf16_dense_tflops = (double)prop.multiProcessorCount * prop.clockRate * 1e3 * 4096.0 / 1e12;
+  if (compute_units) *compute_units = prop.multiProcessorCount;
+  if (clock_khz) *clock_khz = prop.clockRate;
+  return UPIPE_OK;
+}
+
 int upipe_profile_start(void) {
   g_prof.on = true;
   return UPIPE_OK;

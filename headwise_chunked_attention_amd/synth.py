@@ -58,9 +58,12 @@ def _block_rng(seed: int, tensor_id: int, block: int) -> np.random.Generator:
 
 
 def gen_rows(name: str, rows: int, cols: int, std: float, dtype: str, seed: int = 0,
-             row_start: int = 0, row_stop: int | None = None) -> np.ndarray:
+             row_start: int = 0, row_stop: int | None = None,
+             row_scale: np.ndarray | None = None) -> np.ndarray:
     """Rows ``[row_start, row_stop)`` of the ``rows x cols`` tensor ``name``.
 
+    ``row_scale`` (length ``rows``), if given, multiplies row p by
+    ``row_scale[p]`` after the std and before the bf16 rounding.
     Returns float32 (already bf16-rounded when ``dtype == 'bf16'``).
     """
     if row_stop is None:
@@ -86,6 +89,8 @@ def gen_rows(name: str, rows: int, cols: int, std: float, dtype: str, seed: int 
             dst[...] = rng.standard_normal((hi - lo, cols), dtype=np.float32)[s0 - lo:s1 - lo]
         if std != 1.0:
             dst *= np.float32(std)
+        if row_scale is not None:
+            dst *= np.asarray(row_scale[s0:s1], dtype=np.float32)[:, None]
         if dtype == "bf16":
             _round_bf16_inplace(dst)
 
@@ -125,24 +130,41 @@ def gen_gamma(name: str, d: int, mode: str, dtype: str, seed: int = 0) -> np.nda
     return round_to_bf16(g) if dtype == "bf16" else g
 
 
+def sharp_x_row_scale(n_tokens: int, first: int = 64, first_scale: float = 1.0 / 16,
+                      growth: float = 0.25) -> np.ndarray:
+    """Row scales of x for the sharp-softmax stress inputs: the first ``first``
+    rows are shrunk by ``first_scale`` (the keys of a causal row's first tile
+    then score near 0 against every query), and the rest grow linearly from 1
+    to ``1 + growth`` along the sequence (later keys score higher)."""
+    p = np.arange(n_tokens, dtype=np.float64)
+    s = 1.0 + growth * p / max(1, n_tokens)
+    s[:first] = first_scale
+    return s.astype(np.float32)
+
+
 class LayerInputs:
     """All inputs of one attention-layer problem, as float32 host arrays.
 
     Shapes follow the library's layout: x, dy ``[N][D]``; wq ``[Hq*d][D]``;
     wk, wv ``[Hkv*d][D]``; wo ``[D][Hq*d]``; gammas ``[d]`` or None.
+    ``qk_std`` (default ``w_std``) is the std of Wq and Wk alone and
+    ``x_row_scale`` an optional per-row scale of x: together they make the
+    sharp-softmax stress inputs (logit std ``d_model * qk_std**2``).
     """
 
     def __init__(self, n_tokens: int, d_model: int, n_q_heads: int, n_kv_heads: int,
                  head_dim: int, dtype: str, seed: int = 0, w_std: float = 0.02,
-                 qk_norm: str | None = None, with_x: bool = True, with_dy: bool = True):
+                 qk_norm: str | None = None, with_x: bool = True, with_dy: bool = True,
+                 qk_std: float | None = None, x_row_scale: np.ndarray | None = None):
         self.n_tokens, self.d_model = n_tokens, d_model
         self.n_q_heads, self.n_kv_heads, self.head_dim = n_q_heads, n_kv_heads, head_dim
         self.dtype, self.seed, self.w_std = dtype, seed, w_std
         N, D, d = n_tokens, d_model, head_dim
-        self.x = gen_rows("x", N, D, 1.0, dtype, seed) if with_x else None
+        qk_std = w_std if qk_std is None else qk_std
+        self.x = gen_rows("x", N, D, 1.0, dtype, seed, row_scale=x_row_scale) if with_x else None
         self.dy = gen_rows("dy", N, D, 1.0, dtype, seed) if with_dy else None
-        self.wq = gen_rows("wq", n_q_heads * d, D, w_std, dtype, seed)
-        self.wk = gen_rows("wk", n_kv_heads * d, D, w_std, dtype, seed)
+        self.wq = gen_rows("wq", n_q_heads * d, D, qk_std, dtype, seed)
+        self.wk = gen_rows("wk", n_kv_heads * d, D, qk_std, dtype, seed)
         self.wv = gen_rows("wv", n_kv_heads * d, D, w_std, dtype, seed)
         self.wo = gen_rows("wo", D, n_q_heads * d, w_std, dtype, seed)
         if qk_norm is None:

@@ -81,7 +81,10 @@ enum {
  * (backward = 1) needs for these sizes. Pure host arithmetic, no HIP call.
  * Returns 0 when the arguments would be rejected by the entry point.
  * The per-chunk part grows with chunk_heads, not with n_q_heads: this is the
- * one small buffer that every chunk reuses (the method's memory saving).
+ * one small buffer that every chunk reuses, the method's memory saving
+ * (memeeeeeex.com article, section "Untied Ulysses (UPipe) — head 単位の
+ * チャンク化": the next chunk reuses the previous chunk's buffer;
+ * liquidgold.cc notes, "Primary Contribution").
  */
 size_t upipe_attn_workspace_bytes(int64_t n_tokens, int64_t d_model, int n_q_heads,
                                   int n_kv_heads, int head_dim, int chunk_heads,
@@ -113,6 +116,11 @@ int upipe_choose_chunk_heads(int64_t n_tokens, int64_t d_model, int n_q_heads, i
  * Chunks of chunk_heads query heads run in order; each projects its Q (the
  * first chunk of a kv group also projects that group's K and V), runs causal
  * GQA flash attention, and adds O_c Wo_c^T into y (the first chunk writes y).
+ * This is the chunk loop of the memeeeeeex.com article, section "Untied
+ * Ulysses (UPipe) — head 単位のチャンク化" (per chunk: recompute the heads,
+ * compute attention, store the partial result, move on), and of the
+ * liquidgold.cc notes, "Primary Contribution" (heads processed in chunks so
+ * that only one chunk's intermediates exist at a time).
  *   x [N][D], wq [Hq*d][D], wk/wv [Hkv*d][D], wo [D][Hq*d]  (io dtype, in)
  *   q_norm_w, k_norm_w [d] or both NULL; norm_eps their epsilon
  *   y [N][D] io dtype (out), lse [Hq][N] fp32 (out)
@@ -130,7 +138,11 @@ int upipe_attn_fwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n
  * returned for the same inputs. Nothing else is kept from the forward:
  * per chunk the projections and the attention output O are recomputed (O from
  * the saved lse), then the attention backward and the projection gradients
- * run, chunk by chunk, in the same reused workspace.
+ * run, chunk by chunk, in the same reused workspace. The same chunk loop as
+ * the forward (memeeeeeex.com article, section "Untied Ulysses (UPipe) — head
+ * 単位のチャンク化", whose chunks are "recomputed"; liquidgold.cc notes,
+ * "Primary Contribution"), with the talk's activation checkpointing applied
+ * inside the op ("Road to 5 Million Tokens", transcript, checkpointing part).
  *   dy [N][D] io dtype (in), lse [Hq][N] fp32 (in)
  *   dx [N][D] io dtype (out)
  *   dwq, dwk, dwv, dwo fp32 (out), shapes of wq, wk, wv, wo
@@ -363,6 +375,16 @@ int upipe_profile_stop(double* total_ms, int64_t* launches, double* flops, int n
 
 /* Static text for an error code. */
 const char* upipe_strerror(int code);
+
+/*
+ * Dense bf16 MFMA peak of a device from its properties: compute units x
+ * maximum engine clock x 4096 flop per clock per compute unit (CDNA4's dense
+ * bf16 rate per CU). Used by benchmarks to state the peak they divide by.
+ *   device: HIP device ordinal; compute_units, clock_khz: may be NULL
+ * Returns UPIPE_OK, or UPIPE_ERR_HIP when the device cannot be queried
+ * (outputs untouched).
+ */
+int upipe_device_peak(int device, double* bf16_dense_tflops, int* compute_units, int* clock_khz);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int upipe_version(void);

@@ -26,10 +26,10 @@ def host(t):
 
 
 class Case:
-    def __init__(self, N, D, hq, hkv, d, dtype, theta=5e5, norm=None, seed=0, eps=1e-6):
+    def __init__(self, N, D, hq, hkv, d, dtype, theta=5e5, norm=None, seed=0, eps=1e-6, inp=None):
         self.N, self.D, self.hq, self.hkv, self.d = N, D, hq, hkv, d
         self.dtype, self.theta, self.eps = dtype, theta, eps
-        self.inp = LayerInputs(N, D, hq, hkv, d, dtype, seed=seed, qk_norm=norm)
+        self.inp = inp if inp is not None else LayerInputs(N, D, hq, hkv, d, dtype, seed=seed, qk_norm=norm)
         self.norm = norm is not None
         i = self.inp
         self.t = {k: dev(getattr(i, k), dtype) for k in ("x", "dy", "wq", "wk", "wv", "wo", "q_norm", "k_norm")}

@@ -1,0 +1,30 @@
+"""Sharp-softmax stress inputs shared by the replay test (CPU) and the GPU
+parity test. Each case: (dtype, N, d_model, Hq, Hkv, head_dim, qk_std,
+chunk sizes, seed). Wq and Wk have std qk_std (logit std about
+d_model * qk_std^2 before the row scales), and x rows follow
+``synth.sharp_x_row_scale``: the first 64 rows shrunk 16x (the first key
+tile scores near 0 against every query), the rest growing by 25% along the
+sequence. The Llama3-8B-shaped case is the stress input with Wq and Wk at
+three times their usual std (0.06 instead of 0.02: logit std near 15)."""
+import numpy as np
+
+from headwise_chunked_attention_amd.synth import LayerInputs, sharp_x_row_scale
+
+CASES = {
+    "bf16-d128-gqa4": ("bf16", 3000, 512, 4, 1, 128, 0.1, (1, 4), 21),
+    "bf16-d64-gqa4x2": ("bf16", 2100, 512, 8, 2, 64, 0.1, (2,), 22),
+    "bf16-llama-w3": ("bf16", 2304, 4096, 4, 1, 128, 0.06, (1,), 23),
+    "fp32-d64-gqa4x2": ("fp32", 2048, 256, 8, 2, 64, 0.14, (2,), 24),
+    "fp32-d128-w-std15": ("fp32", 1500, 256, 4, 1, 128, 0.242, (4,), 25),
+}
+
+
+def inputs(name):
+    dt, N, D, hq, hkv, d, qk_std, _, seed = CASES[name]
+    return LayerInputs(N, D, hq, hkv, d, dt, seed=seed, qk_std=qk_std, x_row_scale=sharp_x_row_scale(N))
+
+
+def logit_std(inter, head_dim):
+    """Std of the visible scores of q head 0 (natural-log units)."""
+    s = inter["q"][0] @ inter["k"][0].T / np.sqrt(head_dim)
+    return float(s[np.tril(np.ones(s.shape, bool))].std())

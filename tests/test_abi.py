@@ -22,7 +22,7 @@ def test_exports_every_header_symbol(lib):
                           "upipe_profile_stop", "upipe_mlp_workspace_bytes", "upipe_mlp_fwd", "upipe_mlp_bwd",
                           "upipe_loss_workspace_bytes", "upipe_loss_fwd", "upipe_loss_bwd",
                           "upipe_block_workspace_bytes", "upipe_block_fwd", "upipe_block_bwd",
-                          "upipe_stack_workspace_bytes", "upipe_stack_fwd", "upipe_stack_bwd"}
+                          "upipe_stack_workspace_bytes", "upipe_stack_fwd", "upipe_stack_bwd", "upipe_device_peak"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.upipe_version() == 100

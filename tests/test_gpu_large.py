@@ -37,8 +37,9 @@ TOL = 2e-2
 
 CONFIGS = {
     "llama3-8b-share-131k": dict(N=131072, D=4096, hq=4, hkv=1, d=128, theta=5e5, norm=None, chunks=(1, 2, 4)),
-    "llama3-8b-share-1m": dict(N=1048576, D=4096, hq=4, hkv=1, d=128, theta=5e5, norm=None, chunks=(1, 4)),
-    "qwen3-32b-share-512k": dict(N=524288, D=5120, hq=8, hkv=1, d=128, theta=1e6, norm="random", chunks=(1, 8)),
+    "llama3-8b-share-1m": dict(N=1048576, D=4096, hq=4, hkv=1, d=128, theta=5e5, norm=None, chunks=(1, 2, 4)),
+    "qwen3-32b-share-512k": dict(N=524288, D=5120, hq=8, hkv=1, d=128, theta=1e6, norm="random",
+                                 chunks=(1, 2, 4, 8)),
 }
 
 

@@ -79,3 +79,42 @@ def test_bf16_group_of_two(C):
     (K/V and their gradients stay resident between them); at C=4 one chunk holds
     two groups. N not a multiple of any tile."""
     _run(Case(900, 256, 4, 2, 128, "bf16", seed=12), C)
+
+
+def test_side_stream_with_internal_workspace():
+    """fwd+bwd enqueued on a second stream, letting the binding allocate the
+    workspace and outputs, while the default stream allocates and writes
+    memory right after each call: the results must equal those of the same
+    calls on the default stream (the forward bit for bit; the binding allocates on the
+    stream it launches on, so its freed workspace cannot be reused under the
+    side stream's kernels)."""
+    case = Case(1500, 512, 4, 1, 128, "bf16", seed=31)
+    t = case.t
+    kw = case.kw(1)
+    y0, lse0 = api_fwd(t, kw)
+    g0 = api_bwd(t, kw, lse0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    y1, lse1 = api_fwd(t, kw, stream=side)
+    junk = [torch.full((1 << 24,), float(i), device="cuda") for i in range(8)]  # default stream, may reuse freed blocks
+    g1 = api_bwd(t, kw, lse1, stream=side)
+    junk += [torch.full((1 << 24,), -float(i), device="cuda") for i in range(8)]
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(y0, y1) and torch.equal(lse0, lse1)
+    for a, b in zip(g0[:5], g1[:5]):
+        # gradients: split sums are added atomically, in no fixed order, so
+        # only the forward is compared bit for bit
+        e = float((a.double() - b.double()).norm() / a.double().norm())
+        assert e <= 1e-3, e
+
+
+def api_fwd(t, kw, stream=None):
+    from headwise_chunked_attention_amd import api
+    return api.attn_fwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], stream=stream, **kw)
+
+
+def api_bwd(t, kw, lse, stream=None):
+    from headwise_chunked_attention_amd import api
+    return api.attn_bwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], t["dy"], lse, stream=stream, **kw)

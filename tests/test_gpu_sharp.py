@@ -1,0 +1,41 @@
+"""GPU parity on sharp-softmax stress inputs: the forward kernel's online
+softmax moves its base after the first tile (bf16: in both 32-key halves;
+fp32: per tile), which the config-shaped inputs never make it do.
+
+The inputs (``sharp_cases``) have logit std 6 to 18 and key scores that grow
+along the sequence; ``test_sharp_replay.py`` shows on the host that each
+case makes hundreds of base moves. Here every output and gradient is
+compared element by element with the fp64 oracle at the layer's tolerances
+(relative L2 1e-5 fp32, 2e-2 bf16; LSE also max-abs)."""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from gpu_util import Case, check_bwd, check_fwd  # noqa: E402
+from sharp_cases import CASES, inputs  # noqa: E402
+from softmax_replay import replay_layer  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_sharp_softmax_parity(name):
+    dt, N, D, hq, hkv, d, _, chunks, _ = CASES[name]
+    inp = inputs(name)
+    case = Case(N, D, hq, hkv, d, dt, inp=inp)
+    y_ref, lse_ref, inter = oracle.layer_fwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, hq, hkv, d, case.theta, hq,
+                                             keep=True)
+    moves = replay_layer(inter, hq, hkv, dt)["moves"]
+    print(f"case {name}: N={N} D={D} hq={hq} hkv={hkv} d={d} {dt}; replayed base moves {moves}", flush=True)
+    g_ref = case.oracle_bwd(hq)
+    for C in chunks:
+        y, lse = case.gpu_fwd(C)
+        check_fwd(case, C, y, lse, (y_ref, lse_ref))
+        check_bwd(case, C, case.gpu_bwd(C, lse), g_ref)
