@@ -560,7 +560,7 @@ hipError_t launch_dkdv_d(const AttnBwd<T>& p, hipStream_t s) {
   // workgroups per CU. With fewer key blocks than that and several heads, the
   // heads are split over hs workgroups and their partial sums added atomically.
   int hs = 1;
-  while (nkb * hs < 4 * 256 && p.nh % (hs * 2) == 0) hs *= 2;
+  while (!p.no_head_split && nkb * hs < 4 * 256 && p.nh % (hs * 2) == 0) hs *= 2;
   hipError_t e;
   if (hs > 1 && !p.accumulate) {
     if ((e = launch_fill_f32(p.dk_acc, nkb * G::BKEY * D, 0.f, s)) != hipSuccess) return e;

@@ -72,9 +72,20 @@ __global__ __launch_bounds__(256) void grad_finish_kernel(const GradFinish<T> p)
     }
   }
   if (p.gamma && p.dgamma && act) {
-    atomicAdd(p.dgamma + i, dg0);
-    atomicAdd(p.dgamma + i + D / 2, dg1);
+    // this wave's partial sums; dgamma_reduce_kernel adds them in wave order
+    float* part = p.dg_part + ((int64_t)blockIdx.x * 4 + wave_id()) * D;
+    part[i] = dg0;
+    part[i + D / 2] = dg1;
   }
+}
+
+// dgamma[i] += sum over waves w = 0, 1, ... of part[w][i], in that order.
+__global__ __launch_bounds__(128) void dgamma_reduce_kernel(const float* part, int64_t waves, int d, float* dgamma) {
+  const int i = threadIdx.x;
+  if (i >= d) return;
+  float acc = 0.f;
+  for (int64_t w = 0; w < waves; ++w) acc += part[w * d + i];
+  dgamma[i] += acc;
 }
 
 // Sum over the 256 threads of a block; every thread gets the total. red holds
@@ -276,6 +287,12 @@ hipError_t launch_grad_finish(const GradFinish<T>& p, int head_dim, hipStream_t 
   const int64_t rows = (int64_t)p.nh * p.Np;
   int64_t blocks = (rows + 3) / 4;
   if (blocks > 4096) blocks = 4096;
+  const bool dg = p.gamma && p.dgamma;
+  if (dg) {
+    // four waves per block, each with its own row of partial sums
+    if (!p.dg_part || p.dg_waves < 4) return hipErrorInvalidValue;
+    if (blocks > p.dg_waves / 4) blocks = p.dg_waves / 4;
+  }
   if (blocks < 1) return hipSuccess;
   if (head_dim == 64)
     hipLaunchKernelGGL((grad_finish_kernel<T, 64>), dim3((unsigned)blocks), dim3(256), 0, s, p);
@@ -283,6 +300,9 @@ hipError_t launch_grad_finish(const GradFinish<T>& p, int head_dim, hipStream_t 
     hipLaunchKernelGGL((grad_finish_kernel<T, 128>), dim3((unsigned)blocks), dim3(256), 0, s, p);
   else
     return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !dg) return e;
+  hipLaunchKernelGGL(dgamma_reduce_kernel, dim3(1), dim3(128), 0, s, p.dg_part, blocks * 4, head_dim, p.dgamma);
   return hipGetLastError();
 }
 

@@ -704,11 +704,22 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   float* Cs = reinterpret_cast<float*>(smem);
   acc_to_lds<BN>(Cs, 0, BM, wm, wn, acc);
   lds_barrier();
+  const int tid = threadIdx.x;
+  if (p.part && p.ksplit < p.K) {
+    // fixed-order reduction: this split's tile goes whole to part[split], and
+    // splitk_reduce_kernel adds the splits into out one after another
+    float* dst = p.part + (bid / (gm * gn)) * p.M * p.N;
+    for (int c = tid; c < BM * BN / 4; c += NTHREADS) {
+      const int row = c / (BN / 4), col = (c % (BN / 4)) * 4;
+      *reinterpret_cast<f32x4*>(dst + (m0 + row) * p.N + (n0 + col)) =
+          *reinterpret_cast<const f32x4*>(Cs + row * SC + col);
+    }
+    return;
+  }
   int seg = 0;
   while (seg + 1 < p.nseg && n0 >= p.seg_end[seg]) ++seg;
   float* out = p.out[seg];
   const int64_t nc0 = n0 - (seg ? p.seg_end[seg - 1] : 0);
-  const int tid = threadIdx.x;
   if (p.ldn == 1 && p.ksplit >= p.K && (p.ldm & 3) == 0) {
     // one k split: this workgroup is the only writer of its tile in this
     // launch (launches on a stream run in order), so a plain read-modify-write
@@ -727,6 +738,26 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
       const int col = c / BM, row = c % BM;
       atomicAdd(out + (m0 + row) * p.ldm + (nc0 + col) * p.ldn, Cs[row * SC + col]);
     }
+  }
+}
+
+// out (+)= sum over the nsplit partial tiles part[s][M][N], s = 0, 1, ... in
+// that order (one thread per output element; the output addressing and
+// segments are those of the TN GEMM).
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmTN<T> p, int64_t nsplit) {
+  const int64_t total = p.M * p.N;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+    // n fastest when the output's n stride is 1, else m fastest (coalesced stores)
+    const int64_t m = p.ldn == 1 ? idx / p.N : idx % p.M;
+    const int64_t n = p.ldn == 1 ? idx % p.N : idx / p.M;
+    float acc = 0.f;
+    for (int64_t sp = 0; sp < nsplit; ++sp) acc += p.part[sp * total + m * p.N + n];
+    int seg = 0;
+    while (seg + 1 < p.nseg && n >= p.seg_end[seg]) ++seg;
+    const int64_t nc = n - (seg ? p.seg_end[seg - 1] : 0);
+    p.out[seg][m * p.ldm + nc * p.ldn] += acc;
   }
 }
 
@@ -772,13 +803,19 @@ template <typename T>
 hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s) {
   // whole tiles along M and N; every split holds at least one k row
   if (p.K <= 0 || p.ksplit <= 0 || p.M <= 0 || p.M % BM || bn <= 0 || p.N <= 0 || p.N % bn) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((p.M / BM) * (p.N / bn) * ((p.K + p.ksplit - 1) / p.ksplit)));
+  const int64_t nsplit = (p.K + p.ksplit - 1) / p.ksplit;
+  const dim3 grid((unsigned)((p.M / BM) * (p.N / bn) * nsplit));
   if (bn == 128)
     hipLaunchKernelGGL((gemm_tn_kernel<T, 128>), grid, dim3(NTHREADS), 0, s, p);
   else if (bn == 64)
     hipLaunchKernelGGL((gemm_tn_kernel<T, 64>), grid, dim3(NTHREADS), 0, s, p);
   else
     return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.part || nsplit < 2) return e;
+  int64_t blocks = (p.M * p.N + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL((splitk_reduce_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s, p, nsplit);
   return hipGetLastError();
 }
 

@@ -106,6 +106,11 @@ struct GemmTN {
   int64_t seg_end[3];
   int nseg;
   int64_t ldm, ldn;
+  // with several k splits: null = add each split's tile into out with fp32
+  // atomics (order unspecified); else each split stores its tile to
+  // part[split][M][N] and launch_gemm_tn adds the splits into out in split
+  // order (bitwise reproducible)
+  float* part;
 };
 
 // Causal GQA attention forward over one kv head and `nh` q heads.
@@ -153,6 +158,7 @@ struct AttnBwd {
   int accumulate;
   float dk_mul;  // sqrt(D) ln 2: dK from the pre-scaled q (see below)
   float dv_mul;  // sqrt(D): dV from the pre-scaled dout
+  int no_head_split;  // 1: one workgroup per key block (no fp32 atomics)
 };
 
 // Per-row gradient finish for heads stored [nh][Np][D]:
@@ -170,6 +176,10 @@ struct GradFinish {
   int64_t N, Np;
   float eps;
   double log2_theta;
+  // dgamma: each wave stores its partial sums to dg_part[wave][D] (room for
+  // dg_waves waves), and launch_grad_finish adds them into dgamma in wave order
+  float* dg_part;
+  int64_t dg_waves;
 };
 
 // RMSNorm over rows of D elements (row stride D), optionally after a residual add:

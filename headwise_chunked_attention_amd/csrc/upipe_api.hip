@@ -14,6 +14,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "upipe.h"
@@ -30,6 +31,29 @@ Profiler g_prof;
 }  // namespace upipe
 
 namespace {
+
+// Scratch of upipe_attn_fwd_noalloc. In host code `scratch` names a host-side
+// stand-in, not device memory: kernels and copies get the per-device address
+// that noalloc_scratch() looks up once per device.
+__device__ __align__(256) char scratch[UPIPE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// This device's address of `scratch` (looked up on the first call with the
+// device current), or null when the lookup fails.
+void* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 constexpr int64_t ROW_PAD = 256;   // token rows of per-head buffers are padded to this
 
@@ -168,10 +192,14 @@ int run_heads_times_wt(const Shape& s, const T* a_heads, int nheads, const T* b,
 
 // Weight gradient out[m*ldm + n*ldn] += sum_tok rows[tok][m] * heads[n/d][tok][n%d],
 // with the heads split into up to 3 segments of seg_heads[i] heads, each with
-// its own output.
+// its own output. The token sum is split over workgroups; with part == null
+// the splits are added with fp32 atomics, else (deterministic) they go to
+// part (part_bytes of free workspace) and are added in split order, with as
+// many splits as part holds.
 template <typename T>
 int run_weight_grad_segs(const Shape& s, const T* rows, const T* heads, int nseg, const int* seg_heads,
-                         float* const* outs, int64_t ldm, int64_t ldn, hipStream_t st) {
+                         float* const* outs, int64_t ldm, int64_t ldn, hipStream_t st, float* part = nullptr,
+                         size_t part_bytes = 0) {
   GemmTN<T> g;
   memset(&g, 0, sizeof(g));
   g.a = rows;
@@ -195,6 +223,11 @@ int run_weight_grad_segs(const Shape& s, const T* rows, const T* heads, int nseg
   const int bn = all128 ? 128 : 64;  // n tiles never straddle two segments
   const int64_t tiles = (g.M / 128) * (g.N / bn);
   int64_t splits = 1024 / (tiles > 0 ? tiles : 1);
+  if (part) {
+    const int64_t fit = (int64_t)(part_bytes / ((size_t)g.M * g.N * 4));
+    if (splits > fit) splits = fit;
+    g.part = part;
+  }
   if (splits < 1) splits = 1;
   g.ksplit = round_up((s.N + splits - 1) / splits, 64);
   g.ldm = ldm;
@@ -205,8 +238,8 @@ int run_weight_grad_segs(const Shape& s, const T* rows, const T* heads, int nseg
 
 template <typename T>
 int run_weight_grad(const Shape& s, const T* rows, const T* heads, int nheads, float* out, int64_t ldm,
-                    int64_t ldn, hipStream_t st) {
-  return run_weight_grad_segs<T>(s, rows, heads, 1, &nheads, &out, ldm, ldn, st);
+                    int64_t ldn, hipStream_t st, float* part = nullptr, size_t part_bytes = 0) {
+  return run_weight_grad_segs<T>(s, rows, heads, 1, &nheads, &out, ldm, ldn, st, part, part_bytes);
 }
 
 template <typename T>
@@ -268,7 +301,7 @@ template <typename T>
 int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T* wk, const T* wv,
                   const T* wo, const T* qn, const T* kn, float eps, const T* dy, const float* lse,
                   T* dx, float* dwq, float* dwk, float* dwv, float* dwo, float* dqn, float* dkn,
-                  char* ws, hipStream_t st, const T* o_kept = nullptr) {
+                  char* ws, hipStream_t st, const T* o_kept = nullptr, bool det = false) {
   const Plan pl = make_plan(s, true);
   T* Q = reinterpret_cast<T*>(ws + pl.q);
   T* Uq = s.norm ? reinterpret_cast<T*>(ws + pl.uq) : nullptr;
@@ -296,6 +329,16 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
   const float do_scale = (float)(1.0 / sqrt((double)s.d));
   const float dk_mul = (float)(sqrt((double)s.d) * 0.6931471805599453);
   const float dv_mul = (float)sqrt((double)s.d);
+  // Free workspace borrowed by the fixed-order reductions. The dq accumulator
+  // is free while the weight gradients run (dWo before the dQ kernel fills
+  // it, the others after the dq finish has consumed it): deterministic mode
+  // keeps the split-K partial tiles there. dO and O are free once the
+  // attention backward of the chunk is done: the dgamma partials of the
+  // RMSNorm backward go there.
+  float* part = det ? dQa : nullptr;
+  const size_t part_bytes = det ? (size_t)head * s.C * 4 : 0;
+  float* dg_part = reinterpret_cast<float*>(ws + pl.dout);
+  const int64_t dg_waves = (int64_t)((pl.o + (size_t)head * s.C * s.es - pl.dout) / ((size_t)s.d * 4));
 
   HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dwq, (int64_t)s.Hq * s.d * s.D, 0.f, st); }));
   HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_fill_f32(dwk, (int64_t)s.Hkv * s.d * s.D, 0.f, st); }));
@@ -373,7 +416,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
                     [&] { return launch_attn_fwd<T>(a, s.d, 1, st); }));
     }
     // dWo[:, chunk] = dY^T O_c
-    int rc = run_weight_grad<T>(s, dy, O, s.C, dwo + (int64_t)c0 * s.d, (int64_t)s.Hq * s.d, 1, st);
+    int rc = run_weight_grad<T>(s, dy, O, s.C, dwo + (int64_t)c0 * s.d, (int64_t)s.Hq * s.d, 1, st, part, part_bytes);
     if (rc) return rc;
     // attention backward: dK/dV (key-stationary) and dQ (query-stationary)
     for (int j = 0; j < s.kvC; ++j) {
@@ -395,6 +438,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       b.accumulate = new_kv ? 0 : 1;
       b.dk_mul = dk_mul;
       b.dv_mul = dv_mul;
+      b.no_head_split = det ? 1 : 0;
       HIP_TRY(timed(UPIPE_KERNEL_ATTN_BWD_DKDV, 8.0 * s.d * nh * causal_pairs(s.N), st,
                     [&] { return launch_attn_bwd_dkdv<T>(b, s.d, st); }));
       HIP_TRY(timed(UPIPE_KERNEL_ATTN_BWD_DQ, 6.0 * s.d * nh * causal_pairs(s.N), st,
@@ -415,11 +459,13 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       f.Np = s.Np;
       f.eps = eps;
       f.log2_theta = l2t;
+      f.dg_part = dg_part;
+      f.dg_waves = dg_waves;
       HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_grad_finish<T>(f, s.d, st); }));
     }
     const bool group_done = last_kv || s.C >= s.G;  // dk/dv of the kv group are complete
     if (!group_done) {
-      rc = run_weight_grad<T>(s, x, Q, s.C, dwq + (int64_t)c0 * s.d * s.D, 1, s.D, st);
+      rc = run_weight_grad<T>(s, x, Q, s.C, dwq + (int64_t)c0 * s.d * s.D, 1, s.D, st, part, part_bytes);
       if (rc) return rc;
       rc = run_heads_times_wt<T>(s, Q, s.C, WqkvT, ldw, dx, c0 > 0, st);
       if (rc) return rc;
@@ -437,6 +483,8 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
       f.Np = s.Np;
       f.eps = eps;
       f.log2_theta = l2t;
+      f.dg_part = dg_part;
+      f.dg_waves = dg_waves;
       HIP_TRY(timed(UPIPE_KERNEL_OTHER, 0.0, st, [&] { return launch_grad_finish<T>(f, s.d, st); }));
       GradFinish<T> fv;
       memset(&fv, 0, sizeof(fv));
@@ -451,7 +499,7 @@ int attn_bwd_impl(const Shape& s, double theta, const T* x, const T* wq, const T
         const int seg_heads[3] = {s.C, s.kvC, s.kvC};
         float* const outs[3] = {dwq + (int64_t)c0 * s.d * s.D, dwk + (int64_t)g0 * s.d * s.D,
                                 dwv + (int64_t)g0 * s.d * s.D};
-        rc = run_weight_grad_segs<T>(s, x, Q, 3, seg_heads, outs, 1, s.D, st);
+        rc = run_weight_grad_segs<T>(s, x, Q, 3, seg_heads, outs, 1, s.D, st, part, part_bytes);
         if (rc) return rc;
       }
       // dx (+)= [dq_c | dk_g | dv_g] [Wq_c; Wk_g; Wv_g] in one pass over dx
@@ -609,12 +657,39 @@ int upipe_attn_fwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n
                               (const float*)k_norm_w, norm_eps, (float*)y, lse, ws, st);
 }
 
-int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
-                   int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
-                   const void* wk, const void* wv, const void* wo, const void* q_norm_w,
-                   const void* k_norm_w, float norm_eps, const void* dy, const float* lse, void* dx,
-                   float* dwq, float* dwk, float* dwv, float* dwo, float* dq_norm_w, float* dk_norm_w,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+int upipe_attn_fwd_noalloc(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
+                           int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
+                           const void* wk, const void* wv, const void* wo, const void* q_norm_w,
+                           const void* k_norm_w, float norm_eps, void* y, float* lse, void* stream) {
+  Shape s;
+  int rc = check_common(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads,
+                        q_norm_w, k_norm_w, norm_eps, &s);
+  if (rc) return rc;
+  const void* ptrs[] = {x, wq, wk, wv, wo, y, lse};
+  if ((rc = check_ptrs(ptrs, 7))) return rc;
+  if (s.norm) {
+    const void* np[] = {q_norm_w, k_norm_w};
+    if ((rc = check_ptrs(np, 2))) return rc;
+  }
+  if (make_plan(s, false).total > UPIPE_NOALLOC_SCRATCH_BYTES) return UPIPE_ERR_SCRATCH;
+  char* ws = reinterpret_cast<char*>(noalloc_scratch());
+  if (!ws) return UPIPE_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == UPIPE_BF16)
+    return attn_fwd_impl<bf16>(s, rope_theta, (const bf16*)x, (const bf16*)wq, (const bf16*)wk,
+                               (const bf16*)wv, (const bf16*)wo, (const bf16*)q_norm_w,
+                               (const bf16*)k_norm_w, norm_eps, (bf16*)y, lse, ws, st);
+  return attn_fwd_impl<float>(s, rope_theta, (const float*)x, (const float*)wq, (const float*)wk,
+                              (const float*)wv, (const float*)wo, (const float*)q_norm_w,
+                              (const float*)k_norm_w, norm_eps, (float*)y, lse, ws, st);
+}
+
+static int attn_bwd_entry(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
+                          int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
+                          const void* wk, const void* wv, const void* wo, const void* q_norm_w,
+                          const void* k_norm_w, float norm_eps, const void* dy, const float* lse, void* dx,
+                          float* dwq, float* dwk, float* dwv, float* dwo, float* dq_norm_w, float* dk_norm_w,
+                          void* workspace, size_t workspace_bytes, void* stream, bool det) {
   Shape s;
   int rc = check_common(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads,
                         q_norm_w, k_norm_w, norm_eps, &s);
@@ -634,11 +709,34 @@ int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n
     return attn_bwd_impl<bf16>(s, rope_theta, (const bf16*)x, (const bf16*)wq, (const bf16*)wk,
                                (const bf16*)wv, (const bf16*)wo, (const bf16*)q_norm_w,
                                (const bf16*)k_norm_w, norm_eps, (const bf16*)dy, lse, (bf16*)dx, dwq,
-                               dwk, dwv, dwo, dq_norm_w, dk_norm_w, ws, st);
+                               dwk, dwv, dwo, dq_norm_w, dk_norm_w, ws, st, nullptr, det);
   return attn_bwd_impl<float>(s, rope_theta, (const float*)x, (const float*)wq, (const float*)wk,
                               (const float*)wv, (const float*)wo, (const float*)q_norm_w,
                               (const float*)k_norm_w, norm_eps, (const float*)dy, lse, (float*)dx, dwq,
-                              dwk, dwv, dwo, dq_norm_w, dk_norm_w, ws, st);
+                              dwk, dwv, dwo, dq_norm_w, dk_norm_w, ws, st, nullptr, det);
+}
+
+int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
+                   int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
+                   const void* wk, const void* wv, const void* wo, const void* q_norm_w,
+                   const void* k_norm_w, float norm_eps, const void* dy, const float* lse, void* dx,
+                   float* dwq, float* dwk, float* dwv, float* dwo, float* dq_norm_w, float* dk_norm_w,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_bwd_entry(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads, x, wq,
+                        wk, wv, wo, q_norm_w, k_norm_w, norm_eps, dy, lse, dx, dwq, dwk, dwv, dwo, dq_norm_w,
+                        dk_norm_w, workspace, workspace_bytes, stream, false);
+}
+
+int upipe_attn_bwd_deterministic(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads,
+                                 int n_kv_heads, int head_dim, double rope_theta, int chunk_heads, const void* x,
+                                 const void* wq, const void* wk, const void* wv, const void* wo,
+                                 const void* q_norm_w, const void* k_norm_w, float norm_eps, const void* dy,
+                                 const float* lse, void* dx, float* dwq, float* dwk, float* dwv, float* dwo,
+                                 float* dq_norm_w, float* dk_norm_w, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return attn_bwd_entry(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads, x, wq,
+                        wk, wv, wo, q_norm_w, k_norm_w, norm_eps, dy, lse, dx, dwq, dwk, dwv, dwo, dq_norm_w,
+                        dk_norm_w, workspace, workspace_bytes, stream, true);
 }
 
 const char* upipe_strerror(int code) {
@@ -650,6 +748,8 @@ const char* upipe_strerror(int code) {
     case UPIPE_ERR_WORKSPACE: return "workspace missing or smaller than upipe_attn_workspace_bytes()";
     case UPIPE_ERR_ALIGNMENT: return "misaligned pointer (tensors need 16 bytes, the workspace 256 bytes)";
     case UPIPE_ERR_HIP: return "a HIP kernel launch failed";
+    case UPIPE_ERR_SCRATCH: return "upipe_attn_fwd_noalloc: the forward workspace of these sizes exceeds the "
+                                   "built-in scratch (UPIPE_NOALLOC_SCRATCH_BYTES); use upipe_attn_fwd";
     default: return "unknown error code";
   }
 }

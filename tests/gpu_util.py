@@ -64,15 +64,25 @@ class Case:
 GRAD_NAMES = ("dx", "dwq", "dwk", "dwv", "dwo", "dq_norm", "dk_norm")
 
 
-def check_fwd(case, C, y, lse, ref=None, tol=None):
+def check_fwd(case, C, y, lse, ref=None, tol=None, lse_bound=None):
+    """y and LSE against the oracle: relative L2 <= tol, and LSE max-abs <= tol,
+    or, with ``lse_bound`` ([Hq][N]), |LSE - ref| <= lse_bound element by element."""
     tol = tol or TOL[case.dtype]
     y_ref, lse_ref = ref if ref is not None else case.oracle_fwd(C)
     ey = relerr(host(y), y_ref)
     el = relerr(host(lse), lse_ref)
-    ml = float(np.max(np.abs(host(lse) - lse_ref)))
-    print(f"  fwd C={C}: y rel {ey:.3e}  lse rel {el:.3e} max {ml:.3e}", flush=True)
+    dl = np.abs(host(lse) - lse_ref)
+    ml = float(np.max(dl))
+    msg = f"  fwd C={C}: y rel {ey:.3e}  lse rel {el:.3e} max {ml:.3e}"
+    if lse_bound is not None:
+        msg += f" (max of |dLSE| / its rounding bound {float(np.max(dl / lse_bound)):.3f})"
+    print(msg, flush=True)
     assert ey <= tol, ("y", ey)
-    assert el <= tol and ml <= tol, ("lse", el, ml)
+    assert el <= tol, ("lse", el)
+    if lse_bound is None:
+        assert ml <= tol, ("lse max abs", ml)
+    else:
+        assert bool(np.all(dl <= lse_bound)), ("lse beyond its rounding bound", float(np.max(dl / lse_bound)))
 
 
 def check_bwd(case, C, grads, ref=None, tol=None):

@@ -28,3 +28,32 @@ def logit_std(inter, head_dim):
     """Std of the visible scores of q head 0 (natural-log units)."""
     s = inter["q"][0] @ inter["k"][0].T / np.sqrt(head_dim)
     return float(s[np.tril(np.ones(s.shape, bool))].std())
+
+
+def lse_rounding_bound(inter, n_q_heads, n_kv_heads, head_dim, d_model, dtype):
+    """Per-row bound [Hq][N] on |LSE_gpu - LSE_exact| from the io-dtype
+    arithmetic, for sharp scores where an absolute LSE tolerance does not
+    scale: LSE is 1-Lipschitz in the max norm of its row of scores, and the
+    GPU's score S_ij = q_i . k_j / sqrt(d) is formed from q and k that were
+    projected in fp32 and stored in the io dtype, so
+        |dS_ij| <= A_ij * 2 * (rounding of q and k),  A_ij = sum_k |q_ik k_jk| / sqrt(d);
+    the row sum of exp(S - base) adds at most its own relative rounding.
+    bf16: stored values round to 8 significant bits (2^-8 relative, plus 10%
+    for the fp32 projection and rotation before the rounding), and the
+    probabilities summed are bf16 too (2^-8). fp32: worst-case accumulation
+    of the d_model-long projection and the head_dim-long score (gamma_n =
+    n 2^-24), and of the N-long row sum."""
+    g = n_q_heads // n_kv_heads
+    out = []
+    for h in range(n_q_heads):
+        q, k = np.abs(inter["q"][h]), np.abs(inter["k"][h // g])
+        a = q @ k.T / np.sqrt(head_dim)
+        n = a.shape[0]
+        a[np.triu_indices(n, 1)] = 0.0
+        amax = a.max(axis=1)
+        if dtype == "bf16":
+            out.append(2.2 * 2.0 ** -8 * amax + 1.1 * 2.0 ** -8)
+        else:
+            u = 2.0 ** -24
+            out.append(2.2 * (d_model + head_dim + 4) * u * amax + (n + 4) * u)
+    return np.stack(out)

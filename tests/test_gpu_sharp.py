@@ -6,7 +6,11 @@ The inputs (``sharp_cases``) have logit std 6 to 18 and key scores that grow
 along the sequence; ``test_sharp_replay.py`` shows on the host that each
 case makes hundreds of base moves. Here every output and gradient is
 compared element by element with the fp64 oracle at the layer's tolerances
-(relative L2 1e-5 fp32, 2e-2 bf16; LSE also max-abs)."""
+(relative L2 1e-5 fp32, 2e-2 bf16). The LSE's max-abs check uses a per-row
+bound derived from the io-dtype rounding of q and k (``lse_rounding_bound``)
+instead of a fixed absolute tolerance: with logits of std 6 to 18 the
+rounding of bf16 scores alone moves a row's LSE by up to about 0.08 to 0.2,
+in the oracle's arithmetic as on the GPU."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -15,7 +19,7 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 from gpu_util import Case, check_bwd, check_fwd  # noqa: E402
-from sharp_cases import CASES, inputs  # noqa: E402
+from sharp_cases import CASES, inputs, lse_rounding_bound  # noqa: E402
 from softmax_replay import replay_layer  # noqa: E402
 
 
@@ -34,8 +38,9 @@ def test_sharp_softmax_parity(name):
                                              keep=True)
     moves = replay_layer(inter, hq, hkv, dt)["moves"]
     print(f"case {name}: N={N} D={D} hq={hq} hkv={hkv} d={d} {dt}; replayed base moves {moves}", flush=True)
+    bound = lse_rounding_bound(inter, hq, hkv, d, D, dt)
     g_ref = case.oracle_bwd(hq)
     for C in chunks:
         y, lse = case.gpu_fwd(C)
-        check_fwd(case, C, y, lse, (y_ref, lse_ref))
+        check_fwd(case, C, y, lse, (y_ref, lse_ref), lse_bound=bound)
         check_bwd(case, C, case.gpu_bwd(C, lse), g_ref)

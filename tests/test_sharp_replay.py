@@ -28,3 +28,35 @@ def test_stress_inputs_move_the_base(name):
     else:
         assert r["moves"]["tile"] >= 1000, r
     assert r["waves"] >= 100
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if CASES[n][0] == "bf16"])
+def test_lse_bound_covers_bf16_stored_scores(name):
+    """The per-row LSE bound of the stress test holds for the plainest model of
+    the kernel's arithmetic: scores from q (times log2(e)/sqrt(d)) and k
+    rounded to bf16, everything else exact. The bound must hold with room,
+    and must not be so loose that it says nothing (the rounding reaches at
+    least a twentieth of it somewhere)."""
+    import math
+
+    import numpy as np
+
+    from headwise_chunked_attention_amd.synth import round_to_bf16
+    from sharp_cases import lse_rounding_bound
+
+    dt, N, D, hq, hkv, d, _, _, _ = CASES[name]
+    inp = inputs(name)
+    _, lse, inter = oracle.layer_fwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, hq, hkv, d, 5e5, hq, keep=True)
+    bound = lse_rounding_bound(inter, hq, hkv, d, D, dt)
+    g = hq // hkv
+    worst = 0.0
+    for h in range(hq):
+        bq = round_to_bf16(inter["q"][h] * (1 / math.log(2) / math.sqrt(d))).astype(np.float64)
+        bk = round_to_bf16(inter["k"][h // g]).astype(np.float64)
+        s = (bq @ bk.T) * math.log(2)
+        s[np.triu_indices(N, 1)] = -np.inf
+        m = s.max(axis=1)
+        lse_b = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+        worst = max(worst, float(np.max(np.abs(lse_b - lse[h]) / bound[h])))
+    print(name, f"max |dLSE| / bound = {worst:.3f}")
+    assert 0.05 < worst < 0.5
