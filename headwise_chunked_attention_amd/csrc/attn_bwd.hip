@@ -208,15 +208,21 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     // pre-scaled q and dout): the accumulators start at -LSE and -Delta of
     // their query rows (element 4i+j is row 8i + 4h + j of the wave's 32),
     // so the MFMAs do the subtraction. Rows past the end of the sequence
-    // carry LSE = +inf, so their P is 0 without a mask.
-    f32x16 sacc, dpacc;
+    // carry LSE = +inf, so their P is 0 without a mask. fp32 starts the S
+    // chain at 0 and subtracts LSE once at the end instead: a chain started
+    // at -LSE rounds every partial sum at the LSE's magnitude, which for
+    // sharp scores (|LSE| in the hundreds of log2 units) costs fp32 several
+    // times the rounding of the plain S - LSE.
+    constexpr bool SUB_AFTER = sizeof(T) == 4;
+    f32x16 sacc, dpacc, lse_neg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + qt * 32 + 8 * i + 4 * h);
       const f32x4 dv4 = *reinterpret_cast<const f32x4*>(del_s + qt * 32 + 8 * i + 4 * h);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sacc[4 * i + j] = lv[j];
+        lse_neg[4 * i + j] = lv[j];
+        sacc[4 * i + j] = SUB_AFTER ? 0.f : lv[j];
         dpacc[4 * i + j] = dv4[j];
       }
     }
@@ -226,6 +232,10 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
       const Frag<T> vb = s == 0 ? vb0 : ld_frag(Vs + L::idx(krel, s * 16 + 8 * h));
       mma(sacc, ld_frag(Qs + L::idx(qt * 32 + r, s * 16 + 8 * h)), kb);
       mma(dpacc, ld_frag(dOs + L::idx(qt * 32 + r, s * 16 + 8 * h)), vb);
+    }
+    if constexpr (SUB_AFTER) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] += lse_neg[e];
     }
     // bf16: the dO^T / Q^T fragment pairs of the first two dV/dK products are
     // read before the softmax, whose VALU work then covers their latency
@@ -391,10 +401,14 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
   // past the end of the sequence LSE = +inf makes P = 0
   const float lse2 = (q < p.N) ? p.lse[(int64_t)hh * p.lse_stride + q] * 1.4426950408889634f : INFINITY;
   const float dlt = (q < p.N) ? p.delta[(int64_t)hh * p.Np + q] : 0.f;
-  f32x16 init_s, init_dp;  // accumulator starts: -LSE and -Delta of this lane's query
+  // accumulator starts: -LSE and -Delta of this lane's query; fp32 starts the
+  // S chain at 0 and subtracts LSE after it (the rounding of the plain S - LSE,
+  // as in the dK/dV kernel)
+  constexpr bool SUB_AFTER = sizeof(T) == 4;
+  f32x16 init_s, init_dp;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    init_s[e] = -lse2;
+    init_s[e] = SUB_AFTER ? 0.f : -lse2;
     init_dp[e] = -dlt;
   }
   f32x16 dq[ND];
@@ -496,6 +510,10 @@ __global__ __launch_bounds__((DqGeo<T, D>::NT)) void attn_bwd_dq_kernel(const At
         }
         // P = exp2(S - LSE); dS = P (dP - Delta) / sqrt(d) (log2 units and the
         // 1/sqrt(d) come with the pre-scaled q and dout)
+        if constexpr (SUB_AFTER) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[e] -= lse2;
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[e] = fast_exp2(sacc[e]);
         if (k0 + kt * 32 + 31 > q0w) {  // wave-uniform: the half crosses this wave's diagonal

@@ -1,7 +1,7 @@
 """Sharp-softmax stress inputs shared by the replay test (CPU) and the GPU
 parity test. Each case: (dtype, N, d_model, Hq, Hkv, head_dim, qk_std,
 chunk sizes, seed). Wq and Wk have std qk_std (logit std about
-d_model * qk_std^2 before the row scales), and x rows follow
+d_model * qk_std^2 before the row scales: 6 to 28 here), and x rows follow
 ``synth.sharp_x_row_scale``: the first 64 rows shrunk 16x (the first key
 tile scores near 0 against every query), the rest growing by 25% along the
 sequence. The Llama3-8B-shaped case is the stress input with Wq and Wk at
@@ -15,8 +15,15 @@ CASES = {
     "bf16-d64-gqa4x2": ("bf16", 2100, 512, 8, 2, 64, 0.1, (2,), 22),
     "bf16-llama-w3": ("bf16", 2304, 4096, 4, 1, 128, 0.06, (1,), 23),
     "fp32-d64-gqa4x2": ("fp32", 2048, 256, 8, 2, 64, 0.14, (2,), 24),
-    "fp32-d128-w-std15": ("fp32", 1500, 256, 4, 1, 128, 0.242, (4,), 25),
+    "fp32-d128-std25": ("fp32", 1500, 256, 4, 1, 128, 0.3, (4,), 25),
 }
+
+# Cases whose gradients are too ill-conditioned for the layer's fixed bars
+# (logit std 18 and 28): the textbook backward in plain fp32 arithmetic with
+# io-dtype storage already lands beyond the bar from the oracle
+# (``test_sharp_replay.py`` checks that), so their gradients are held to a
+# bar derived from that distance instead.
+ILL_CONDITIONED = ("bf16-llama-w3", "fp32-d128-std25")
 
 
 def inputs(name):

@@ -60,13 +60,13 @@ def test_deterministic_backward_is_bitwise_repeatable(name):
         assert torch.equal(a, b) and torch.equal(a, c)
     # the deterministic gradients are the layer's gradients
     check_bwd(case, C, g1)
-    # and the default backward's differ from them by rounding only
+    # and the default backward's differ from them by rounding only (within the bars)
     g0 = _bwd(case, C, lse, False)
     for a, b in zip(g0, g1):
         if a is None:
             continue
         e = float((a.double() - b.double()).norm() / b.double().norm())
-        assert e <= (1e-6 if case.dtype == "fp32" else 1e-2), e
+        assert e <= (1e-5 if case.dtype == "fp32" else 1e-2), e
 
 
 GUARD = 1 << 20  # bytes on each side (a multiple of 256 keeps the views aligned)

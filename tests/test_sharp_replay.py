@@ -60,3 +60,26 @@ def test_lse_bound_covers_bf16_stored_scores(name):
         worst = max(worst, float(np.max(np.abs(lse_b - lse[h]) / bound[h])))
     print(name, f"max |dLSE| / bound = {worst:.3f}")
     assert 0.05 < worst < 0.5
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_ill_conditioned_cases_are_beyond_the_bar_in_plain_arithmetic(name):
+    """The cases whose GPU gradients get a derived bar are exactly those where
+    the textbook backward in plain fp32 arithmetic with io-dtype storage
+    already misses the layer's bar in dx; the others meet it with room."""
+    import numpy as np
+
+    from precision_model import plain_grads
+    from sharp_cases import ILL_CONDITIONED
+
+    dt, N, D, hq, hkv, d, _, _, _ = CASES[name]
+    inp = inputs(name)
+    ref = oracle.layer_bwd(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, inp.dy, hq, hkv, d, 5e5, hq)[0]
+    dx = plain_grads(inp, hq, hkv, d, 5e5, dt)[0]
+    e = float(np.linalg.norm(dx - ref) / np.linalg.norm(ref))
+    bar = 2e-2 if dt == "bf16" else 1e-5
+    print(name, f"plain {dt} arithmetic: dx rel {e:.3e} (bar {bar:.0e})")
+    if name in ILL_CONDITIONED:
+        assert e > bar
+    else:
+        assert e < 0.6 * bar
