@@ -70,6 +70,9 @@ def load():
                                    vp, vp, vp, vp, vp, vp, vp, flt, vp, vp, vp,
                                    vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.upipe_attn_bwd.restype = i32
+    lib.upipe_attn_fwd_noalloc.argtypes = [i32, i64, i64, i32, i32, i32, dbl, i32,
+                                           vp, vp, vp, vp, vp, vp, vp, flt, vp, vp, vp]
+    lib.upipe_attn_fwd_noalloc.restype = i32
     lib.upipe_attn_bwd_deterministic.argtypes = lib.upipe_attn_bwd.argtypes
     lib.upipe_attn_bwd_deterministic.restype = i32
     lib.upipe_choose_chunk_heads.argtypes = [i64, i64, i32, i32, i32, i32, i32, i32, sz,
@@ -231,6 +234,40 @@ def attn_fwd(x, wq, wk, wv, wo, *, n_q_heads, n_kv_heads, head_dim, rope_theta, 
                             _stream_handle(dev, stream))
     if rc != 0:
         raise UpipeError(rc, "upipe_attn_fwd")
+    return y, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # UPIPE_NOALLOC_SCRATCH_BYTES
+
+
+def attn_fwd_noalloc(x, wq, wk, wv, wo, y, lse, *, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads,
+                     q_norm=None, k_norm=None, eps=1e-6, stream=None):
+    """upipe_attn_fwd_noalloc: the forward into the caller's y and lse, with the
+    chunk buffers in the library's static device scratch (nothing allocated,
+    here or in the library)."""
+    lib = load()
+    N, D = x.shape
+    dev = x.device
+    dt = x.dtype
+    d = head_dim
+    _check(x, "x", dt, (N, D), dev)
+    _check(wq, "wq", dt, (n_q_heads * d, D), dev)
+    _check(wk, "wk", dt, (n_kv_heads * d, D), dev)
+    _check(wv, "wv", dt, (n_kv_heads * d, D), dev)
+    _check(wo, "wo", dt, (D, n_q_heads * d), dev)
+    if (q_norm is None) != (k_norm is None):
+        raise ValueError("q_norm and k_norm must both be given or both be None")
+    if q_norm is not None:
+        _check(q_norm, "q_norm", dt, (d,), dev)
+        _check(k_norm, "k_norm", dt, (d,), dev)
+    _check(y, "y", dt, (N, D), dev)
+    _check(lse, "lse", torch.float32, (n_q_heads, N), dev)
+    with torch.cuda.device(dev):  # the library takes the current device's scratch
+        rc = lib.upipe_attn_fwd_noalloc(dtype_code(dt), N, D, n_q_heads, n_kv_heads, d, float(rope_theta),
+                                        chunk_heads, _ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(q_norm),
+                                        _ptr(k_norm), float(eps), _ptr(y), _ptr(lse), _stream_handle(dev, stream))
+    if rc != 0:
+        raise UpipeError(rc, "upipe_attn_fwd_noalloc")
     return y, lse
 
 

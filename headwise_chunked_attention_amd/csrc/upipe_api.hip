@@ -14,6 +14,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "upipe.h"
@@ -30,6 +31,29 @@ Profiler g_prof;
 }  // namespace upipe
 
 namespace {
+
+// Scratch of upipe_attn_fwd_noalloc. In host code `scratch` names a host-side
+// stand-in, not device memory: kernels and copies get the per-device address
+// that noalloc_scratch() looks up once per device.
+__device__ __align__(256) char scratch[UPIPE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// This device's address of `scratch` (looked up on the first call with the
+// device current), or null when the lookup fails.
+void* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 constexpr int64_t ROW_PAD = 256;   // token rows of per-head buffers are padded to this
 
@@ -633,6 +657,33 @@ int upipe_attn_fwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n
                               (const float*)k_norm_w, norm_eps, (float*)y, lse, ws, st);
 }
 
+int upipe_attn_fwd_noalloc(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
+                           int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
+                           const void* wk, const void* wv, const void* wo, const void* q_norm_w,
+                           const void* k_norm_w, float norm_eps, void* y, float* lse, void* stream) {
+  Shape s;
+  int rc = check_common(dtype, n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, rope_theta, chunk_heads,
+                        q_norm_w, k_norm_w, norm_eps, &s);
+  if (rc) return rc;
+  const void* ptrs[] = {x, wq, wk, wv, wo, y, lse};
+  if ((rc = check_ptrs(ptrs, 7))) return rc;
+  if (s.norm) {
+    const void* np[] = {q_norm_w, k_norm_w};
+    if ((rc = check_ptrs(np, 2))) return rc;
+  }
+  if (make_plan(s, false).total > UPIPE_NOALLOC_SCRATCH_BYTES) return UPIPE_ERR_SCRATCH;
+  char* ws = reinterpret_cast<char*>(noalloc_scratch());
+  if (!ws) return UPIPE_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == UPIPE_BF16)
+    return attn_fwd_impl<bf16>(s, rope_theta, (const bf16*)x, (const bf16*)wq, (const bf16*)wk,
+                               (const bf16*)wv, (const bf16*)wo, (const bf16*)q_norm_w,
+                               (const bf16*)k_norm_w, norm_eps, (bf16*)y, lse, ws, st);
+  return attn_fwd_impl<float>(s, rope_theta, (const float*)x, (const float*)wq, (const float*)wk,
+                              (const float*)wv, (const float*)wo, (const float*)q_norm_w,
+                              (const float*)k_norm_w, norm_eps, (float*)y, lse, ws, st);
+}
+
 static int attn_bwd_entry(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads, int n_kv_heads,
                           int head_dim, double rope_theta, int chunk_heads, const void* x, const void* wq,
                           const void* wk, const void* wv, const void* wo, const void* q_norm_w,
@@ -697,6 +748,8 @@ const char* upipe_strerror(int code) {
     case UPIPE_ERR_WORKSPACE: return "workspace missing or smaller than upipe_attn_workspace_bytes()";
     case UPIPE_ERR_ALIGNMENT: return "misaligned pointer (tensors need 16 bytes, the workspace 256 bytes)";
     case UPIPE_ERR_HIP: return "a HIP kernel launch failed";
+    case UPIPE_ERR_SCRATCH: return "upipe_attn_fwd_noalloc: the forward workspace of these sizes exceeds the "
+                                   "built-in scratch (UPIPE_NOALLOC_SCRATCH_BYTES); use upipe_attn_fwd";
     default: return "unknown error code";
   }
 }

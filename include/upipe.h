@@ -73,7 +73,8 @@ enum {
   UPIPE_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, D not a multiple of 128, bad chunking */
   UPIPE_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than upipe_attn_workspace_bytes */
   UPIPE_ERR_ALIGNMENT = -4,   /* a tensor not 16-B aligned or the workspace not 256-B aligned */
-  UPIPE_ERR_HIP = -5          /* a HIP launch failed */
+  UPIPE_ERR_HIP = -5,         /* a HIP launch failed */
+  UPIPE_ERR_SCRATCH = -6      /* upipe_attn_fwd_noalloc: needs more than its built-in scratch */
 };
 
 /*
@@ -157,6 +158,32 @@ int upipe_attn_bwd(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n
                    float* dwq, float* dwk, float* dwv, float* dwo, float* dq_norm_w,
                    float* dk_norm_w, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * upipe_attn_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results as upipe_attn_fwd, without the
+ * workspace: the chunk buffers live in a scratch array of
+ * UPIPE_NOALLOC_SCRATCH_BYTES that the library holds in each GPU's memory
+ * (a static device array, allocated with the library's code when it loads
+ * on that GPU and kept until the process ends). The call allocates nothing.
+ * Limit: upipe_attn_workspace_bytes(..., backward = 0) of the arguments must
+ * not exceed UPIPE_NOALLOC_SCRATCH_BYTES (bf16, head_dim 128, chunk_heads 1:
+ * about 65000 tokens), else UPIPE_ERR_SCRATCH and nothing is launched.
+ * Every call on a GPU uses that GPU's one scratch array: calls that overlap
+ * in time on one GPU (other streams, other threads) race and must not be
+ * issued; calls in stream order are safe. The forward writes every scratch
+ * byte it reads in the same call, so nothing needs clearing between calls.
+ * The scratch used is the current device's (hipGetDevice), which must be the
+ * device of the tensors and the stream. The first call on a device looks up
+ * that device's scratch address (UPIPE_ERR_HIP if the lookup fails).
+ */
+#define UPIPE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int upipe_attn_fwd_noalloc(upipe_dtype_t dtype, int64_t n_tokens, int64_t d_model, int n_q_heads,
+                           int n_kv_heads, int head_dim, double rope_theta, int chunk_heads,
+                           const void* x, const void* wq, const void* wk, const void* wv,
+                           const void* wo, const void* q_norm_w, const void* k_norm_w,
+                           float norm_eps, void* y, float* lse, void* stream);
 
 /*
  * upipe_attn_bwd with bitwise reproducible results: the same arguments,

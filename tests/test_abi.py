@@ -23,11 +23,11 @@ def test_exports_every_header_symbol(lib):
                           "upipe_loss_workspace_bytes", "upipe_loss_fwd", "upipe_loss_bwd",
                           "upipe_block_workspace_bytes", "upipe_block_fwd", "upipe_block_bwd",
                           "upipe_stack_workspace_bytes", "upipe_stack_fwd", "upipe_stack_bwd", "upipe_device_peak",
-                          "upipe_attn_bwd_deterministic"}
+                          "upipe_attn_bwd_deterministic", "upipe_attn_fwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.upipe_version() == 100
-    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, ALIGN, -5):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, ALIGN, -5, -6):
         assert len(api.strerror(code)) > 5
     assert "unknown" in api.strerror(-99)
 
@@ -177,6 +177,22 @@ def test_bwd_validation_errors(lib):
     need = api.workspace_bytes(256, 512, 8, 2, 64, 2, False, "fp32", True)
     assert bwd(wsb=need - 256) == WORKSPACE
     assert bwd(ws=P + 16) == ALIGN
+
+
+def test_noalloc_fwd_validation_errors(lib):
+    """The allocation-free forward checks like upipe_attn_fwd, and rejects a
+    problem whose forward workspace exceeds its built-in scratch before any
+    HIP call (so this runs without a GPU)."""
+    def fwd(N=256, D=512, hq=8, hkv=2, d=64, C=2, x=P):
+        return lib.upipe_attn_fwd_noalloc(1, N, D, hq, hkv, d, 5e5, C, x, P, P, P, P, None, None, 1e-6, P, P, None)
+    assert fwd(d=96) == UNSUPPORTED
+    assert fwd(x=None) == INVALID
+    assert fwd(x=P + 8) == ALIGN
+    scratch = 64 << 20
+    for N, D, hq, hkv, d, C in ((70000, 128, 4, 1, 128, 1), (4096, 512, 64, 8, 128, 64), (1 << 20, 4096, 4, 1, 128, 1)):
+        assert api.workspace_bytes(N, D, hq, hkv, d, C, False, "bf16", False) > scratch
+        assert fwd(N, D, hq, hkv, d, C) == -6
+    assert "scratch" in api.strerror(-6)
 
 
 def test_profile_stop_without_launches_is_empty(lib):
