@@ -224,7 +224,7 @@ DEV void epi_pass(const GemmNT<T>& p, const float* Cs, int64_t mr0, int64_t n0, 
         st16_f<T>(g.a + m * g.ldf + n0 / 2 + cv * VEC, v);
       }
     }
-    if (g.hu) {  // h and u as computed, in the tile's own column order
+    if (g.hu) {  // h and u as computed, in blocks of 64 features: h block, then u block
       for (int c = tid; c < ROWS * BN / VEC; c += NTH) {
         const int row = c / (BN / VEC), cv = c % (BN / VEC);
         const int64_t m = mr0 + row;
@@ -232,7 +232,9 @@ DEV void epi_pass(const GemmNT<T>& p, const float* Cs, int64_t mr0, int64_t n0, 
         float v[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) v[e] = Cs[row * SC + cv * VEC + e];
-        st16_f<T>(g.hu + m * 2 * g.ldf + n0 + cv * VEC, v);
+        // tile column cc: feature n0/2 + cc % (BN/2), h for cc < BN/2, else u
+        const int cc = cv * VEC, f = cc % (BN / 2);
+        st16_f<T>(g.hu + m * 2 * g.ldf + n0 + (f / 64) * 128 + (cc >= BN / 2 ? 64 : 0) + f % 64, v);
       }
     }
   } else if constexpr (EPI == EPI_GLU_BWD) {
@@ -262,31 +264,36 @@ DEV void epi_pass(const GemmNT<T>& p, const float* Cs, int64_t mr0, int64_t n0, 
       st16_f<T>(g.a + m * g.ldf + f0, av);
     }
   } else if constexpr (EPI == EPI_CE) {
-    // four threads per row, 32 logits each: the tile's row max and sum of
-    // exp(logit - max), and the target's logit where the tile holds it
-    static_assert(ROWS * 4 == NTH && BN == 128, "four threads per row");
+    // four threads per row, 32 logits each of every 128-column part of the
+    // tile: the part's row max and sum of exp(logit - max), and the target's
+    // logit where the part holds it
+    static_assert(ROWS * 4 == NTH && BN % 128 == 0, "four threads per row");
     const CeOut<T>& ce = p.ce;
     const int row = tid >> 2, qq = tid & 3;
     const int64_t m = mr0 + row;
-    const float* cr = Cs + row * SC + qq * 32;
-    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) mx = fmaxf(mx, cr[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    float se = 0.f;
+    for (int hb = 0; hb < BN / 128; ++hb) {
+      const float* cr = Cs + row * SC + hb * 128 + qq * 32;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) se += fast_exp2((cr[j] - mx) * LOG2E_F);
-    se += __shfl_xor(se, 1);
-    se += __shfl_xor(se, 2);
-    if (m < p.M) {
-      if (qq == 0) {
-        float* pp = ce.part + (m * (p.N / BN) + n0 / BN) * 2;
-        pp[0] = mx;
-        pp[1] = se;
+      for (int j = 0; j < 32; ++j) mx = fmaxf(mx, cr[j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      float se = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) se += fast_exp2((cr[j] - mx) * LOG2E_F);
+      se += __shfl_xor(se, 1);
+      se += __shfl_xor(se, 2);
+      if (m < p.M) {
+        const int64_t n1 = n0 + hb * 128;
+        if (qq == 0) {
+          float* pp = ce.part + (m * (p.N / 128) + n1 / 128) * 2;
+          pp[0] = mx;
+          pp[1] = se;
+        }
+        const int64_t t = (int64_t)ce.targets[m] - n1 - qq * 32;
+        if (t >= 0 && t < 32) ce.tgt[m] = cr[t];
       }
-      const int64_t t = (int64_t)ce.targets[m] - n0 - qq * 32;
-      if (t >= 0 && t < 32) ce.tgt[m] = cr[t];
     }
   } else if constexpr (EPI == EPI_CE_BWD) {
     const CeOut<T>& ce = p.ce;
@@ -547,6 +554,166 @@ __global__ __launch_bounds__(NTHREADS) void gemm_nt_kernel(const GemmNT<T> p) {
 }
 
 // ------------------------------------------------------------------------
+// gemm_nt on 256 x 256 tiles (bf16, long k: the MLP and LM-head products)
+// ------------------------------------------------------------------------
+// 8 waves in 2 x 4, each 128 x 64 of 32x32 MFMA tiles: per 16-wide k step a
+// wave reads 4 A and 2 B fragments for 8 MFMAs, where the 128 x 128 kernel
+// reads 4 for 4, and a k tile of 64 is 32 MFMAs per wave between barriers
+// instead of 16. k tiles arrive by direct global -> LDS loads into two
+// 64 KB stages of swizzled 128-byte rows (no register staging). Rows of A
+// past M load row M - 1. The epilogue runs in two passes of 128 rows
+// through an fp32 staging tile, with the epilogue code of the 128 x 128
+// kernel.
+constexpr int BIG = 256;
+constexpr int BIG_THREADS = 512;
+constexpr int BIG_BK = 64;
+using BigL = Tile<bf16, BIG_BK>;  // [rows][64 k]
+
+constexpr int big_smem_bytes() {
+  constexpr int main_bytes = 2 * 2 * BigL::ELEMS(BIG) * 2;  // two stages of A and B
+  constexpr int epi_bytes = (BIG / 2) * (BIG + 4) * 4;
+  return main_bytes > epi_bytes ? main_bytes : epi_bytes;
+}
+
+// Direct loads of rows [row0, row0 + 8) of a [BIG][64] k tile: row `row` of
+// the tile comes from src_row(row) (a pointer at the tile's first k).
+template <class F>
+DEV void big_dma_rows(bf16* tile, int row0, F src_row) {
+  constexpr int CPR = BigL::ROW_BYTES / 16;  // 16-byte chunks per row
+  const int l = lane_id();
+  const int row = row0 + l / CPR;
+  const int chunk = (l % CPR) ^ BigL::swz(row);
+  const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)(tile + row0 * BigL::STRIDE);
+  lds_dma16(src_row(row) + chunk * BigL::E, __builtin_amdgcn_readfirstlane(lds));
+}
+
+template <int EPI>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_nt_big_kernel(const GemmNT<bf16> p) {
+  using T = bf16;
+  constexpr int SC = BIG + 4;
+  constexpr int TILE = BigL::ELEMS(BIG);
+  constexpr int RPI = 1024 / BigL::ROW_BYTES;  // rows per direct-load instruction
+  static_assert(BIG / RPI / (BIG_THREADS / 64) == 4, "four direct loads per wave and operand");
+  __shared__ __attribute__((aligned(16))) char smem[big_smem_bytes()];
+  T* sm = reinterpret_cast<T*>(smem);  // stage s: A at 2 s TILE, B at (2 s + 1) TILE
+
+  // tile order as in gemm_nt_kernel (XCD-aware; the smaller operand's tiles
+  // vary fastest)
+  const int64_t ntn = p.N / BIG;
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  int64_t mtile, ntile;
+  if (p.M < p.N) {
+    const int64_t mtn = gridDim.x / ntn;
+    mtile = bid % mtn;
+    ntile = bid / mtn;
+  } else {
+    mtile = bid / ntn;
+    ntile = bid % ntn;
+  }
+  const int64_t m0 = mtile * BIG, n0 = ntile * BIG;
+  const int64_t ldb = p.ldb[0];
+  const T* blo;
+  const T* bhi;
+  if constexpr (EPI == EPI_GLU) {  // 128 gate rows, then the same 128 up rows
+    blo = p.b[0] + (n0 / 2) * ldb;
+    bhi = p.b[1] + (n0 / 2) * ldb;
+  } else {
+    blo = p.b[0] + n0 * ldb;
+    bhi = blo + (BIG / 2) * ldb;
+  }
+
+  const int w = wave_id(), l = lane_id(), r = l & 31, h = l >> 5;
+  const int wm = w >> 2, wn = w & 3;  // rows wm*128 .., columns wn*64 ..
+  const int tid = threadIdx.x;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
+
+  const int64_t nk = p.K / BIG_BK;
+  // A's offset of a k tile: its k block times the block stride plus k within
+  // the block (the blocks hold whole k tiles)
+  int64_t a_blk = 0, a_kin = 0;
+  auto dma_tile = [&](int64_t kt, int stage) {
+    T* As = sm + 2 * stage * TILE;
+    T* Bs = As + TILE;
+    const T* a = p.a + a_blk + a_kin;
+    const int64_t k0 = kt * BIG_BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row0 = (w * 4 + i) * RPI;
+      big_dma_rows(As, row0, [&](int row) { return a + min(m0 + row, p.M - 1) * p.lda; });
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row0 = (w * 4 + i) * RPI;  // a whole instruction is in one half (wave-uniform)
+      if (row0 < BIG / 2)
+        big_dma_rows(Bs, row0, [&](int row) { return blo + row * ldb + k0; });
+      else
+        big_dma_rows(Bs, row0, [&](int row) { return bhi + (row - BIG / 2) * ldb + k0; });
+    }
+    a_kin += BIG_BK;
+    if (a_kin == p.a_kblk) {
+      a_kin = 0;
+      a_blk += p.a_kblk_stride;
+    }
+  };
+
+  // fragments of 16-wide k step ks of the stage in LDS
+  auto frags = [&](const T* As, const T* Bs, int ks, Frag<T> (&fa)[4], Frag<T> (&fb)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) fa[mt] = ld_frag(As + BigL::idx(wm * 128 + mt * 32 + r, ks * 16 + 8 * h));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) fb[nt] = ld_frag(Bs + BigL::idx(wn * 64 + nt * 32 + r, ks * 16 + 8 * h));
+  };
+
+  dma_tile(0, 0);
+  wait_vmem();
+  lds_barrier();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int stage = (int)(kt & 1);
+    if (kt + 1 < nk) dma_tile(kt + 1, stage ^ 1);
+    const T* As = sm + 2 * stage * TILE;
+    const T* Bs = As + TILE;
+    Frag<T> fa[2][4], fb[2][2];
+    frags(As, Bs, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < BIG_BK / 16; ++ks) {
+      if (ks + 1 < BIG_BK / 16) frags(As, Bs, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this step's MFMAs
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) mma(acc[mt][nt], fa[ks & 1][mt], fb[ks & 1][nt]);
+    }
+    if (kt + 1 < nk) wait_vmem();  // this wave's loads of the next stage have landed
+    lds_barrier();
+  }
+
+  // Epilogue in two passes of 128 rows through Cs[128][BIG + 4]: pass q
+  // holds the rows of the waves with wm == q.
+  float* Cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass) lds_barrier();  // the previous pass is done with Cs
+    if (wm == pass) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              Cs[(mt * 32 + 8 * i + 4 * h + j) * SC + wn * 64 + nt * 32 + r] = acc[mt][nt][4 * i + j];
+    }
+    lds_barrier();
+    epi_pass<T, BIG, EPI, BIG / 2, BIG_THREADS>(p, Cs, m0 + pass * (BIG / 2), n0, tid);
+  }
+}
+
+// ------------------------------------------------------------------------
 // split-K GEMM for weight gradients
 // ------------------------------------------------------------------------
 // A token-major tile [BK tokens][COLS] kept row-major in LDS (Tile layout):
@@ -775,6 +942,26 @@ hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
   if ((epi == EPI_GLU || epi == EPI_GLU_BWD) && (bn != 128 || p.N % 128 || p.glu.ldf % 64))
     return hipErrorInvalidValue;
   if ((epi == EPI_CE || epi == EPI_CE_BWD) && (bn != 128 || p.N % 128)) return hipErrorInvalidValue;
+  if constexpr (sizeof(T) == 2) {
+    // bf16 products with 256-wide N tiles and one B operand (or the gated
+    // pair): 256 x 256 tiles
+    const bool big_epi = epi == EPI_STORE || epi == EPI_GLU || epi == EPI_GLU_BWD || epi == EPI_CE || epi == EPI_CE_BWD;
+    if (big_epi && p.N % BIG == 0 && p.nseg == 1 && p.K % BIG_BK == 0 && p.a_kblk % BIG_BK == 0 &&
+        (epi != EPI_GLU || p.glu.ldf % (BIG / 2) == 0)) {
+      const dim3 g((unsigned)(((p.M + BIG - 1) / BIG) * (p.N / BIG)));
+      if (epi == EPI_STORE)
+        hipLaunchKernelGGL((gemm_nt_big_kernel<EPI_STORE>), g, dim3(BIG_THREADS), 0, s, p);
+      else if (epi == EPI_GLU)
+        hipLaunchKernelGGL((gemm_nt_big_kernel<EPI_GLU>), g, dim3(BIG_THREADS), 0, s, p);
+      else if (epi == EPI_GLU_BWD)
+        hipLaunchKernelGGL((gemm_nt_big_kernel<EPI_GLU_BWD>), g, dim3(BIG_THREADS), 0, s, p);
+      else if (epi == EPI_CE)
+        hipLaunchKernelGGL((gemm_nt_big_kernel<EPI_CE>), g, dim3(BIG_THREADS), 0, s, p);
+      else
+        hipLaunchKernelGGL((gemm_nt_big_kernel<EPI_CE_BWD>), g, dim3(BIG_THREADS), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   if (epi == EPI_CE)
     hipLaunchKernelGGL((gemm_nt_kernel<T, 128, EPI_CE>), dim3(grid), dim3(NTHREADS), 0, s, p);
   else if (epi == EPI_CE_BWD)
