@@ -908,6 +908,183 @@ __global__ __launch_bounds__(NTHREADS) void gemm_tn_kernel(const GemmTN<T> p) {
   }
 }
 
+// ------------------------------------------------------------------------
+// gemm_tn on 256 x 256 tiles (bf16): the MLP and LM-head weight gradients
+// ------------------------------------------------------------------------
+// 8 waves in 2 x 4, each 128 x 64 of the output. A k tile is 64 tokens of
+// both operands' 256 columns, each operand kept as two [64][128] halves in
+// swizzled 256-byte rows and loaded straight into LDS; the MFMA operands
+// (8 consecutive tokens of one column) are LDS transpose reads. Two 64 KB
+// stages. The output tile goes through an fp32 staging tile in two passes of
+// 128 rows and is added as in gemm_tn_kernel.
+using TnBigL = Tile<bf16, 128>;  // [tokens][128 columns]
+
+template <int UNUSED = 0>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_tn_big_kernel(const GemmTN<bf16> p) {
+  using T = bf16;
+  constexpr int HALF = TnBigL::ELEMS(BIG_BK);  // [64 tokens][128 columns]
+  constexpr int OPER = 2 * HALF;                // one operand's k tile: halves 0 and 1
+  constexpr int SC = BIG + 4;
+  constexpr int CPR = TnBigL::ROW_BYTES / 16;  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                // rows per direct-load instruction
+  static_assert(2 * 2 * BIG_BK / RPI == 8 * (BIG_THREADS / 64), "eight direct loads per wave");
+  __shared__ __attribute__((aligned(16))) char smem[big_smem_bytes()];
+  T* sm = reinterpret_cast<T*>(smem);  // stage s: A at 2 s OPER, B at (2 s + 1) OPER
+
+  // tile order as in gemm_tn_kernel
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t gm = p.M / BIG, gn = p.N / BIG;
+  const bool mfast = p.M <= p.N;
+  const int64_t m0 = (mfast ? bid % gm : (bid / gn) % gm) * BIG;
+  const int64_t n0 = (mfast ? (bid / gm) % gn : bid % gn) * BIG;
+  const int64_t split = bid / (gm * gn);
+  const int64_t kb = split * p.ksplit;
+  const int64_t ke = (kb + p.ksplit < p.K) ? kb + p.ksplit : p.K;
+  // column bases of the operands' halves (a half never straddles a B block);
+  // plain values, not an array indexed per wave (that would live in scratch)
+  const T* a0 = p.a + m0;
+  const T* a1 = a0 + 128;
+  const T* b0 = p.b + (n0 / p.b_nblk) * p.b_nblk_stride + (n0 % p.b_nblk);
+  const T* b1 = p.b + ((n0 + 128) / p.b_nblk) * p.b_nblk_stride + ((n0 + 128) % p.b_nblk);
+
+  const int w = wave_id(), l = lane_id(), r = l & 31, h = l >> 5;
+  const int wm = w >> 2, wn = w & 3;
+  const int tid = threadIdx.x;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = zero16();
+
+  // Load i of a stage (unrolled: operand i / 4, half (i / 2) % 2 known at
+  // compile time) moves token rows 4 rb .. 4 rb + 3 of the k tile, row block
+  // rb = (i % 2) * 8 + w; the eight waves cover the 16 row blocks of each half.
+  const int64_t lda = p.lda, ldb = p.ldb;
+  auto dma_tile = [&](int64_t t0, int stage) {
+    T* st = sm + 2 * stage * OPER;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int op = i / 4, hb = (i / 2) % 2;
+      const int row0 = ((i % 2) * 8 + w) * RPI;
+      const T* src = op ? (hb ? b1 : b0) : (hb ? a1 : a0);
+      const int64_t ld = op ? ldb : lda;
+      T* tile = st + op * OPER + hb * HALF;
+      const int row = row0 + l / CPR;
+      const int chunk = (l % CPR) ^ TnBigL::swz(row);
+      const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)(tile + row0 * TnBigL::STRIDE);
+      lds_dma16(src + (t0 + row) * ld + chunk * TnBigL::E, __builtin_amdgcn_readfirstlane(lds));
+    }
+  };
+  // Lane offsets of the column reads, computed once: the swizzle depends only
+  // on a row's low four bits, which a 16-token step does not change, so step
+  // ks adds 16 ks rows to the base. Output column c of the tile lives in half
+  // c / 128: A rows wm*128 + mt*32 are half wm, B columns wn*64 + nt*32 half
+  // wn / 2.
+  int offa[2][4], offb[2][2];
+  {
+    const int Ln = l & 15, hi = (l >> 4) & 1;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) offa[x][mt] = TnBigL::idx(4 * x + 8 * h + (Ln >> 2), mt * 32 + 16 * hi + 4 * (Ln & 3));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        offb[x][nt] = TnBigL::idx(4 * x + 8 * h + (Ln >> 2), (wn * 64 + nt * 32) % 128 + 16 * hi + 4 * (Ln & 3));
+    }
+  }
+  auto frags = [&](const T* st, int ks, Frag<T> (&fa)[4], Frag<T> (&fb)[2]) {
+    const T* Xa = st + wm * HALF + ks * 16 * TnBigL::STRIDE;
+    const T* Xb = st + OPER + (wn >> 1) * HALF + ks * 16 * TnBigL::STRIDE;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) fa[mt] = frag_from_col4<T>(ld_col4_at(Xa, offa[0][mt]), ld_col4_at(Xa, offa[1][mt]));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) fb[nt] = frag_from_col4<T>(ld_col4_at(Xb, offb[0][nt]), ld_col4_at(Xb, offb[1][nt]));
+  };
+
+  const int64_t nk = (ke - kb) / BIG_BK;  // the launcher admits whole k tiles only
+  if (nk > 0) {
+    dma_tile(kb, 0);
+    wait_vmem();
+  }
+  lds_barrier();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int stage = (int)(kt & 1);
+    if (kt + 1 < nk) dma_tile(kb + (kt + 1) * BIG_BK, stage ^ 1);
+    const T* st = sm + 2 * stage * OPER;
+    Frag<T> fa[2][4], fb[2][2];
+    frags(st, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < BIG_BK / 16; ++ks) {
+      if (ks + 1 < BIG_BK / 16) frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this step's MFMAs
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) mma(acc[mt][nt], fa[ks & 1][mt], fb[ks & 1][nt]);
+    }
+    if (kt + 1 < nk) wait_vmem();  // this wave's loads of the next stage have landed
+    lds_barrier();
+  }
+
+  // output segment of the tile (constant indices: an argument array indexed
+  // at run time would be copied to scratch)
+  float* out = p.out[0];
+  int64_t nc0 = n0;
+  if (p.nseg > 1 && n0 >= p.seg_end[0]) {
+    out = p.out[1];
+    nc0 = n0 - p.seg_end[0];
+  }
+  if (p.nseg > 2 && n0 >= p.seg_end[1]) {
+    out = p.out[2];
+    nc0 = n0 - p.seg_end[1];
+  }
+  float* Cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass) lds_barrier();  // the previous pass is done with Cs
+    if (wm == pass) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              Cs[(mt * 32 + 8 * i + 4 * h + j) * SC + wn * 64 + nt * 32 + r] = acc[mt][nt][4 * i + j];
+    }
+    lds_barrier();
+    const int64_t mr0 = m0 + pass * (BIG / 2);  // first output row of the pass
+    constexpr int ROWS = BIG / 2;
+    if (p.part && p.ksplit < p.K) {
+      // fixed-order reduction: this split's tile goes to part[split]
+      float* dst = p.part + split * p.M * p.N;
+      for (int c = tid; c < ROWS * BIG / 4; c += BIG_THREADS) {
+        const int row = c / (BIG / 4), col = (c % (BIG / 4)) * 4;
+        *reinterpret_cast<f32x4*>(dst + (mr0 + row) * p.N + (n0 + col)) =
+            *reinterpret_cast<const f32x4*>(Cs + row * SC + col);
+      }
+    } else if (p.ldn == 1 && p.ksplit >= p.K && (p.ldm & 3) == 0) {
+      // one k split: the only writer of its tile in this launch
+      for (int c = tid; c < ROWS * BIG / 4; c += BIG_THREADS) {
+        const int row = c / (BIG / 4), col = (c % (BIG / 4)) * 4;
+        f32x4* o = reinterpret_cast<f32x4*>(out + (mr0 + row) * p.ldm + (nc0 + col));
+        *o += *reinterpret_cast<const f32x4*>(Cs + row * SC + col);
+      }
+    } else if (p.ldn == 1) {
+      for (int c = tid; c < ROWS * BIG; c += BIG_THREADS) {
+        const int row = c / BIG, col = c % BIG;
+        atomicAdd(out + (mr0 + row) * p.ldm + (nc0 + col), Cs[row * SC + col]);
+      }
+    } else {
+      for (int c = tid; c < ROWS * BIG; c += BIG_THREADS) {
+        const int col = c / ROWS, row = c % ROWS;
+        atomicAdd(out + (mr0 + row) * p.ldm + (nc0 + col) * p.ldn, Cs[row * SC + col]);
+      }
+    }
+  }
+}
+
 // out (+)= sum over the nsplit partial tiles part[s][M][N], s = 0, 1, ... in
 // that order (one thread per output element; the output addressing and
 // segments are those of the TN GEMM).
@@ -991,6 +1168,20 @@ hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s) {
   // whole tiles along M and N; every split holds at least one k row
   if (p.K <= 0 || p.ksplit <= 0 || p.M <= 0 || p.M % BM || bn <= 0 || p.N <= 0 || p.N % bn) return hipErrorInvalidValue;
   const int64_t nsplit = (p.K + p.ksplit - 1) / p.ksplit;
+  bool big = false;
+  if constexpr (sizeof(T) == 2) {
+    // 256 x 256 tiles when the shapes hold whole tiles and k tiles of 64
+    // tokens, no 128-column half straddles a B block or an output segment,
+    // and there are enough tiles to fill the chip
+    big = p.M % BIG == 0 && p.N % BIG == 0 && p.K % BIG_BK == 0 && p.ksplit % BIG_BK == 0 && p.b_nblk % 128 == 0 &&
+          (p.M / BIG) * (p.N / BIG) * nsplit >= 256;
+    for (int sg = 0; sg < p.nseg; ++sg) big = big && p.seg_end[sg] % BIG == 0;
+    if (big) {
+      const dim3 g((unsigned)((p.M / BIG) * (p.N / BIG) * nsplit));
+      hipLaunchKernelGGL((gemm_tn_big_kernel<0>), g, dim3(BIG_THREADS), 0, s, p);
+    }
+  }
+  if (!big) {
   const dim3 grid((unsigned)((p.M / BM) * (p.N / bn) * nsplit));
   if (bn == 128)
     hipLaunchKernelGGL((gemm_tn_kernel<T, 128>), grid, dim3(NTHREADS), 0, s, p);
@@ -998,6 +1189,7 @@ hipError_t launch_gemm_tn(const GemmTN<T>& p, int bn, hipStream_t s) {
     hipLaunchKernelGGL((gemm_tn_kernel<T, 64>), grid, dim3(NTHREADS), 0, s, p);
   else
     return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.part || nsplit < 2) return e;
   int64_t blocks = (p.M * p.N + 255) / 256;
