@@ -640,15 +640,16 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_nt_big_kernel(const GemmNT<b
     T* Bs = As + TILE;
     const T* a = p.a + a_blk + a_kin;
     const int64_t k0 = kt * BIG_BK;
+    // load i moves rows 8 (8 i + w) .. +7: B loads 0, 1 are gate/low rows, 2, 3 high rows
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row0 = (w * 4 + i) * RPI;
+      const int row0 = (i * 8 + w) * RPI;
       big_dma_rows(As, row0, [&](int row) { return a + min(m0 + row, p.M - 1) * p.lda; });
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row0 = (w * 4 + i) * RPI;  // a whole instruction is in one half (wave-uniform)
-      if (row0 < BIG / 2)
+      const int row0 = (i * 8 + w) * RPI;
+      if (i < 2)
         big_dma_rows(Bs, row0, [&](int row) { return blo + row * ldb + k0; });
       else
         big_dma_rows(Bs, row0, [&](int row) { return bhi + (row - BIG / 2) * ldb + k0; });
@@ -673,11 +674,14 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_nt_big_kernel(const GemmNT<b
   lds_barrier();
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int stage = (int)(kt & 1);
-    if (kt + 1 < nk) dma_tile(kt + 1, stage ^ 1);
     const T* As = sm + 2 * stage * TILE;
     const T* Bs = As + TILE;
     Frag<T> fa[2][4], fb[2][2];
+    // the first fragment reads go out before the next tile's loads are
+    // issued, so their latency overlaps that issue
     frags(As, Bs, 0, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) dma_tile(kt + 1, stage ^ 1);
 #pragma unroll
     for (int ks = 0; ks < BIG_BK / 16; ++ks) {
       if (ks + 1 < BIG_BK / 16) frags(As, Bs, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
