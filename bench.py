@@ -618,6 +618,9 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=HEADLINE,
                     help="the headline workload (default: the Llama3-8B share at N = 1048576)")
     ap.add_argument("--prof-steps", type=int, default=2, help="steps of the per-kernel timing run")
+    ap.add_argument("--mlp-only", action="store_true",
+                    help="run only the sequence-tiled MLP and loss measurements and print their JSON "
+                         "(for profiling those GEMMs; not a bench line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) so that "
                          "profiler byte counters can be scaled against a kernel of known traffic")
@@ -642,6 +645,13 @@ def main():
         torch.cuda.synchronize()
         print("# calibration copy: 3 x (1 GiB read + 1 GiB written)", file=sys.stderr, flush=True)
         del src, dst
+
+    if args.mlp_only:
+        mlp = mlp_bench(dev, max(2, args.steps // 2), 1)
+        torch.cuda.empty_cache()
+        loss = loss_bench(dev, max(2, args.steps // 2), 1)
+        print(json.dumps({"mlp": mlp, "loss": loss}), flush=True)
+        return
 
     name = args.workload
     w = WORKLOADS[name]

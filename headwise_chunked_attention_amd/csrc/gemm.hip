@@ -1125,10 +1125,11 @@ hipError_t launch_gemm_nt(const GemmNT<T>& p, int epi, int bn, hipStream_t s) {
   if ((epi == EPI_CE || epi == EPI_CE_BWD) && (bn != 128 || p.N % 128)) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2) {
     // bf16 products with 256-wide N tiles and one B operand (or the gated
-    // pair): 256 x 256 tiles
+    // pair): 256 x 256 tiles, when there are enough of them to fill the chip
     const bool big_epi = epi == EPI_STORE || epi == EPI_GLU || epi == EPI_GLU_BWD || epi == EPI_CE || epi == EPI_CE_BWD;
+    const int64_t big_tiles = ((p.M + BIG - 1) / BIG) * (p.N / BIG);
     if (big_epi && p.N % BIG == 0 && p.nseg == 1 && p.K % BIG_BK == 0 && p.a_kblk % BIG_BK == 0 &&
-        (epi != EPI_GLU || p.glu.ldf % (BIG / 2) == 0)) {
+        (epi != EPI_GLU || p.glu.ldf % (BIG / 2) == 0) && big_tiles >= 256) {
       const dim3 g((unsigned)(((p.M + BIG - 1) / BIG) * (p.N / BIG)));
       if (epi == EPI_STORE)
         hipLaunchKernelGGL((gemm_nt_big_kernel<EPI_STORE>), g, dim3(BIG_THREADS), 0, s, p);
