@@ -74,9 +74,12 @@ def test_mlp_bf16_wide_multi_tile():
     _run(1100, 1024, 2816, 256, "bf16", seed=2)
 
 
-def test_mlp_llama8b_shape_sampled_rows_and_identities():
-    """Llama3-8B MLP (d_model 4096, d_ff 14336), N = 16384 in tiles of 4096, bf16."""
-    N, D, F, T = 16384, 4096, 14336, 4096
+@pytest.mark.parametrize("N,T", [(16384, 4096), (4480, 8192)])
+def test_mlp_llama8b_shape_sampled_rows_and_identities(N, T):
+    """Llama3-8B MLP (d_model 4096, d_ff 14336), bf16: N = 16384 in tiles of 4096, and
+    N = 4480 in one tile, whose last 256-row GEMM tile holds 128 rows and whose weight
+    gradients sum over 70 (not a multiple of 4) k tiles of 64 tokens."""
+    D, F = 4096, 14336
     print(f"mlp large N={N} D={D} F={F} tile={T} bf16", flush=True)
     inp = MlpInputs(N, D, F, "bf16", seed=3)
     t = _upload(inp, "bf16")
@@ -94,7 +97,8 @@ def test_mlp_llama8b_shape_sampled_rows_and_identities():
     assert abs(a_u - ref) <= TOL["bf16"] * abs(ref)
 
     rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([[0, 1, T - 1, T, N - 1], rng.integers(0, N, 27)]))
+    edge = [0, 1, N - 129, N - 128, N - 1] + ([T - 1, T] if T < N else [])
+    rows = np.unique(np.concatenate([edge, rng.integers(0, N, 27)]))
     idx = torch.from_numpy(rows).to("cuda")
     y_rows = host(y.index_select(0, idx))
     dx_rows = host(dx.index_select(0, idx))
