@@ -387,14 +387,16 @@ def stack_bench(dev, steps):
 
 
 LOSS_WORKLOAD = dict(name="llama3-lm-head-loss-seq-shard-16k", n_tokens=16384, d_model=4096, vocab=128256,
-                     tile_tokens=1024, dtype="bf16")
+                     tile_tokens=4096, lean_tile_tokens=1024, dtype="bf16")
 
 
 def loss_bench(dev, steps, warmup):
     """The sequence-tiled cross-entropy of the Llama3 LM head (vocab 128256) on
-    the same 16384-token sequence shard, tile_tokens 1024, bf16: forward and
-    backward times, model TFLOP/s (2 N D V forward, 4 N D V backward: dh and
-    dW), kernel table and the tiled vs untiled logits buffer."""
+    the same 16384-token sequence shard, tile_tokens 4096 (as the MLP), bf16:
+    forward and backward times, model TFLOP/s (2 N D V forward, 4 N D V
+    backward: dh and dW), kernel table and the tiled vs untiled logits buffer;
+    plus the step time and workspace at tile_tokens 1024 (``lean_tile``), the
+    smaller-memory point of the same trade."""
     import numpy as np
     import torch
 
@@ -455,7 +457,37 @@ def loss_bench(dev, steps, warmup):
                          "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                          "kernel": "gemm_nt_kernel (loss and store epilogues) + row reduction"},
             "workspace_gb": {"tiled_bwd": api.loss_workspace_bytes(N, D, V, T, "bf16", True) / 1e9,
-                             "untiled_logits": N * V * 2 / 1e9}}
+                             "untiled_logits": N * V * 2 / 1e9},
+            "lean_tile": _loss_lean_tile(dev, h, wt, tg, g, loss, lse, dh, dw, w["lean_tile_tokens"], model)}
+
+
+def _loss_lean_tile(dev, h, wt, tg, g, loss, lse, dh, dw, T, model, steps=3):
+    """The loss fwd+bwd at a smaller tile: median step time and its workspace."""
+    import numpy as np
+    import torch
+
+    from headwise_chunked_attention_amd import api
+
+    N, D = h.shape
+    V = wt.shape[0]
+    ws = api.alloc_workspace(max(api.loss_workspace_bytes(N, D, V, T, "bf16", True),
+                                 api.loss_workspace_bytes(N, D, V, T, "bf16", False)), dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        api.loss_fwd(h, wt, tg, tile_tokens=T, loss=loss, lse=lse, workspace=ws)
+        api.loss_bwd(h, wt, tg, lse, g, tile_tokens=T, dh=dh, dw=dw, workspace=ws)
+
+    step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    return {"tile_tokens": T, "step_ms": ms, "model_tflops": model / (ms * 1e-3) / 1e12,
+            "workspace_gb_tiled_bwd": api.loss_workspace_bytes(N, D, V, T, "bf16", True) / 1e9}
 
 
 def _wait(events, label, every_s=30.0):
