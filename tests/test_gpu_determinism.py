@@ -127,3 +127,24 @@ def test_nothing_written_outside_workspace_and_outputs(norm):
     assert all(_intact(b) for b in bufs)
     # and the results are the layer's
     check_bwd(case, C, tuple(outs))
+
+
+def test_deterministic_split_partials_at_32k():
+    """Llama3-8B layout at N = 32768 with chunks of 4 heads: the deterministic
+    backward's weight gradients then run split over the tokens with per-split
+    partial tiles (the 256x256 weight-gradient kernel's partial path) and are
+    added in split order. Bitwise repeatable, and within the bf16 bar of the
+    default backward (whose splits add with atomics)."""
+    case = Case(32768, 4096, 4, 1, 128, "bf16", seed=47)
+    C = 4
+    print(f"case llama-32k: N=32768 D=4096 hq=4 hkv=1 d=128 bf16 C={C}", flush=True)
+    y, lse = case.gpu_fwd(C)
+    g1 = _bwd(case, C, lse, True)
+    g2 = _bwd(case, C, lse, True)
+    g0 = _bwd(case, C, lse, False)
+    for a, b, c in zip(g1, g2, g0):
+        if a is None:
+            continue
+        assert torch.equal(a, b)
+        e = float((c.double() - a.double()).norm() / a.double().norm())
+        assert e <= 1e-2, e
