@@ -54,10 +54,6 @@ KERNEL_NAMES = {"attn_fwd": "attn_fwd_kernel<bf16,128,0>", "attn_recompute": "at
 # removes its entries until they are measured again; a workload without an
 # entry reports null.
 TRAFFIC_BYTES = {
-    # profiles/attn_llama1m_hbm_traffic.md: fetch 971.68 GB + write 1.07 GB
-    ("llama3-8b-ulysses-share-1m", "attn_bwd_dkdv"): 972.75e9,
-    # profiles/attn_bwd_dkdv_llama131k_c1_traffic.md: fetch 4.105 GB + write 0.134 GB
-    ("llama3-8b-ulysses-share-131k", "attn_bwd_dkdv"): 4.239e9,
 }
 
 

@@ -45,11 +45,19 @@ namespace {
 // query tile w / KT (32 queries) of each step, so a workgroup covers
 // BKEY = 32*KT keys and BQ = 32*QT queries per step; with 8 waves two waves
 // share each SIMD. Q/dO tiles are double buffered in LDS.
+//
+// Every Q/dO tile a workgroup loads serves its BKEY keys, so the direct loads
+// (and their LDS writes) per flop fall as BKEY grows. bf16 with head_dim 128
+// takes the widest block that fits: 8 x 1 waves, 256 keys, 32 queries per
+// step. K and V of 256 keys (128 KB) and two 32-query Q/dO buffers (32 KB)
+// fill the 160 KB of LDS, so the per-step LSE/Delta go into bytes of the K
+// tile that no step reads (see stat_at in the kernel).
 template <typename T, int D>
 struct DkdvGeo {
   static constexpr bool BIG = (sizeof(T) == 4 && D == 128);  // fp32, head_dim 128: smaller block (LDS)
-  static constexpr int KT = BIG ? 2 : 4;
-  static constexpr int QT = BIG ? 1 : 2;
+  static constexpr bool WIDE = (sizeof(T) == 2 && D == 128);
+  static constexpr int KT = BIG ? 2 : (WIDE ? 8 : 4);
+  static constexpr int QT = (BIG || WIDE) ? 1 : 2;
   static constexpr int NW = KT * QT;
   static constexpr int NT = 64 * NW;
   static constexpr int BKEY = 32 * KT;
@@ -65,7 +73,8 @@ struct DkdvGeo {
   static constexpr int T_ELEMS = V_OFF + L::ELEMS(BKEY);
   static constexpr int RCH = D / VEC;         // 16-byte chunks per row
   static constexpr int PER = BQ * RCH / NT;   // prefetch chunks per thread and tensor
-  static constexpr size_t SMEM = (size_t)T_ELEMS * sizeof(T) + 2 * 2 * BQ * sizeof(float);
+  static constexpr size_t SMEM = (size_t)T_ELEMS * sizeof(T) + (WIDE ? 0 : 2 * 2 * BQ * sizeof(float));
+  static_assert(!WIDE || (2 * 2 * BQ <= 8 * 16 && BKEY >= 128), "statistics fit the dead K row heads");
   // end-of-kernel reduction of the QT partial dK/dV sums per key tile
   static constexpr size_t RED = (size_t)KT * 64 * 16 * (D / 32) * sizeof(float);
   static_assert((BQ * RCH) % NT == 0, "tile chunks");
@@ -100,6 +109,16 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   T* Ks = sm + G::K_OFF;
   T* Vs = sm + G::V_OFF;
   float* stat = reinterpret_cast<float*>(sm + G::T_ELEMS);  // [2 buffers][lse | delta][BQ]
+  // float f of those statistics. WIDE: K rows r with r % 16 in {0, 4} keep
+  // their head-dim columns 0..15 (logical chunks 0 and 1) at physical chunks
+  // 0 and 1, and every wave holds those columns of its keys in registers
+  // before the walk, so the first 32 bytes of 16 such rows hold 8 floats each.
+  auto stat_at = [&](int f) -> float* {
+    if constexpr (G::WIDE)
+      return reinterpret_cast<float*>(Ks + ((f / 8) / 2 * 16 + (f / 8) % 2 * 4) * L::STRIDE) + f % 8;
+    else
+      return stat + f;
+  };
 
   const int l = lane_id(), r = l & 31, h = l >> 5;
   const int w = wave_id();
@@ -167,11 +186,20 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     }
     if (tid < BQ) {
       // negated: they start the S and dP accumulators; rows past the end get P = 0
-      stat[b * 2 * BQ + tid] = rvalid ? -rl * 1.4426950408889634f : -INFINITY;
-      stat[b * 2 * BQ + BQ + tid] = rvalid ? -rd : 0.f;
+      *stat_at(b * 2 * BQ + tid) = rvalid ? -rl * 1.4426950408889634f : -INFINITY;
+      *stat_at(b * 2 * BQ + BQ + tid) = rvalid ? -rd : 0.f;
     }
   };
 
+  Frag<T> kb0, vb0;
+  if constexpr (G::WIDE) {
+    // the first d step of this lane's K and V leave LDS before the statistics
+    // are written over them
+    lds_barrier();
+    kb0 = ld_frag(Ks + L::idx(krel, 8 * h));
+    vb0 = ld_frag(Vs + L::idx(krel, 8 * h));
+    lds_barrier();
+  }
   prefetch(h0, k0, 0);
   commit(0);
   lds_barrier();
@@ -185,8 +213,10 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   if constexpr (sizeof(T) == 2) cplan.init();
   // the K and V fragments of the first d step stay in registers: the first
   // MFMAs of a step then wait only for the Q and dO reads
-  const Frag<T> kb0 = ld_frag(Ks + L::idx(krel, 8 * h));
-  const Frag<T> vb0 = ld_frag(Vs + L::idx(krel, 8 * h));
+  if constexpr (!G::WIDE) {
+    kb0 = ld_frag(Ks + L::idx(krel, 8 * h));
+    vb0 = ld_frag(Vs + L::idx(krel, 8 * h));
+  }
   auto step = [&](auto bc, int64_t it) {
     constexpr int B = decltype(bc)::value;
     int nh_next = hh;
@@ -198,8 +228,6 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     if (it + 1 < total) prefetch(nh_next, q_next, B ^ 1);
     const T* Qs = sm + G::BUF_OFF + B * G::BUF_ELEMS;
     const T* dOs = Qs + L::ELEMS(BQ);
-    const float* lse_s = stat + B * 2 * BQ;
-    const float* del_s = lse_s + BQ;
     const int qrel0 = (int)(q0 - k0) + qt * 32;  // wave's first row - block start
     // wave-uniform: only tiles that cross the diagonal need the causal mask
     const bool diag = qrel0 < kt * 32 + 32;
@@ -217,8 +245,8 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
     f32x16 sacc, dpacc, lse_neg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(lse_s + qt * 32 + 8 * i + 4 * h);
-      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(del_s + qt * 32 + 8 * i + 4 * h);
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(stat_at(B * 2 * BQ + qt * 32 + 8 * i + 4 * h));
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(stat_at(B * 2 * BQ + BQ + qt * 32 + 8 * i + 4 * h));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         lse_neg[4 * i + j] = lv[j];
