@@ -54,6 +54,10 @@ KERNEL_NAMES = {"attn_fwd": "attn_fwd_kernel<bf16,128,0>", "attn_recompute": "at
 # removes its entries until they are measured again; a workload without an
 # entry reports null.
 TRAFFIC_BYTES = {
+    # profiles/attn_llama1m_hbm_traffic.md: fetch 666.965 GB + write 1.074 GB
+    ("llama3-8b-ulysses-share-1m", "attn_bwd_dkdv"): 668.04e9,
+    # profiles/attn_llama131k_hbm_traffic.md: fetch 5.314 GB + write 0.135 GB
+    ("llama3-8b-ulysses-share-131k", "attn_bwd_dkdv"): 5.449e9,
 }
 
 

@@ -51,7 +51,7 @@ namespace {
 // takes the widest block that fits: 8 x 1 waves, 256 keys, 32 queries per
 // step. K and V of 256 keys (128 KB) and two 32-query Q/dO buffers (32 KB)
 // fill the 160 KB of LDS, so the per-step LSE/Delta go into bytes of the K
-// tile that no step reads (see stat_at in the kernel).
+// tile that no step reads (stat_at in the kernel).
 template <typename T, int D>
 struct DkdvGeo {
   static constexpr bool BIG = (sizeof(T) == 4 && D == 128);  // fp32, head_dim 128: smaller block (LDS)
@@ -74,7 +74,7 @@ struct DkdvGeo {
   static constexpr int RCH = D / VEC;         // 16-byte chunks per row
   static constexpr int PER = BQ * RCH / NT;   // prefetch chunks per thread and tensor
   static constexpr size_t SMEM = (size_t)T_ELEMS * sizeof(T) + (WIDE ? 0 : 2 * 2 * BQ * sizeof(float));
-  static_assert(!WIDE || (2 * 2 * BQ <= 8 * 16 && BKEY >= 128), "statistics fit the dead K row heads");
+  static_assert(!WIDE || (2 * 2 * BQ <= 8 * 16 && BKEY >= 32), "statistics fit the unread K bytes of 16 rows");
   // end-of-kernel reduction of the QT partial dK/dV sums per key tile
   static constexpr size_t RED = (size_t)KT * 64 * 16 * (D / 32) * sizeof(float);
   static_assert((BQ * RCH) % NT == 0, "tile chunks");
@@ -109,15 +109,21 @@ __global__ __launch_bounds__((DkdvGeo<T, D>::NT)) void attn_bwd_dkdv_kernel(cons
   T* Ks = sm + G::K_OFF;
   T* Vs = sm + G::V_OFF;
   float* stat = reinterpret_cast<float*>(sm + G::T_ELEMS);  // [2 buffers][lse | delta][BQ]
-  // float f of those statistics. WIDE: K rows r with r % 16 in {0, 4} keep
-  // their head-dim columns 0..15 (logical chunks 0 and 1) at physical chunks
-  // 0 and 1, and every wave holds those columns of its keys in registers
-  // before the walk, so the first 32 bytes of 16 such rows hold 8 floats each.
+  // float f of those statistics. WIDE: every wave holds head-dim columns
+  // 0..15 of its keys' K in registers before the walk, and in K row r those
+  // columns (logical chunks 0 and 1) sit at physical chunks 2k and 2k + 1,
+  // k = swz(r) / 2, where no step reads. Slot s = f / 8 (8 floats) goes to
+  // one of wave 0's rows, chosen so that the four slots of one commit store
+  // (slots 4j .. 4j + 3) have k = 0, 1, 2, 3: 32-byte runs at byte offsets 0,
+  // 32, 64 and 96 of their rows, on different LDS banks.
   auto stat_at = [&](int f) -> float* {
-    if constexpr (G::WIDE)
-      return reinterpret_cast<float*>(Ks + ((f / 8) / 2 * 16 + (f / 8) % 2 * 4) * L::STRIDE) + f % 8;
-    else
+    if constexpr (G::WIDE) {
+      const int sl = f / 8;
+      const int row = 16 * (sl >> 3) + 4 * ((sl >> 2) & 1) + 8 * (sl & 1) + ((sl >> 1) & 1);
+      return reinterpret_cast<float*>(Ks + row * L::STRIDE + (L::swz(row) >> 1) * 16) + f % 8;
+    } else {
       return stat + f;
+    }
   };
 
   const int l = lane_id(), r = l & 31, h = l >> 5;
