@@ -139,6 +139,34 @@ def cpu_baseline(w, sample_n=8192):
             "rows": rows}
 
 
+def tiny_gpu_seconds(dev, reps=10, warmup=3):
+    """Median fwd+bwd seconds of the tiny fp32 configuration (N 2048, d_model
+    512, 8 q / 2 kv heads, head_dim 64, chunk_heads 2) on the GPU, inputs
+    resident: the GPU side of the oracle's tiny-configuration row."""
+    import numpy as np
+    import torch
+
+    from headwise_chunked_attention_amd import api
+    from headwise_chunked_attention_amd.synth import LayerInputs
+
+    inp = LayerInputs(2048, 512, 8, 2, 64, "fp32", seed=0)
+    t = {k: torch.from_numpy(getattr(inp, k)).to(dev) for k in ("x", "wq", "wk", "wv", "wo", "dy")}
+    kw = dict(n_q_heads=8, n_kv_heads=2, head_dim=64, rope_theta=5e5, chunk_heads=2)
+    ws = api.alloc_workspace(max(api.workspace_bytes(2048, 512, 8, 2, 64, 2, False, "fp32", b) for b in (False, True)),
+                             dev)
+    times = []
+    for i in range(warmup + reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        y, lse = api.attn_fwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], workspace=ws, **kw)
+        api.attn_bwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], t["dy"], lse, workspace=ws, **kw)
+        e1.record()
+        e1.synchronize()
+        if i >= warmup:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    return float(np.median(times))
+
+
 MLP_WORKLOAD = dict(name="llama3-8b-mlp-seq-shard-16k", n_tokens=16384, d_model=4096, d_ff=14336,
                     tile_tokens=4096, dtype="bf16")
 
@@ -729,6 +757,13 @@ def main():
     if not args.no_cpu:
         print("# cpu baseline: the fp64 oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w)
+        # GPU speedups: against the workload's projected oracle time, and
+        # against the oracle's tiny-configuration run (timed on the GPU here)
+        main_row = cpu["rows"][0]
+        main_row["gpu_speedup_vs_projected"] = main_row["projected_seconds_at_n"]["seconds"] / (head["ms_per_step"] * 1e-3)
+        tiny_row = cpu["rows"][1]
+        tiny_row["gpu_seconds"] = tiny_gpu_seconds(dev)
+        tiny_row["gpu_speedup"] = tiny_row["seconds"] / tiny_row["gpu_seconds"]
 
     N, D, hq, hkv, d = (w[k] for k in ("n_tokens", "d_model", "n_q_heads", "n_kv_heads", "head_dim"))
     line = {
