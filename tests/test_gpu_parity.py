@@ -42,6 +42,15 @@ def test_fp32_ragged(N, d):
     _run(Case(N, 256, 4, 1, d, "fp32", seed=N), 2)
 
 
+@pytest.mark.parametrize("N", [1, 7, 300, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_ragged(N, d):
+    """Sequences shorter than one key block and ragged tails in bf16: with
+    head_dim 128 the dK/dV kernel's 256-key block then holds mostly padding
+    rows, and its last query step mostly rows past the end."""
+    _run(Case(N, 256, 4, 1, d, "bf16", seed=100 + N), 2)
+
+
 def test_fp32_qk_norm_random_gamma():
     _run(Case(700, 256, 8, 1, 128, "fp32", theta=1e6, norm="random", seed=3), 2)
 
