@@ -672,28 +672,41 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_nt_big_kernel(const GemmNT<b
   dma_tile(0, 0);
   wait_vmem();
   lds_barrier();
+  // As in the TN kernel, the last 16-wide step of k tile kt issues its MFMAs
+  // after the barrier (from ring slot 1), covering the latency of tile
+  // kt + 1's first fragment reads.
+  constexpr int NKS = BIG_BK / 16;
+  static_assert(NKS % 2 == 0, "the deferred step uses ring slot 1");
+  Frag<T> fa[2][4], fb[2][2];
+  auto mma_step = [&](int slot) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) mma(acc[mt][nt], fa[slot][mt], fb[slot][nt]);
+  };
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int stage = (int)(kt & 1);
     const T* As = sm + 2 * stage * TILE;
     const T* Bs = As + TILE;
-    Frag<T> fa[2][4], fb[2][2];
     // the first fragment reads go out before the next tile's loads are
     // issued, so their latency overlaps that issue
     frags(As, Bs, 0, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
     if (kt + 1 < nk) dma_tile(kt + 1, stage ^ 1);
+    if (kt > 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(1);  // the deferred last step of tile kt - 1
+    }
 #pragma unroll
-    for (int ks = 0; ks < BIG_BK / 16; ++ks) {
-      if (ks + 1 < BIG_BK / 16) frags(As, Bs, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+    for (int ks = 0; ks < NKS - 1; ++ks) {
+      frags(As, Bs, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this step's MFMAs
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) mma(acc[mt][nt], fa[ks & 1][mt], fb[ks & 1][nt]);
+      mma_step(ks & 1);
     }
     if (kt + 1 < nk) wait_vmem();  // this wave's loads of the next stage have landed
     lds_barrier();
   }
+  if (nk > 0) mma_step(1);
 
   // Epilogue in two passes of 128 rows through Cs[128][BIG + 4]: pass q
   // holds the rows of the waves with wm == q.
@@ -1011,24 +1024,38 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_tn_big_kernel(const GemmTN<b
     wait_vmem();
   }
   lds_barrier();
+  // The last 16-wide step of k tile kt issues its MFMAs after the barrier,
+  // beside the first column reads of tile kt + 1: its fragments are in
+  // registers (slot 1 of the ring), so the LDS latency after the barrier is
+  // covered by MFMA work instead of stalling every wave at once.
+  constexpr int NKS = BIG_BK / 16;
+  static_assert(NKS % 2 == 0, "the deferred step uses ring slot 1");
+  Frag<T> fa[2][4], fb[2][2];
+  auto mma_step = [&](int slot) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) mma(acc[mt][nt], fa[slot][mt], fb[slot][nt]);
+  };
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int stage = (int)(kt & 1);
     if (kt + 1 < nk) dma_tile(kb + (kt + 1) * BIG_BK, stage ^ 1);
     const T* st = sm + 2 * stage * OPER;
-    Frag<T> fa[2][4], fb[2][2];
     frags(st, 0, fa[0], fb[0]);
+    if (kt > 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(1);  // the deferred last step of tile kt - 1
+    }
 #pragma unroll
-    for (int ks = 0; ks < BIG_BK / 16; ++ks) {
-      if (ks + 1 < BIG_BK / 16) frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+    for (int ks = 0; ks < NKS - 1; ++ks) {
+      frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this step's MFMAs
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) mma(acc[mt][nt], fa[ks & 1][mt], fb[ks & 1][nt]);
+      mma_step(ks & 1);
     }
     if (kt + 1 < nk) wait_vmem();  // this wave's loads of the next stage have landed
     lds_barrier();
   }
+  if (nk > 0) mma_step(1);
 
   // output segment of the tile (constant indices: an argument array indexed
   // at run time would be copied to scratch)
