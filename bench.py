@@ -40,6 +40,12 @@ LLAMA = dict(d_model=4096, n_q_heads=4, n_kv_heads=1, head_dim=128, rope_theta=5
 WORKLOADS = {
     "llama3-8b-ulysses-share-1m": dict(LLAMA, n_tokens=1048576),
     "llama3-8b-ulysses-share-131k": dict(LLAMA, n_tokens=131072),
+    # the other two large configurations, on request (--workload): the 5M-token
+    # share (one step takes minutes) and the Qwen3-32B-shaped share with q/k
+    # RMSNorm
+    "llama3-8b-ulysses-share-5m": dict(LLAMA, n_tokens=5242880, chunks=(1,)),
+    "qwen3-32b-ulysses-share-512k": dict(d_model=5120, n_q_heads=8, n_kv_heads=1, head_dim=128, rope_theta=1e6,
+                                         dtype="bf16", chunks=(1, 2, 4, 8), n_tokens=524288, qk_norm=True),
 }
 HEADLINE = "llama3-8b-ulysses-share-1m"
 SECONDARY = "llama3-8b-ulysses-share-131k"
@@ -545,10 +551,12 @@ def attention_bench(dev, name, w, chunk, steps, warmup, sweep_steps, prof_steps,
 
     N, D, hq, hkv, d, theta = (w[k] for k in ("n_tokens", "d_model", "n_q_heads", "n_kv_heads", "head_dim",
                                               "rope_theta"))
+    norm = bool(w.get("qk_norm", False))
     t0 = time.perf_counter()
     t = {}
-    inp = LayerInputs(N, D, hq, hkv, d, "bf16", seed=0, with_x=False, with_dy=False)
-    for k in ("wq", "wk", "wv", "wo"):
+    inp = LayerInputs(N, D, hq, hkv, d, "bf16", seed=0, with_x=False, with_dy=False,
+                      qk_norm="random" if norm else None)
+    for k in ("wq", "wk", "wv", "wo") + (("q_norm", "k_norm") if norm else ()):
         t[k] = torch.from_numpy(getattr(inp, k)).to(dev).to(torch.bfloat16)
     from headwise_chunked_attention_amd.synth import gen_rows
     for k in ("x", "dy"):
@@ -566,8 +574,10 @@ def attention_bench(dev, name, w, chunk, steps, warmup, sweep_steps, prof_steps,
 
     def run_chunk(C, steps, warmup, profile):
         kw = dict(n_q_heads=hq, n_kv_heads=hkv, head_dim=d, rope_theta=theta, chunk_heads=C)
-        ws_f = api.workspace_bytes(N, D, hq, hkv, d, C, False, "bf16", False)
-        ws_b = api.workspace_bytes(N, D, hq, hkv, d, C, False, "bf16", True)
+        if norm:
+            kw.update(q_norm=t["q_norm"], k_norm=t["k_norm"])
+        ws_f = api.workspace_bytes(N, D, hq, hkv, d, C, norm, "bf16", False)
+        ws_b = api.workspace_bytes(N, D, hq, hkv, d, C, norm, "bf16", True)
         ws = api.alloc_workspace(max(ws_f, ws_b), dev)
         y = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((hq, N), dtype=torch.float32, device=dev)
@@ -575,7 +585,8 @@ def attention_bench(dev, name, w, chunk, steps, warmup, sweep_steps, prof_steps,
         out = (torch.empty((N, D), dtype=torch.bfloat16, device=dev),
                torch.empty(t["wq"].shape, dtype=f32, device=dev), torch.empty(t["wk"].shape, dtype=f32, device=dev),
                torch.empty(t["wv"].shape, dtype=f32, device=dev), torch.empty(t["wo"].shape, dtype=f32, device=dev),
-               None, None)
+               torch.empty((d,), dtype=f32, device=dev) if norm else None,
+               torch.empty((d,), dtype=f32, device=dev) if norm else None)
 
         def fwd():
             api.attn_fwd(t["x"], t["wq"], t["wk"], t["wv"], t["wo"], y=y, lse=lse, workspace=ws, **kw)
@@ -781,6 +792,7 @@ def main():
         "data": "synthetic (seeded host Gaussian inputs, random-init weights; no dataset)",
         "config": {"workload": name, "n_tokens": N, "d_model": D, "n_q_heads": hq, "n_kv_heads": hkv,
                    "head_dim": d, "rope_theta": w["rope_theta"], "causal": True, "chunk_heads": args.chunk,
+                   "qk_norm": bool(w.get("qk_norm", False)),
                    "parallelism": "one GPU's Ulysses head share (no collectives)"},
         "frac_of_peak": head["tflops"] / PEAK_BF16_TFLOPS,
         "peak_from_device": dict(peak_dev, frac_of_peak=head["tflops"] / peak_dev["bf16_dense_tflops"]),
