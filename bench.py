@@ -20,6 +20,7 @@ checkpointed transformer block built from them (``block``), and four such
 blocks with their inputs offloaded to host memory (``stack``).
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--chunk 1] [--no-sweep] [--no-cpu]
+                  [--workload llama3-8b-ulysses-share-5m | qwen3-32b-ulysses-share-512k | ...]
 """
 from __future__ import annotations
 
@@ -687,7 +688,8 @@ def main():
     ap.add_argument("--no-block", action="store_true", help="skip the transformer-block measurement")
     ap.add_argument("--no-secondary", action="store_true", help="skip the N = 131072 measurement")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=HEADLINE,
-                    help="the headline workload (default: the Llama3-8B share at N = 1048576)")
+                    help="the workload timed (default: the Llama3-8B share at N = 1048576; the 131072-token, "
+                         "5M-token and Qwen3-32B-shaped shares on request)")
     ap.add_argument("--prof-steps", type=int, default=2, help="steps of the per-kernel timing run")
     ap.add_argument("--mlp-only", action="store_true",
                     help="run only the sequence-tiled MLP and loss measurements and print their JSON "
