@@ -13,10 +13,12 @@
 // the exponent in log2 units and dO V^T is dP/sqrt(d); the dK/dV kernel
 // scales its two results back once at the end. Both kernels form the same
 // dS values.
-// Two kernels, no atomics:
+// Two kernels, no dQ atomics:
 //  * dK/dV kernel, key-stationary: a workgroup owns a block of keys and walks
 //    the query tiles at or after it for every q head of the chunk reading this
-//    kv head, so dK and dV sum over the GQA group in registers. Per step it
+//    kv head, so dK and dV sum over the GQA group in registers (short
+//    sequences split the heads over several workgroups per key block and add
+//    their sums with fp32 atomics; the deterministic entry point does not). Per step it
 //    computes S = Q K^T and dP = dO V^T (rows q, one key per lane), then
 //    dV^T += dO^T P and dK^T += Q^T dS with P/dS fed from the accumulators.
 //  * dQ kernel, query-stationary (the forward's shape): a wave owns 32 queries
